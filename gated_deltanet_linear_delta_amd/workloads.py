@@ -1,0 +1,193 @@
+"""Seeded synthetic inputs for the gated delta rule.
+
+This module only draws random numbers and prepares them the way a caller of
+the layer would (L2-normalised q/k, beta = sigmoid(.), g = -softplus(.),
+bf16 rounding of the activations).  It holds none of the recurrence's
+arithmetic, so both the HIP path and the fp64 oracle can be fed from it.
+
+Workload shapes follow the layer described in Perplexity, "Optimizing
+on-device inference for Apple Silicon", section "Qwen creates three distinct
+workload shapes" (a recurrent layer with a fixed-size per-head state) and
+section "Keeping the recurrent state on chip" (fp32 state and gate, bf16
+query/key activations).  The pages give no head counts for this layer; the
+named configurations below fix them (16 query/key heads shared by 32 value
+heads, d_k = d_v = 128).
+
+All arrays are numpy: activations are float32 arrays whose values are exactly
+representable in the requested io dtype (bf16 values are produced by
+round-to-nearest-even), gates and state are float32.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Inputs", "DecodeInputs", "round_to_bf16", "make_prefill", "make_decode", "config"]
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns
+    float32 values that are exactly representable in bfloat16.  Inputs must be
+    finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    r = (u + bias) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _unit_rows(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def _io(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    if io_dtype == "bf16":
+        return round_to_bf16(x)
+    if io_dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(f"io_dtype must be 'bf16' or 'f32', not {io_dtype!r}")
+
+
+@dataclass
+class Inputs:
+    """A packed prefill batch.  Shapes: q, k [T, h_qk, d_k]; v [T, h_v, d_v];
+    g, beta [T, h_v]; cu_seqlens [N+1] int32; state_in [N, h_v, d_v, d_k] or
+    None."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    cu_seqlens: np.ndarray
+    state_in: np.ndarray | None
+    io_dtype: str
+    chunk_size: int = 64
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        T, h_qk, d_k = self.q.shape
+        return dict(num_seqs=len(self.cu_seqlens) - 1, total_tokens=T, h_qk=h_qk,
+                    h_v=self.v.shape[1], d_k=d_k, d_v=self.v.shape[2])
+
+
+@dataclass
+class DecodeInputs:
+    """``steps`` decode steps for B sequences: q, k [steps, B, h_qk, d_k];
+    v [steps, B, h_v, d_v]; g, beta [steps, B, h_v]; state [B, h_v, d_v, d_k]."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    state: np.ndarray
+    io_dtype: str
+    meta: dict = field(default_factory=dict)
+
+
+def _draw_gate(rng, shape, shift):
+    beta_raw = rng.standard_normal(shape)
+    g_raw = rng.standard_normal(shape)
+    beta = _sigmoid(beta_raw).astype(np.float32)
+    g = (-_softplus(g_raw + shift)).astype(np.float32)
+    return g, beta
+
+
+def make_prefill(lengths, h_qk, h_v, d_k, d_v, io_dtype="bf16", gate_shift=0.0,
+                 state_std=None, seed=0, chunk_size=64, rng=None) -> Inputs:
+    """Draw a packed batch of sequences with the given lengths.
+
+    Draw order: q, k, v (standard normal, float32), beta_raw, g_raw (float64),
+    then the initial state (normal with standard deviation ``state_std``; no
+    state if None).  q and k are L2-normalised per (token, head) before
+    rounding to the io dtype; beta = sigmoid(beta_raw),
+    g = -softplus(g_raw + gate_shift).
+    """
+    rng = np.random.default_rng(seed) if rng is None else rng
+    lengths = [int(x) for x in lengths]
+    if any(x < 0 for x in lengths):
+        raise ValueError("lengths must be >= 0")
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q = _io(_unit_rows(rng.standard_normal((T, h_qk, d_k), dtype=np.float32)), io_dtype)
+    k = _io(_unit_rows(rng.standard_normal((T, h_qk, d_k), dtype=np.float32)), io_dtype)
+    v = _io(rng.standard_normal((T, h_v, d_v), dtype=np.float32), io_dtype)
+    g, beta = _draw_gate(rng, (T, h_v), gate_shift)
+    state = None
+    if state_std is not None:
+        state = (rng.standard_normal((len(lengths), h_v, d_v, d_k), dtype=np.float32)
+                 * np.float32(state_std)).astype(np.float32)
+    return Inputs(q, k, v, g, beta, cu, state, io_dtype, chunk_size,
+                  dict(lengths=lengths, gate_shift=gate_shift, state_std=state_std, seed=seed))
+
+
+def make_decode(steps, batch, h_qk, h_v, d_k, d_v, io_dtype="bf16", gate_shift=0.0,
+                state_std=0.02, seed=0, rng=None, state=None) -> DecodeInputs:
+    """Draw ``steps`` decode steps at batch ``batch``.  Draw order: the
+    initial state (unless given), then q, k, v, beta_raw, g_raw as arrays of
+    shape [steps, batch, ...]."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    if state is None:
+        state = (rng.standard_normal((batch, h_v, d_v, d_k), dtype=np.float32)
+                 * np.float32(state_std)).astype(np.float32)
+    q = _io(_unit_rows(rng.standard_normal((steps, batch, h_qk, d_k), dtype=np.float32)), io_dtype)
+    k = _io(_unit_rows(rng.standard_normal((steps, batch, h_qk, d_k), dtype=np.float32)), io_dtype)
+    v = _io(rng.standard_normal((steps, batch, h_v, d_v), dtype=np.float32), io_dtype)
+    g, beta = _draw_gate(rng, (steps, batch, h_v), gate_shift)
+    return DecodeInputs(q, k, v, g, beta, np.ascontiguousarray(state, dtype=np.float32), io_dtype,
+                        dict(steps=steps, batch=batch, gate_shift=gate_shift, seed=seed))
+
+
+def ragged_lengths(rng, n, lo=256, hi=8192):
+    """Sequence lengths log-uniform in [lo, hi], rounded to integers."""
+    x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+# The five named workloads.  Seeds are 1000 + index.
+CONFIG_NAMES = {
+    0: "tiny fp32: T=64, H=2, d=16, chunk 16",
+    1: "decode B=1, 16 qk / 32 v heads, d=128, bf16, 1000 carried steps",
+    2: "prefill T=4096, B=1, 16 qk / 32 v heads, d=128, bf16, chunk 64",
+    3: "long prefill T=131072, B=1, 16 qk / 32 v heads, d=128, bf16, chunk 64",
+    4: "ragged prefill 32 seqs log-uniform [256, 8192] + 256 decode steps at B=32",
+}
+
+
+def config(index: int, decode_steps: int | None = None):
+    """Return the inputs of a named workload.
+
+    0 -> Inputs; 1 -> DecodeInputs; 2, 3 -> Inputs; 4 -> (Inputs, DecodeInputs).
+    ``decode_steps`` shortens the decode part of configs 1 and 4.
+    """
+    rng = np.random.default_rng(1000 + index)
+    if index == 0:
+        return make_prefill([64], 2, 2, 16, 16, "f32", 0.0, None, rng=rng, chunk_size=16)
+    if index == 1:
+        steps = 1000 if decode_steps is None else decode_steps
+        return make_decode(steps, 1, 16, 32, 128, 128, "bf16", 0.0, 0.02, rng=rng)
+    if index in (2, 3):
+        T = 4096 if index == 2 else 131072
+        return make_prefill([T], 16, 32, 128, 128, "bf16", 2.0, None, rng=rng, chunk_size=64)
+    if index == 4:
+        lengths = ragged_lengths(rng, 32)
+        pre = make_prefill(lengths, 16, 32, 128, 128, "bf16", 2.0, 0.02, rng=rng, chunk_size=64)
+        steps = 256 if decode_steps is None else decode_steps
+        dec = make_decode(steps, 32, 16, 32, 128, 128, "bf16", 2.0, rng=rng,
+                          state=np.zeros((32, 32, 128, 128), np.float32))
+        return pre, dec
+    raise ValueError(f"no config {index}")

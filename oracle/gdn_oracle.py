@@ -1,0 +1,213 @@
+"""Plain fp64 CPU oracle for the gated delta rule.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker that the HIP path is
+measured against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  The library path
+(``gated_deltanet_linear_delta_amd``) never imports, calls or falls back to it,
+and this module imports nothing from the library: the two share no code.
+
+What it computes
+----------------
+Source: Perplexity, "Optimizing on-device inference for Apple Silicon"
+(Slovak and Spanish editions of the same post).
+
+* Section "Qwen creates three distinct workload shapes" (sk: "Qwen vytvára
+  tri rôzne tvary pracovného zaťaženia"; es: "Qwen crea tres formas de carga
+  de trabajo distintas") describes a Gated DeltaNet layer as a fixed-size
+  recurrent state, a learned gate that sets how much of the old state is kept,
+  and a delta update that folds in the current token; every token depends on
+  the state left by the previous one.  Prefill may walk the tokens carrying
+  the state, or regroup the updates into blocks; both evaluate the same
+  computation.
+* Section "Keeping the recurrent state on chip" (es: "Mantener el estado
+  recurrente en el chip") says the state is a matrix, and that the state and
+  its gate are fp32 while query/key activations are bf16.
+* Section "Bounding scratch memory by chunking the prompt" (es: "Limitar la
+  memoria temporal mediante la fragmentación de mensajes") says the state is
+  carried from one prompt segment to the next without changing the output.
+
+The pages give the recurrence in prose only.  The equation used here is the
+gated delta rule, the plainest formula that fits that prose:
+
+    S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+    o_t = S_t q_t                       (post-update state)
+    alpha_t = exp(g_t)                  (g is the log-gate, passed in)
+
+per sequence and per value head, with S a [d_v, d_k] matrix (row index over
+d_v, column index over d_k).  With H_qk query/key heads shared by H_v value
+heads, value head h reads query/key head h // (H_v / H_qk) (contiguous
+groups).  No softplus, sigmoid, q/k normalisation or q scaling is applied
+here: those belong to the caller, and the inputs arrive already prepared.
+
+Every input is widened exactly to fp64 (bf16 and fp32 values are exactly
+representable) and every step runs in fp64.
+
+Parity status: each public function is pinned by ``tests/test_oracle.py``
+(brute force on the literal matrix form, exact rational arithmetic, the delta
+invariant, closed forms for pure decay / constancy / orthonormal keys, a
+hand-worked fixture in ``tests/golden/``, and agreement of the two forms
+below).  No function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "qk_head_of",
+    "gated_delta_recurrence",
+    "gated_delta_decode_step",
+    "gated_delta_chunk_form",
+]
+
+
+def qk_head_of(h_v: int, h_qk: int) -> np.ndarray:
+    """Query/key head read by each value head: contiguous groups of
+    ``h_v // h_qk`` value heads share one query/key head.
+
+    The pages describe head sharing only for the attention layers (section
+    "Qwen creates three distinct workload shapes": several query heads share
+    each key/value head).  For the recurrent layer the same contiguous-group
+    convention is taken.
+    """
+    if h_qk <= 0 or h_v % h_qk != 0:
+        raise ValueError(f"h_v={h_v} must be a positive multiple of h_qk={h_qk}")
+    return np.arange(h_v) // (h_v // h_qk)
+
+
+def _as_f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check_inputs(q, k, v, g, beta, cu_seqlens, state_in):
+    q, k, v, g, beta = (_as_f64(a) for a in (q, k, v, g, beta))
+    if q.ndim != 3 or k.shape != q.shape:
+        raise ValueError("q and k must both be [T, H_qk, d_k]")
+    T, h_qk, d_k = q.shape
+    if v.ndim != 3 or v.shape[0] != T:
+        raise ValueError("v must be [T, H_v, d_v]")
+    h_v, d_v = v.shape[1], v.shape[2]
+    if g.shape != (T, h_v) or beta.shape != (T, h_v):
+        raise ValueError("g and beta must be [T, H_v]")
+    if not np.all(np.isfinite(g)):
+        raise ValueError("g (log-gate) must be finite")
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must be non-decreasing, start at 0 and end at T")
+    n = cu.size - 1
+    if state_in is None:
+        s0 = np.zeros((n, h_v, d_v, d_k), dtype=np.float64)
+    else:
+        s0 = _as_f64(state_in)
+        if s0.shape != (n, h_v, d_v, d_k):
+            raise ValueError(f"state_in must be [{n}, {h_v}, {d_v}, {d_k}]")
+    return q, k, v, g, beta, cu, s0, qk_head_of(h_v, h_qk)
+
+
+def gated_delta_recurrence(q, k, v, g, beta, cu_seqlens=None, state_in=None):
+    """Token-by-token gated delta rule over a packed, ragged batch (fp64).
+
+    Follows the prose of "Qwen creates three distinct workload shapes" (walk
+    the tokens and carry the state) and "Keeping the recurrent state on chip"
+    (the state is a matrix) with the gated delta rule stated in the module
+    header.  The update is applied in its expanded rank-one form
+
+        p = S k,  u = beta (v - alpha p),  S <- alpha S + u k^T,  o = S q,
+
+    which is the same algebra as alpha S (I - beta k k^T) + beta v k^T.
+
+    Args (widened to fp64):
+      q, k: [T, H_qk, d_k]; v: [T, H_v, d_v]; g, beta: [T, H_v]
+      cu_seqlens: [N+1] token offsets of the packed sequences (None = one
+        sequence of length T); zero-length sequences are allowed.
+      state_in: [N, H_v, d_v, d_k] or None (zeros).
+    Returns:
+      o: [T, H_v, d_v] fp64, state_out: [N, H_v, d_v, d_k] fp64.
+    """
+    q, k, v, g, beta, cu, s0, qmap = _check_inputs(q, k, v, g, beta, cu_seqlens, state_in)
+    T, h_v, d_v = v.shape
+    o = np.zeros((T, h_v, d_v), dtype=np.float64)
+    s_out = np.empty_like(s0)
+    for n in range(cu.size - 1):
+        S = s0[n].copy()  # [H_v, d_v, d_k]
+        for t in range(int(cu[n]), int(cu[n + 1])):
+            kt = k[t, qmap]  # [H_v, d_k]
+            qt = q[t, qmap]
+            alpha = np.exp(g[t])  # [H_v]
+            p = np.einsum("hij,hj->hi", S, kt)
+            u = beta[t][:, None] * (v[t] - alpha[:, None] * p)
+            S = alpha[:, None, None] * S + u[:, :, None] * kt[:, None, :]
+            o[t] = np.einsum("hij,hj->hi", S, qt)
+        s_out[n] = S
+    return o, s_out
+
+
+def gated_delta_decode_step(q, k, v, g, beta, state):
+    """One recurrent step per sequence for a batch of B sequences (fp64).
+
+    Decode runs one step of the recurrence per new token; its cost is the
+    bytes moved per token (section "Decode: minimize bytes moved per token",
+    es: "Decodificación: minimizar los bytes transferidos por token").
+
+    Args: q, k: [B, H_qk, d_k]; v: [B, H_v, d_v]; g, beta: [B, H_v];
+          state: [B, H_v, d_v, d_k].
+    Returns: o [B, H_v, d_v], new state [B, H_v, d_v, d_k] (fp64).
+    """
+    q = _as_f64(q)
+    B = q.shape[0]
+    cu = np.arange(B + 1, dtype=np.int64)
+    return gated_delta_recurrence(q, k, v, g, beta, cu_seqlens=cu, state_in=state)
+
+
+def gated_delta_chunk_form(q, k, v, g, beta, chunk_size, cu_seqlens=None, state_in=None):
+    """Blockwise evaluation of the same recurrence (fp64), used only to
+    self-check the token loop.
+
+    Section "Qwen creates three distinct workload shapes" says the updates can
+    be regrouped into blocks that expose matrix operations and evaluate the
+    same computation.  The pages print no block formula; this is the one that
+    follows from unrolling the recurrence inside a block of n tokens that
+    starts from state S0.  With gamma_r = exp(G_r), unrolling gives
+    S_r = gamma_r S0 + sum_{i<=r} (gamma_r / gamma_i) u_i k_i^T and
+    u_r = beta_r (v_r - alpha_r S_{r-1} k_r); substituting the first into the
+    second yields the triangular system (I + A) U = diag(beta) V -
+    diag(beta gamma) K S0^T below, and o_r = S_r q_r gives O:
+
+      G_r   = sum_{i<=r} g_i           (log-decay inside the block)
+      A_ri  = beta_r exp(G_r - G_i) (k_r . k_i)        for i < r, else 0
+      U     = (I + A)^{-1} (diag(beta) V - diag(beta exp(G)) K S0^T)
+      O     = diag(exp(G)) Q S0^T + (M * Q K^T) U,  M_ri = exp(G_r - G_i), i <= r
+      S_end = exp(G_{n-1}) S0 + (diag(exp(G_{n-1} - G)) U)^T K
+
+    Blocks start at each sequence's first token; the last one may be short.
+    ``np.linalg.solve`` serves as the triangular solve.
+    """
+    if chunk_size < 1:
+        raise ValueError("chunk_size must be >= 1")
+    q, k, v, g, beta, cu, s0, qmap = _check_inputs(q, k, v, g, beta, cu_seqlens, state_in)
+    T, h_v, d_v = v.shape
+    o = np.zeros((T, h_v, d_v), dtype=np.float64)
+    s_out = np.empty_like(s0)
+    for n in range(cu.size - 1):
+        for h in range(h_v):
+            S = s0[n, h].copy()  # [d_v, d_k]
+            j = qmap[h]
+            for c0 in range(int(cu[n]), int(cu[n + 1]), chunk_size):
+                c1 = min(c0 + chunk_size, int(cu[n + 1]))
+                Kc, Qc, Vc = k[c0:c1, j], q[c0:c1, j], v[c0:c1, h]
+                bc, G = beta[c0:c1, h], np.cumsum(g[c0:c1, h])
+                nb = c1 - c0
+                D = G[:, None] - G[None, :]
+                lower_strict = np.tril(np.ones((nb, nb), dtype=bool), -1)
+                lower = np.tril(np.ones((nb, nb), dtype=bool), 0)
+                decay = np.where(lower, np.exp(np.where(lower, D, 0.0)), 0.0)
+                A = np.where(lower_strict, bc[:, None] * decay * (Kc @ Kc.T), 0.0)
+                rhs = bc[:, None] * Vc - (bc * np.exp(G))[:, None] * (Kc @ S.T)
+                U = np.linalg.solve(np.eye(nb) + A, rhs)
+                o[c0:c1, h] = np.exp(G)[:, None] * (Qc @ S.T) + (decay * (Qc @ Kc.T)) @ U
+                S = np.exp(G[-1]) * S + (np.exp(G[-1] - G)[:, None] * U).T @ Kc
+            s_out[n, h] = S
+    return o, s_out

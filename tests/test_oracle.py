@@ -1,0 +1,360 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: the literal
+matrix form of the gated delta rule, exact rational arithmetic, a hand-worked
+fixture, the delta-rule invariant, closed forms, and the independently derived
+block form.  The recurrence is the one Perplexity's "Optimizing on-device
+inference for Apple Silicon" describes in prose (section "Qwen creates three
+distinct workload shapes"); the carried-state property is from section
+"Bounding scratch memory by chunking the prompt".
+
+The last tests plant plausible mistakes in copies of the oracle's token loop
+and check that at least one pin fails for each.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import (gated_delta_chunk_form, gated_delta_decode_step,
+                    gated_delta_recurrence, qk_head_of)
+from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(x, r):
+    return np.linalg.norm(np.ravel(x - r)) / max(np.linalg.norm(np.ravel(r)), 1e-300)
+
+
+def rand_problem(seed, T, h_qk, h_v, d_k, d_v, unit_k=True, gate_shift=0.0, state=True, N=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, h_qk, d_k))
+    k = rng.standard_normal((T, h_qk, d_k))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, h_v, d_v))
+    g = -np.logaddexp(0, rng.standard_normal((T, h_v)) + gate_shift)
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, h_v))))
+    n = 1 if N is None else N
+    s0 = rng.standard_normal((n, h_v, d_v, d_k)) * 0.5 if state else None
+    return q, k, v, g, beta, s0
+
+
+# ---------------------------------------------------------------- P1 brute force
+def literal_matrix_form(q, k, v, g, beta, s0):
+    """S_t = alpha S_{t-1} (I - beta k k^T) + beta v k^T with explicit d_k x d_k
+    transition matrices; one sequence."""
+    T, h_qk, d_k = q.shape
+    h_v = v.shape[1]
+    grp = h_v // h_qk
+    o = np.zeros(v.shape)
+    S_all = s0[0].copy()
+    for h in range(h_v):
+        S = S_all[h]
+        for t in range(T):
+            kk = k[t, h // grp][:, None]
+            P = math.exp(g[t, h]) * (np.eye(d_k) - beta[t, h] * (kk @ kk.T))
+            S = S @ P + beta[t, h] * (v[t, h][:, None] @ kk.T)
+            o[t, h] = S @ q[t, h // grp]
+        S_all[h] = S
+    return o, S_all[None]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_p1_brute_force_literal_form(seed):
+    args = rand_problem(seed, 12, 2, 4, 5, 3, unit_k=(seed % 2 == 0))
+    o_ref, s_ref = literal_matrix_form(*args)
+    o, s = gated_delta_recurrence(*args[:5], state_in=args[5])
+    assert rel(o, o_ref) < 1e-13 and rel(s, s_ref) < 1e-13
+
+
+# ---------------------------------------------------------------- P2 exact rationals
+def fraction_recurrence(q, k, v, alpha, beta, s0):
+    """Exact rational evaluation of the literal matrix form (one head)."""
+    T, d_k = len(k), len(k[0])
+    d_v = len(v[0])
+    S = [row[:] for row in s0]
+    outs = []
+    for t in range(T):
+        P = [[alpha[t] * ((1 if i == j else 0) - beta[t] * k[t][i] * k[t][j]) for j in range(d_k)]
+             for i in range(d_k)]
+        S = [[sum(S[a][i] * P[i][j] for i in range(d_k)) + beta[t] * v[t][a] * k[t][j]
+              for j in range(d_k)] for a in range(d_v)]
+        outs.append([sum(S[a][j] * q[t][j] for j in range(d_k)) for a in range(d_v)])
+    return outs, S
+
+
+def test_p2_exact_rationals():
+    rng = np.random.default_rng(7)
+    T, d_k, d_v = 6, 3, 2
+    fr = lambda lo, hi: Fraction(int(rng.integers(lo, hi)), int(rng.integers(1, 9)))
+    q = [[fr(-9, 10) for _ in range(d_k)] for _ in range(T)]
+    k = [[fr(-9, 10) for _ in range(d_k)] for _ in range(T)]  # not unit norm
+    v = [[fr(-9, 10) for _ in range(d_v)] for _ in range(T)]
+    alpha = [Fraction(int(rng.integers(1, 8)), 8) for _ in range(T)]
+    beta = [Fraction(int(rng.integers(0, 9)), 8) for _ in range(T)]
+    s0 = [[fr(-5, 6) for _ in range(d_k)] for _ in range(d_v)]
+    o_ex, s_ex = fraction_recurrence(q, k, v, alpha, beta, s0)
+    f = lambda x: np.array(x, dtype=np.float64)
+    o, s = gated_delta_recurrence(f(q)[:, None], f(k)[:, None], f(v)[:, None],
+                                  np.log(f(alpha))[:, None], f(beta)[:, None],
+                                  state_in=f(s0)[None, None])
+    assert rel(o[:, 0], f(o_ex)) < 1e-13
+    assert rel(s[0, 0], f(s_ex)) < 1e-13
+
+
+# ---------------------------------------------------------------- golden fixture
+def load_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rhs = (x.strip() for x in line.split("=", 1))
+            vals[key] = np.array([float(Fraction(x.strip())) for x in rhs.split(",")])
+    return vals
+
+
+def test_golden_hand_worked_T2():
+    gv = load_golden("hand_worked_T2.txt")
+    q = gv["q"].reshape(2, 1, 2)
+    k = gv["k"].reshape(2, 1, 2)
+    v = gv["v"].reshape(2, 1, 2)
+    g = np.log(gv["alpha"]).reshape(2, 1)
+    beta = gv["beta"].reshape(2, 1)
+    s0 = gv["S0"].reshape(1, 1, 2, 2)
+    o, s = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    np.testing.assert_allclose(o.reshape(-1), gv["o"], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(s.reshape(-1), gv["S2"], rtol=1e-14, atol=1e-14)
+    # the block form must reproduce the same fixture for every block size
+    for C in (1, 2, 3):
+        o2, s2 = gated_delta_chunk_form(q, k, v, g, beta, C, state_in=s0)
+        np.testing.assert_allclose(o2.reshape(-1), gv["o"], rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(s2.reshape(-1), gv["S2"], rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- P3 delta invariant
+def test_p3_delta_invariant():
+    """beta = 1 and unit k: the update writes v exactly at key k, so
+    S_t k_t = v_t; with q = k the output is v."""
+    q, k, v, g, beta, s0 = rand_problem(3, 20, 2, 2, 8, 5)
+    beta = np.ones_like(beta)
+    o, _ = gated_delta_recurrence(k, k, v, g, beta, state_in=s0)
+    assert np.max(np.abs(o - v)) < 1e-13
+    # and the state after every prefix satisfies S_t k_t = v_t
+    for t in (0, 7, 19):
+        _, s = gated_delta_recurrence(q[:t + 1], k[:t + 1], v[:t + 1], g[:t + 1], beta[:t + 1], state_in=s0)
+        for h in range(2):
+            assert np.max(np.abs(s[0, h] @ k[t, h] - v[t, h])) < 1e-13
+
+
+# ---------------------------------------------------------------- P4 / P5 closed forms
+def test_p4_constancy():
+    q, k, v, g, beta, s0 = rand_problem(4, 16, 2, 4, 6, 3)
+    o, s = gated_delta_recurrence(q, k, v, np.zeros_like(g), np.zeros_like(beta), state_in=s0)
+    grp = 2
+    expect = np.einsum("hij,thj->thi", s0[0], np.repeat(q, grp, axis=1))
+    assert np.array_equal(s, s0)
+    assert np.max(np.abs(o - expect)) < 1e-14
+
+
+def test_p5_pure_decay():
+    q, k, v, g, beta, s0 = rand_problem(5, 16, 2, 2, 6, 3, gate_shift=-1.0)
+    o, s = gated_delta_recurrence(q, k, v, g, np.zeros_like(beta), state_in=s0)
+    cum = np.exp(np.cumsum(g, axis=0))  # [T, H_v]
+    assert rel(s[0], cum[-1][:, None, None] * s0[0]) < 1e-14
+    expect = cum[:, :, None] * np.einsum("hij,thj->thi", s0[0], q)
+    assert rel(o, expect) < 1e-14
+
+
+# ---------------------------------------------------------------- P6 orthonormal keys
+def test_p6_orthonormal_keys():
+    """k_t = e_{pi(t)}: column pi(t) becomes alpha(1-beta) col + beta v, every
+    other column is scaled by alpha."""
+    rng = np.random.default_rng(6)
+    d_k, d_v, T = 6, 3, 6
+    perm = rng.permutation(d_k)
+    k = np.eye(d_k)[perm][:, None]
+    q = rng.standard_normal((T, 1, d_k))
+    v = rng.standard_normal((T, 1, d_v))
+    g = -rng.uniform(0.1, 2, (T, 1))
+    beta = rng.uniform(0, 1, (T, 1))
+    s0 = rng.standard_normal((1, 1, d_v, d_k))
+    S = s0[0, 0].copy()
+    for t in range(T):
+        a, b, j = math.exp(g[t, 0]), beta[t, 0], perm[t]
+        S = a * S
+        S[:, j] = (1 - b) * S[:, j] + b * v[t, 0]
+    _, s = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    assert rel(s[0, 0], S) < 1e-14
+
+
+# ---------------------------------------------------------------- P7 two forms agree
+@pytest.mark.parametrize("C", [1, 2, 3, 16, 64, 200])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 67])
+def test_p7_scan_equals_chunk_form(C, T):
+    q, k, v, g, beta, s0 = rand_problem(100 + T + C, T, 2, 4, 8, 5, gate_shift=2.0)
+    o1, s1 = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    o2, s2 = gated_delta_chunk_form(q, k, v, g, beta, C, state_in=s0)
+    assert rel(o2, o1) < 1e-12 and rel(s2, s1) < 1e-12
+
+
+def test_p7_long_strong_gate():
+    q, k, v, g, beta, s0 = rand_problem(77, 1000, 1, 2, 16, 8, gate_shift=2.0)
+    o1, s1 = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    o2, s2 = gated_delta_chunk_form(q, k, v, g, beta, 64, state_in=s0)
+    assert rel(o2, o1) < 1e-12 and rel(s2, s1) < 1e-12
+
+
+# ---------------------------------------------------------------- P8 linearity
+def test_p8_linearity():
+    q, k, v, g, beta, s0 = rand_problem(8, 24, 2, 2, 6, 4)
+    rng = np.random.default_rng(88)
+    v2, s02 = rng.standard_normal(v.shape), rng.standard_normal(s0.shape)
+    a, b = 0.7, -1.3
+    o1, s1 = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    o2, s2 = gated_delta_recurrence(q, k, v2, g, beta, state_in=s02)
+    o3, s3 = gated_delta_recurrence(q, k, a * v + b * v2, g, beta, state_in=a * s0 + b * s02)
+    assert rel(o3, a * o1 + b * o2) < 1e-12 and rel(s3, a * s1 + b * s2) < 1e-12
+    o4, s4 = gated_delta_recurrence(2.5 * q, k, v, g, beta, state_in=s0)
+    assert rel(o4, 2.5 * o1) < 1e-14 and rel(s4, s1) == 0.0
+
+
+# ---------------------------------------------------------------- P9 split / carry
+@pytest.mark.parametrize("split", [0, 1, 13, 40])
+def test_p9_split_carry(split):
+    q, k, v, g, beta, s0 = rand_problem(9, 40, 2, 4, 6, 4)
+    o, s = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    oa, sa = gated_delta_recurrence(q[:split], k[:split], v[:split], g[:split], beta[:split], state_in=s0)
+    ob, sb = gated_delta_recurrence(q[split:], k[split:], v[split:], g[split:], beta[split:], state_in=sa)
+    assert rel(np.concatenate([oa, ob]), o) < 1e-13 and rel(sb, s) < 1e-13
+
+
+# ---------------------------------------------------------------- P10 ragged batch
+def test_p10_ragged_equals_independent():
+    lens = [5, 0, 17, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, g, beta, s0 = rand_problem(10, T, 2, 4, 6, 3, N=len(lens))
+    o, s = gated_delta_recurrence(q, k, v, g, beta, cu_seqlens=cu, state_in=s0)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        on, sn = gated_delta_recurrence(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], state_in=s0[n:n + 1])
+        assert np.array_equal(o[a:b], on) and np.array_equal(s[n], sn[0])
+    assert np.array_equal(s[1], s0[1])  # zero-length sequence passes its state through
+    oc, sc = gated_delta_chunk_form(q, k, v, g, beta, 4, cu_seqlens=cu, state_in=s0)
+    assert rel(oc, o) < 1e-12 and rel(sc, s) < 1e-12
+
+
+# ---------------------------------------------------------------- P11 head sharing
+def test_p11_gqa_mapping():
+    q, k, v, g, beta, s0 = rand_problem(11, 10, 2, 6, 5, 3)
+    o, s = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    qr, kr = np.repeat(q, 3, axis=1), np.repeat(k, 3, axis=1)
+    o2, s2 = gated_delta_recurrence(qr, kr, v, g, beta, state_in=s0)
+    assert np.array_equal(o, o2) and np.array_equal(s, s2)
+    assert list(qk_head_of(6, 2)) == [0, 0, 0, 1, 1, 1]
+
+
+# ---------------------------------------------------------------- P12 decode == prefill
+def test_p12_decode_equals_prefill():
+    q, k, v, g, beta, s0 = rand_problem(12, 7, 2, 4, 6, 3)
+    o, s = gated_delta_recurrence(q, k, v, g, beta, state_in=s0)
+    S = s0
+    for t in range(7):
+        ot, S = gated_delta_decode_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], beta[t:t + 1], S)
+        assert rel(ot[0], o[t]) < 1e-13
+    assert rel(S, s) < 1e-13
+    # batched decode: B sequences at once == each alone
+    B = 3
+    qb, kb, vb, gb, bb, sb = rand_problem(13, B, 2, 4, 6, 3, N=B)
+    ob, snew = gated_delta_decode_step(qb, kb, vb, gb, bb, sb)
+    for i in range(B):
+        oi, si = gated_delta_recurrence(qb[i:i + 1], kb[i:i + 1], vb[i:i + 1], gb[i:i + 1], bb[i:i + 1],
+                                        state_in=sb[i:i + 1])
+        assert np.array_equal(ob[i], oi[0]) and np.array_equal(snew[i], si[0])
+
+
+# ---------------------------------------------------------------- P13 rounding floor
+def test_p13_bf16_rounding_floor():
+    """Rounding the fp64 output to bf16 costs ~1e-3 relative (per head,
+    Frobenius), so a 3e-3 bound on bf16 outputs is attainable."""
+    inp = make_prefill([256], 2, 4, 32, 32, "bf16", 2.0, None, seed=3)
+    o, _ = gated_delta_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    ob = round_to_bf16(o.astype(np.float32)).astype(np.float64)
+    worst = max(rel(ob[:, h], o[:, h]) for h in range(4))
+    assert 5e-4 < worst < 2e-3
+
+
+def test_round_to_bf16_ties_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e-39], dtype=np.float32)
+    r = round_to_bf16(x)
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == np.float32(1.0 + 4 * 2 ** -8) and r[3] == -2.5
+    bits = r.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+
+
+def test_config0_shapes_and_distributions():
+    inp = config(0)
+    assert inp.q.shape == (64, 2, 16) and inp.v.shape == (64, 2, 16) and inp.chunk_size == 16
+    assert np.allclose(np.linalg.norm(inp.q, axis=-1), 1, atol=1e-6)
+    assert np.all(inp.g < 0) and np.all((inp.beta > 0) & (inp.beta < 1))
+    o1, s1 = gated_delta_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    o2, s2 = gated_delta_chunk_form(inp.q, inp.k, inp.v, inp.g, inp.beta, 16)
+    assert rel(o2, o1) < 1e-12 and rel(s2, s1) < 1e-12
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _mutant(kind):
+    """A copy of the token loop with one plausible mistake planted in it."""
+    def run(q, k, v, g, beta, cu_seqlens=None, state_in=None):
+        T, h_qk, d_k = q.shape
+        h_v, d_v = v.shape[1], v.shape[2]
+        qmap = np.arange(h_v) // (h_v // h_qk)
+        if kind == "interleaved_heads":
+            qmap = np.arange(h_v) % h_qk
+        S = np.zeros((h_v, d_v, d_k)) if state_in is None else np.array(state_in[0], dtype=float)
+        o = np.zeros((T, h_v, d_v))
+        for t in range(T):
+            kt, qt = k[t, qmap], q[t, qmap]
+            a = np.exp(g[t])
+            p = np.einsum("hij,hj->hi", S, kt)
+            if kind == "alpha_after_delta":
+                u = beta[t][:, None] * (v[t] - p)
+            elif kind == "sign":
+                u = beta[t][:, None] * (v[t] + a[:, None] * p)
+            elif kind == "transposed_state":
+                p = np.einsum("hji,hj->hi", S, kt) if d_v == d_k else p
+                u = beta[t][:, None] * (v[t] - a[:, None] * p)
+            else:
+                u = beta[t][:, None] * (v[t] - a[:, None] * p)
+            Sn = a[:, None, None] * S + u[:, :, None] * kt[:, None, :]
+            if kind == "no_decay":
+                Sn = S + u[:, :, None] * kt[:, None, :]
+            o[t] = np.einsum("hij,hj->hi", S if kind == "pre_update_output" else Sn, qt)
+            S = Sn
+        return o, S[None]
+    return run
+
+
+@pytest.mark.parametrize("kind", ["alpha_after_delta", "sign", "transposed_state", "no_decay",
+                                  "pre_update_output", "interleaved_heads"])
+def test_pins_catch_planted_mistakes(kind):
+    fn = _mutant(kind)
+    failures = 0
+    # golden fixture
+    gv = load_golden("hand_worked_T2.txt")
+    o, s = fn(gv["q"].reshape(2, 1, 2), gv["k"].reshape(2, 1, 2), gv["v"].reshape(2, 1, 2),
+              np.log(gv["alpha"]).reshape(2, 1), gv["beta"].reshape(2, 1), state_in=gv["S0"].reshape(1, 1, 2, 2))
+    failures += not (np.allclose(o.reshape(-1), gv["o"]) and np.allclose(s.reshape(-1), gv["S2"]))
+    # brute force on the literal form with shared heads
+    args = rand_problem(1, 12, 2, 4, 5, 5)
+    o_ref, s_ref = literal_matrix_form(*args)
+    o, s = fn(*args[:5], state_in=args[5])
+    failures += not (rel(o, o_ref) < 1e-12 and rel(s, s_ref) < 1e-12)
+    assert failures >= 1
