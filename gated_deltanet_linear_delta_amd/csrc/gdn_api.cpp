@@ -1,0 +1,164 @@
+// C ABI of libgdn.so (declared in include/gdn.h): host-side validation and
+// dispatch.  Nothing here touches device memory; every check happens before
+// the first launch, and a failed check enqueues nothing.
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdn_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status_t fail(gdn_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status_t ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by all entry points.  Sizes are bounded so that every
+// element index of the largest tensor fits in int32 arithmetic on the
+// (sequence, head, row) granularity the kernels use.
+gdn_status_t check_dims(int n, int t, int h_qk, int h_v, int d_k, int d_v, gdn_dtype_t io, const char* what) {
+  if (n < 1) return fail(GDN_ERR_INVALID, "%s: num_seqs/batch must be >= 1 (got %d)", what, n);
+  if (t < 0) return fail(GDN_ERR_INVALID, "%s: total_tokens must be >= 0 (got %d)", what, t);
+  if (h_qk < 1 || h_v < 1 || h_v % h_qk != 0)
+    return fail(GDN_ERR_INVALID, "%s: h_v (%d) must be a positive multiple of h_qk (%d)", what, h_v, h_qk);
+  if (io != GDN_DTYPE_F32 && io != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID, "%s: io_dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16", what);
+  if (!supported_dim(d_k) || !supported_dim(d_v))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: d_k=%d, d_v=%d; supported sizes are 16, 32, 64, 128", what, d_k, d_v);
+  const long long rows = (long long)n * h_v * d_v;
+  if (rows > (1ll << 30)) return fail(GDN_ERR_UNSUPPORTED, "%s: num_seqs * h_v * d_v too large", what);
+  if ((long long)t * h_v > (1ll << 31) - 1 || (long long)t * h_qk > (1ll << 31) - 1)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: total_tokens * heads exceeds int32", what);
+  return GDN_OK;
+}
+
+gdn_status_t check_ptrs(const char* what, std::initializer_list<std::pair<const char*, const void*>> ps) {
+  for (auto& p : ps) {
+    if (!p.second) return fail(GDN_ERR_INVALID, "%s: %s is NULL", what, p.first);
+    if (!aligned16(p.second)) return fail(GDN_ERR_INVALID, "%s: %s is not 16-byte aligned", what, p.first);
+  }
+  return GDN_OK;
+}
+
+gdn_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+gdn::Dims dims_of(const gdn_shape_t* s) {
+  return gdn::Dims{s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, s->io_dtype == GDN_DTYPE_BF16};
+}
+
+gdn_status_t check_prefill(const gdn_shape_t* s, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* cu, const float* state_in, const void* out,
+                           const float* state_out, const char* what) {
+  if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
+  gdn_status_t st = check_dims(s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, s->io_dtype, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"q", q}, {"k", k}, {"v", v}, {"g", g}, {"beta", beta}, {"cu_seqlens", cu},
+                         {"out", out}, {"state_out", state_out}});
+  if (st != GDN_OK) return st;
+  if (state_in && !aligned16(state_in)) return fail(GDN_ERR_INVALID, "%s: state_in is not 16-byte aligned", what);
+  if (out == q || out == k || out == v || out == state_in || out == state_out)
+    return fail(GDN_ERR_INVALID, "%s: out aliases another tensor", what);
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status_t status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID: return "GDN_ERR_INVALID";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status_t gdn_prefill_scan(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const int32_t* cu_seqlens,
+                              const float* state_in, void* out, float* state_out, void* stream) {
+  gdn_status_t st =
+      check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, "gdn_prefill_scan");
+  if (st != GDN_OK) return st;
+  return launched(gdn::launch_scan(dims_of(shape), q, k, v, g, beta, cu_seqlens, state_in, out, state_out,
+                                   static_cast<hipStream_t>(stream)),
+                  "gdn_prefill_scan");
+}
+
+size_t gdn_prefill_chunked_workspace(const gdn_shape_t* shape, int32_t chunk_size) {
+  if (!shape || (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)) return 0;
+  if (check_dims(shape->num_seqs, shape->total_tokens, shape->h_qk, shape->h_v, shape->d_k, shape->d_v,
+                 shape->io_dtype, "gdn_prefill_chunked_workspace") != GDN_OK)
+    return 0;
+  return gdn::chunked_workspace_bytes(dims_of(shape), chunk_size);
+}
+
+gdn_status_t gdn_prefill_chunked(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const int32_t* cu_seqlens,
+                                 const float* state_in, void* out, float* state_out, int32_t chunk_size,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "gdn_prefill_chunked";
+  gdn_status_t st = check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, what);
+  if (st != GDN_OK) return st;
+  if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: chunk_size %d; supported sizes are 16, 32, 64", what, chunk_size);
+  const gdn::Dims d = dims_of(shape);
+  if (gdn::chunked_max_chunks(d, chunk_size) > size_t(1u << 31) - 1)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: too many chunks", what);
+  const size_t need = gdn::chunked_workspace_bytes(d, chunk_size);
+  if (!workspace) return fail(GDN_ERR_INVALID, "%s: workspace is NULL", what);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GDN_ERR_INVALID, "%s: workspace is not 256-byte aligned", what);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", what, workspace_bytes, need);
+  return launched(gdn::launch_chunked(d, chunk_size, q, k, v, g, beta, cu_seqlens, state_in, out, state_out,
+                                      workspace, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                             gdn_dtype_t io_dtype, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* state_in, void* out, float* state_out,
+                             void* stream) {
+  const char* what = "gdn_decode_step";
+  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, io_dtype, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"q", q}, {"k", k}, {"v", v}, {"g", g}, {"beta", beta}, {"state_in", state_in},
+                         {"out", out}, {"state_out", state_out}});
+  if (st != GDN_OK) return st;
+  if (out == q || out == k || out == v || out == state_in || out == state_out)
+    return fail(GDN_ERR_INVALID, "%s: out aliases another tensor", what);
+  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, io_dtype == GDN_DTYPE_BF16};
+  return launched(gdn::launch_decode(d, q, k, v, g, beta, state_in, out, state_out,
+                                     static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Decode step of the gated delta rule: one token per sequence.
+//
+// Perplexity, "Optimizing on-device inference for Apple Silicon", section
+// "Decode: minimize bytes moved per token": at batch 1 a decode step is bound
+// by the bytes it moves.  Here those bytes are almost all the fp32 state
+// (2 * d_v * d_k * 4 per head), so the kernel reads every state row once and
+// writes it once, fully coalesced, with the two dot products S.k and S.q
+// reduced across lanes by DPP instead of LDS.  The update is the rank-one
+// form of the gated delta rule:
+//   p = S k,  u = beta (v - alpha p),  S' = alpha S + u k^T,
+//   o = S' q = alpha (S q) + u (k . q),      alpha = exp(g).
+//
+// Layout: a state row (fixed value index i) is d_k contiguous floats.  LPR =
+// d_k / 8 lanes share a row, each holding 8 floats as two float4 at column
+// offsets 4*l and d_k/2 + 4*l, so every load instruction covers contiguous
+// 16*LPR-byte runs.  A workgroup holds 16 rows (16 * LPR threads).
+#include "gdn_common.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+template <typename IO>
+__device__ __forceinline__ void load4(const IO* p, float* x) {
+  if constexpr (sizeof(IO) == 4) {
+    f4 t = *reinterpret_cast<const f4*>(p);
+    x[0] = t[0]; x[1] = t[1]; x[2] = t[2]; x[3] = t[3];
+  } else {
+    uint2 t = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(t.x << 16);
+    x[1] = __uint_as_float(t.x & 0xffff0000u);
+    x[2] = __uint_as_float(t.y << 16);
+    x[3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+}
+
+template <typename IO, int DK>
+__global__ __launch_bounds__(16 * (DK / 8)) void decode_kernel(
+    int total_rows, int h_qk, int h_v, int d_v, const IO* __restrict__ q, const IO* __restrict__ k,
+    const IO* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    const float* s_in, IO* __restrict__ out, float* s_out) {
+  constexpr int LPR = DK / 8;
+  const int l = threadIdx.x % LPR;
+  const int row = blockIdx.x * 16 + threadIdx.x / LPR;
+  if (row >= total_rows) return;  // whole row groups leave together
+  const int i = row % d_v;
+  const int bh = row / d_v;  // b * h_v + h
+  const int h = bh % h_v;
+  const int b = bh / h_v;
+  const int j = h / (h_v / h_qk);
+  const int c0 = 4 * l, c1 = DK / 2 + 4 * l;
+
+  const float* sr = s_in + size_t(row) * DK;
+  f4 sa = *reinterpret_cast<const f4*>(sr + c0);
+  f4 sb = *reinterpret_cast<const f4*>(sr + c1);
+  const IO* kp = k + (size_t(b) * h_qk + j) * DK;
+  const IO* qp = q + (size_t(b) * h_qk + j) * DK;
+  float kv[8], qv[8];
+  load4(kp + c0, kv);
+  load4(kp + c1, kv + 4);
+  load4(qp + c0, qv);
+  load4(qp + c1, qv + 4);
+  const float alpha = expf(g[bh]);
+  const float bt = beta[bh];
+  const float vi = io_traits<IO>::load(v + size_t(bh) * d_v + i);
+
+  float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f, kq0 = 0.f, kq1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p0 = fmaf(s[e], kv[e], p0);
+    p1 = fmaf(s[e + 4], kv[e + 4], p1);
+    r0 = fmaf(s[e], qv[e], r0);
+    r1 = fmaf(s[e + 4], qv[e + 4], r1);
+    kq0 = fmaf(kv[e], qv[e], kq0);
+    kq1 = fmaf(kv[e + 4], qv[e + 4], kq1);
+  }
+  const float p = sum_lanes<LPR>(p0 + p1);
+  const float r = sum_lanes<LPR>(r0 + r1);
+  const float kq = sum_lanes<LPR>(kq0 + kq1);
+  const float u = bt * (vi - alpha * p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], u * kv[e]);
+  float* so = s_out + size_t(row) * DK;
+  *reinterpret_cast<f4*>(so + c0) = f4{s[0], s[1], s[2], s[3]};
+  *reinterpret_cast<f4*>(so + c1) = f4{s[4], s[5], s[6], s[7]};
+  if (l == 0) io_traits<IO>::store(out + size_t(bh) * d_v + i, fmaf(alpha, r, u * kq));
+}
+
+template <typename IO, int DK>
+static hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const float* s_in, void* out, float* s_out,
+                                  hipStream_t st) {
+  const int rows = d.num_seqs * d.h_v * d.d_v;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((rows + 15) / 16), block(16 * (DK / 8));
+  hipLaunchKernelGGL((decode_kernel<IO, DK>), grid, block, 0, st, rows, d.h_qk, d.h_v, d.d_v,
+                     static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g, beta,
+                     s_in, static_cast<IO*>(out), s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Dims& d, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* s_in, void* out, float* s_out, hipStream_t st) {
+#define GDN_DEC(IO, DK) return launch_decode_t<IO, DK>(d, q, k, v, g, beta, s_in, out, s_out, st)
+  if (d.bf16) {
+    switch (d.d_k) {
+      case 16: GDN_DEC(uint16_t, 16);
+      case 32: GDN_DEC(uint16_t, 32);
+      case 64: GDN_DEC(uint16_t, 64);
+      case 128: GDN_DEC(uint16_t, 128);
+    }
+  } else {
+    switch (d.d_k) {
+      case 16: GDN_DEC(float, 16);
+      case 32: GDN_DEC(float, 32);
+      case 64: GDN_DEC(float, 64);
+      case 128: GDN_DEC(float, 128);
+    }
+  }
+#undef GDN_DEC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

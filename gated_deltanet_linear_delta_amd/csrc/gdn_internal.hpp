@@ -1,0 +1,32 @@
+// Host-side launcher declarations shared by the C ABI (gdn_api.cpp) and the
+// kernel translation units.  Every launcher assumes its arguments were
+// validated by the caller and only enqueues work on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Dims {
+  int num_seqs, total_tokens, h_qk, h_v, d_k, d_v;
+  bool bf16;  // io dtype: bf16 if true, fp32 otherwise
+};
+
+// Decode: `batch` sequences, one token each.
+hipError_t launch_decode(const Dims& d, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* s_in, void* out, float* s_out, hipStream_t st);
+
+// Prefill by direct token scan.
+hipError_t launch_scan(const Dims& d, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const int32_t* cu, const float* s_in, void* out, float* s_out,
+                       hipStream_t st);
+
+// Chunked prefill: workspace layout and the three launches.
+size_t chunked_max_chunks(const Dims& d, int chunk);
+size_t chunked_workspace_bytes(const Dims& d, int chunk);
+hipError_t launch_chunked(const Dims& d, int chunk, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const int32_t* cu, const float* s_in, void* out,
+                          float* s_out, void* workspace, hipStream_t st);
+
+}  // namespace gdn

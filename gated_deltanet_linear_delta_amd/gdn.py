@@ -1,0 +1,206 @@
+"""Python binding of libgdn.so: argument marshalling only.
+
+Every function takes torch tensors on the GPU, checks their dtypes, shapes and
+contiguity, and passes raw device pointers and the current HIP stream to the
+C ABI declared in include/gdn.h.  All arithmetic runs in the library's HIP
+kernels; there is no fallback.  If libgdn.so is missing or does not load,
+every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
+
+GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+EXPORTS = ("gdn_prefill_scan", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace", "gdn_decode_step",
+           "gdn_status_string", "gdn_last_error")
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("h_qk", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libgdn.so once and declare its signatures; raises if it is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} not found: build it with `python -m gated_deltanet_linear_delta_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    shp = ctypes.POINTER(GdnShape)
+    lib.gdn_prefill_scan.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, vp]
+    lib.gdn_prefill_scan.restype = ctypes.c_int
+    lib.gdn_prefill_chunked.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, vp, ctypes.c_size_t, vp]
+    lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_workspace.argtypes = [shp, i32]
+    lib.gdn_prefill_chunked_workspace.restype = ctypes.c_size_t
+    lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f, f, vp, f, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        lib = load_library()
+        name = lib.gdn_status_string(status).decode()
+        raise GdnError(status, f"{name}: {lib.gdn_last_error().decode()}")
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, not {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in):
+    io = _io_dtype(q)
+    T, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    _need(q, "q", q.dtype, (T, h_qk, d_k))
+    _need(k, "k", q.dtype, (T, h_qk, d_k))
+    _need(v, "v", q.dtype, (T, h_v, d_v))
+    _need(g, "g", torch.float32, (T, h_v))
+    _need(beta, "beta", torch.float32, (T, h_v))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (N, h_v, d_v, d_k))
+    return GdnShape(N, T, h_qk, h_v, d_k, d_v, io)
+
+
+def _outputs(shape: GdnShape, like, out, state_out):
+    if out is None:
+        out = torch.empty((shape.total_tokens, shape.h_v, shape.d_v), dtype=like.dtype, device=like.device)
+    else:
+        _need(out, "out", like.dtype, (shape.total_tokens, shape.h_v, shape.d_v))
+    sshape = (shape.num_seqs, shape.h_v, shape.d_v, shape.d_k)
+    if state_out is None:
+        state_out = torch.empty(sshape, dtype=torch.float32, device=like.device)
+    else:
+        _need(state_out, "state_out", torch.float32, sshape)
+    return out, state_out
+
+
+def prefill_scan(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, stream=None):
+    """Direct token scan (gdn_prefill_scan).  Returns (out, state_out)."""
+    lib = load_library()
+    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+    out, state_out = _outputs(shape, q, out, state_out)
+    _check(lib.gdn_prefill_scan(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
+    return out, state_out
+
+
+def chunked_workspace_bytes(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype=GDN_DTYPE_BF16, chunk_size=64):
+    lib = load_library()
+    shape = GdnShape(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype)
+    return int(lib.gdn_prefill_chunked_workspace(ctypes.byref(shape), chunk_size))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of at least nbytes."""
+    return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned_ptr(ws: torch.Tensor):
+    p = ws.data_ptr()
+    return (p + 255) // 256 * 256, ws.numel() - ((p + 255) // 256 * 256 - p)
+
+
+def prefill_chunked(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, chunk_size=64,
+                    workspace=None, stream=None):
+    """Chunked prefill (gdn_prefill_chunked).  Returns (out, state_out).
+    ``workspace`` is a uint8 device tensor from alloc_workspace (allocated
+    here if None)."""
+    lib = load_library()
+    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+    out, state_out = _outputs(shape, q, out, state_out)
+    need = int(lib.gdn_prefill_chunked_workspace(ctypes.byref(shape), int(chunk_size)))
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    wp, wn = _aligned_ptr(workspace)
+    _check(lib.gdn_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
+                                   ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)), _stream(stream)))
+    return out, state_out
+
+
+def decode_step(q, k, v, g, beta, state_in, out=None, state_out=None, stream=None):
+    """One recurrent step per sequence (gdn_decode_step).  q, k [B, h_qk, d_k];
+    v [B, h_v, d_v]; g, beta [B, h_v]; state_in [B, h_v, d_v, d_k].
+    ``state_out`` may be ``state_in`` for an in-place update.  Returns
+    (out, state_out)."""
+    lib = load_library()
+    io = _io_dtype(q)
+    B, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, (B, h_qk, d_k))
+    _need(q, "q", q.dtype, (B, h_qk, d_k))
+    _need(v, "v", q.dtype, (B, h_v, d_v))
+    _need(g, "g", torch.float32, (B, h_v))
+    _need(beta, "beta", torch.float32, (B, h_v))
+    _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
+    if out is None:
+        out = torch.empty((B, h_v, d_v), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, h_v, d_v))
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    else:
+        _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
+    _check(lib.gdn_decode_step(B, h_qk, h_v, d_k, d_v, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
+    return out, state_out

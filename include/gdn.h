@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the gated delta rule on MI355X (gfx950).
+ *
+ * The operation.  Perplexity, "Optimizing on-device inference for Apple
+ * Silicon", section "Qwen creates three distinct workload shapes", describes a
+ * Gated DeltaNet layer: a fixed-size recurrent state per head, a learned gate
+ * that decides how much of the old state is kept, and a delta update from the
+ * current token, each token depending on the previous state; prefill walks the
+ * tokens directly or regroups them into blocks.  Section "Keeping the
+ * recurrent state on chip" fixes the precisions: state and gate fp32, query
+ * and key activations bf16.  The recurrence computed here, per sequence and
+ * per value head h, is the gated delta rule
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * with S a d_v x d_k fp32 matrix.  Value head h reads query/key head
+ * h / (h_v / h_qk) (contiguous groups).  The library applies no softplus,
+ * sigmoid, normalisation or scaling to q, k, v, g or beta: callers pass g as
+ * the log of the decay (finite, normally <= 0) and beta as the write strength.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers allocated and owned by the
+ *    caller; the library never allocates or frees device memory and keeps no
+ *    pointer after returning.  Layouts are dense row-major, last index
+ *    fastest:
+ *        q, k        [T, h_qk, d_k]        io_dtype
+ *        v, out      [T, h_v,  d_v]        io_dtype
+ *        g, beta     [T, h_v]              fp32
+ *        cu_seqlens  [num_seqs + 1]        int32, cu[0] = 0, cu[N] = T,
+ *                                          non-decreasing (zero-length
+ *                                          sequences allowed)
+ *        state_in,
+ *        state_out   [num_seqs, h_v, d_v, d_k]  fp32 (d_k fastest)
+ *    Pointers must be 16-byte aligned.
+ *  - state_in may be NULL (zero initial state).  state_out may be the same
+ *    pointer as state_in (in place); no other output may alias any input.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously.  A call returns after validating its arguments on
+ *    the host and enqueueing kernels; it never synchronises the device.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    on failure the call returns GDN_ERR_INVALID or GDN_ERR_UNSUPPORTED and
+ *    enqueues nothing.  cu_seqlens lives on the device and its contents are
+ *    not checked on the host; kernels clamp every offset to [0, T], so a
+ *    malformed cu_seqlens gives meaningless results but no out-of-bounds
+ *    access.  A launch failure returns GDN_ERR_LAUNCH.  gdn_last_error()
+ *    gives a message for the last failing call on the calling thread.
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; h_v a positive multiple
+ *    of h_qk.  Results are deterministic (no atomics).
+ *  - Outputs in bf16 are rounded to nearest even from fp32.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID = 1,     /* null pointer, bad shape, misalignment, workspace too small */
+  GDN_ERR_UNSUPPORTED = 2, /* well-formed but outside the built sizes (d_k, d_v, chunk) */
+  GDN_ERR_LAUNCH = 3       /* the HIP runtime reported an error while enqueueing */
+} gdn_status_t;
+
+typedef enum {
+  GDN_DTYPE_F32 = 0,  /* q, k, v, out in fp32 */
+  GDN_DTYPE_BF16 = 1  /* q, k, v, out in bf16 */
+} gdn_dtype_t;
+
+typedef struct {
+  int32_t num_seqs;     /* N >= 1 packed sequences */
+  int32_t total_tokens; /* T = cu_seqlens[N] >= 0 */
+  int32_t h_qk;         /* query/key heads, >= 1 */
+  int32_t h_v;          /* value heads, a multiple of h_qk */
+  int32_t d_k;          /* key dimension: 16, 32, 64 or 128 */
+  int32_t d_v;          /* value dimension: 16, 32, 64 or 128 */
+  gdn_dtype_t io_dtype; /* dtype of q, k, v and out */
+} gdn_shape_t;
+
+/*
+ * Prefill by direct token scan: each state row stays in registers for the
+ * whole sequence and the tokens are walked in order (section "Keeping the
+ * recurrent state on chip": the state is loaded once, carried through the
+ * scan, and written back once).  Writes out[T, h_v, d_v] and
+ * state_out[N, h_v, d_v, d_k].
+ */
+gdn_status_t gdn_prefill_scan(const gdn_shape_t* shape,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const int32_t* cu_seqlens, const float* state_in,
+                              void* out, float* state_out, void* stream);
+
+/*
+ * Bytes of device workspace gdn_prefill_chunked needs for this shape and
+ * chunk size (0 if the shape or chunk size is invalid).  The bound depends
+ * only on num_seqs, total_tokens, h_v and chunk_size.
+ */
+size_t gdn_prefill_chunked_workspace(const gdn_shape_t* shape, int32_t chunk_size);
+
+/*
+ * Prefill in blocks of chunk_size tokens (section "Qwen creates three
+ * distinct workload shapes": the updates regrouped into blocks to expose
+ * matrix operations).  Same tensors and results as gdn_prefill_scan, up to
+ * rounding.  Chunks start at each sequence's first token; the last one may
+ * be short.  chunk_size must be 16, 32 or 64.  `workspace` is caller-owned
+ * device memory of at least gdn_prefill_chunked_workspace() bytes, 256-byte
+ * aligned; its contents on entry do not matter and are garbage on exit.
+ * Calls that share a workspace must be ordered on one stream.
+ */
+gdn_status_t gdn_prefill_chunked(const gdn_shape_t* shape,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, const float* state_in,
+                                 void* out, float* state_out,
+                                 int32_t chunk_size, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * One recurrent step for each of `batch` sequences (section "Decode: minimize
+ * bytes moved per token": one step per new token, bound by the bytes moved).
+ * Tensors: q, k [batch, h_qk, d_k]; v, out [batch, h_v, d_v] (io_dtype);
+ * g, beta [batch, h_v] fp32; state_in, state_out [batch, h_v, d_v, d_k] fp32.
+ * state_in must not be NULL; state_out may equal state_in (in place).
+ */
+gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                             gdn_dtype_t io_dtype,
+                             const void* q, const void* k, const void* v,
+                             const float* g, const float* beta,
+                             const float* state_in, void* out, float* state_out, void* stream);
+
+/* Static, human-readable name of a status code ("GDN_OK", ...). */
+const char* gdn_status_string(gdn_status_t status);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

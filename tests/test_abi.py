@@ -1,0 +1,117 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/gdn.h declares, sizes the workspace, and rejects bad
+arguments with the documented status before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_linear_delta_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        from gated_deltanet_linear_delta_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "GDN_OK"), (1, "GDN_ERR_INVALID"), (2, "GDN_ERR_UNSUPPORTED"), (3, "GDN_ERR_LAUNCH")]:
+        assert lib.gdn_status_string(code).decode() == name
+    assert lib.gdn_status_string(99).decode() == "GDN_ERR_UNKNOWN"
+
+
+def shape(**kw):
+    base = dict(num_seqs=1, total_tokens=4096, h_qk=16, h_v=32, d_k=128, d_v=128, io_dtype=gdn.GDN_DTYPE_BF16)
+    base.update(kw)
+    return gdn.GdnShape(**base)
+
+
+def test_workspace_size(lib):
+    s = shape()
+    # offsets (N+1 int32, padded to 256) + ceil-bound chunks * h_v * per-chunk bytes
+    per = 2 * 10 * 1024 + 4 * 64 * 4
+    max_chunks = (4096 + 1 * 63) // 64
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64) == 256 + max_chunks * 32 * per
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 48) == 0
+    assert lib.gdn_prefill_chunked_workspace(None, 64) == 0
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(shape(h_v=24)), 64) == 0
+    s2 = shape(num_seqs=32, total_tokens=73000)
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s2), 32) == \
+        (33 * 4 + 255) // 256 * 256 + (73000 + 32 * 31) // 32 * 32 * (2 * 3 * 1024 + 4 * 32 * 4)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
+
+
+def prefill_args(s, **over):
+    a = dict(q=FAKE, k=FAKE + 256, v=FAKE + 512, g=FAKE + 768, beta=FAKE + 1024, cu=FAKE + 1280,
+             state_in=None, out=FAKE + 1536, state_out=FAKE + 1792)
+    a.update(over)
+    return [ctypes.byref(s) if s is not None else None, a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"],
+            a["state_in"], a["out"], a["state_out"]]
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(s=None), 1),
+    (dict(s=shape(h_v=24)), 1),
+    (dict(s=shape(num_seqs=0)), 1),
+    (dict(s=shape(total_tokens=-1)), 1),
+    (dict(s=shape(d_k=48)), 2),
+    (dict(s=shape(d_v=256)), 2),
+    (dict(s=shape(io_dtype=7)), 1),
+    (dict(s=shape(), q=None), 1),
+    (dict(s=shape(), beta=FAKE + 4), 1),
+    (dict(s=shape(), out=FAKE), 1),
+    (dict(s=shape(), state_in=FAKE + 8), 1),
+])
+def test_prefill_rejects(lib, case, status):
+    s = case.pop("s")
+    args = prefill_args(s, **case)
+    assert lib.gdn_prefill_scan(*args, None) == status
+    assert lib.gdn_last_error().decode() != ""
+    assert lib.gdn_prefill_chunked(*args, 64, FAKE + 4096, 1 << 40, None) == status
+
+
+def test_chunked_rejects_chunk_and_workspace(lib):
+    s = shape()
+    args = prefill_args(s)
+    need = lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64)
+    assert lib.gdn_prefill_chunked(*args, 128, FAKE + 4096, need, None) == 2
+    assert lib.gdn_prefill_chunked(*args, 64, None, need, None) == 1
+    assert lib.gdn_prefill_chunked(*args, 64, FAKE + 4096 + 16, need, None) == 1
+    assert lib.gdn_prefill_chunked(*args, 64, FAKE + 4096, need - 1, None) == 1
+    assert "needs" in lib.gdn_last_error().decode()
+
+
+def test_decode_rejects(lib):
+    p = [FAKE + 256 * i for i in range(8)]
+    ok = [1, 16, 32, 128, 128, gdn.GDN_DTYPE_BF16]
+    assert lib.gdn_decode_step(0, 16, 32, 128, 128, 1, *p, None) == 1
+    assert lib.gdn_decode_step(1, 16, 24, 128, 128, 1, *p, None) == 1
+    assert lib.gdn_decode_step(1, 16, 32, 96, 128, 1, *p, None) == 2
+    bad = list(p)
+    bad[5] = None  # state_in is required for decode
+    assert lib.gdn_decode_step(*ok, *bad, None) == 1
+    bad = list(p)
+    bad[6] = p[5]  # out aliases state_in
+    assert lib.gdn_decode_step(*ok, *bad, None) == 1
