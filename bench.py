@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule layer core on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Headline: chunked prefill of one 4096-token sequence (16 query/key heads shared
+by 32 value heads, d_k = d_v = 128, bf16 q/k/v, fp32 gate and state, chunk 64).
+One step is one gdn_prefill_chunked call over that prompt with every input
+already resident in device memory; value = 4096 / (seconds per step).  The
+same JSON line also carries:
+  decode      one gdn_decode_step per token: B=1 with the state carried in
+              place (it stays cache-resident), and B=32 "cold", rotating over
+              eight state sets (512 MiB, twice the 256 MB Infinity Cache) so
+              each step streams its state from HBM; timed by replaying a HIP
+              graph of captured steps, and per kernel with HIP events;
+  scan        gdn_prefill_scan over the same 4096-token prompt (the
+              direct-scan alternative, kept for the crossover);
+  roofline    for the longest kernel of the chunked call: algorithmic bytes
+              per launch over its mean duration, from HIP events that the
+              library records on the launch stream while profiling is on;
+  cpu_baseline  the fp64 oracle timed on this host on a prefix of the same
+              prompt.
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
+
+T, HQK, HV, DK, DV, CHUNK = 4096, 16, 32, 128, 128, 64
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(t, hv=HV, hqk=HQK, dk=DK, dv=DV, c=CHUNK):
+    """Useful flops of the chunked form per call: the inter-chunk products
+    (K S^T, Q S^T, state update: 6 dk dv), the Gram products counted once per
+    query/key head (2 C dk Hqk/Hv), the causal halves of the C x C products
+    with U (C dv each for T Y and QKm U) and of T's construction (C dk), and
+    the triangular inverse (C^2 / 3), per token and value head."""
+    return t * hv * (6 * dk * dv + 2 * c * dk * hqk / hv + c * dk + 2 * c * dv + c * c / 3)
+
+
+def kernel_bytes(name, t, n_seqs, state_in):
+    """Algorithmic HBM bytes of one launch: each input read once, each output
+    written once (bf16 activations, fp32 gate, beta and state)."""
+    qk = t * 2 * HQK * DK * 2
+    vo = t * HV * DV * 2
+    gb = t * 2 * HV * 4
+    st = n_seqs * HV * DV * DK * 4
+    if name == "chunk_sweep":
+        return qk + 2 * vo + st * (2 if state_in else 1)
+    if name == "chunk_prep":
+        return qk + gb
+    if name == "chunk_offsets":
+        return 4 * (n_seqs + 1) * 2
+    if name == "scan":
+        return qk + 2 * vo + gb + st * (2 if state_in else 1)
+    raise KeyError(name)
+
+
+def decode_bytes(b):
+    return b * (2 * HV * DV * DK * 4 + 2 * HQK * DK * 2 + 2 * HV * DV * 2 + 2 * HV * 4)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def mean_by_name(records):
+    acc = {}
+    for name, ms in records:
+        acc.setdefault(name, []).append(ms)
+    return {k: (float(np.mean(v)), len(v)) for k, v in acc.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scan", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no multi-GPU path "
+              "in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_linear_delta_amd import gdn
+    from gated_deltanet_linear_delta_amd.workloads import config, make_decode
+
+    gdn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+
+    # ------------------------------------------------------------ inputs
+    log("generating the 4096-token prefill workload")
+    inp = config(2)
+
+    def io(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).to(dev)
+
+    q, k, v = io(inp.q), io(inp.k), io(inp.v)
+    g = torch.from_numpy(inp.g).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    cu = torch.tensor(inp.cu_seqlens, dtype=torch.int32, device=dev)
+    out = torch.empty((T, HV, DV), dtype=torch.bfloat16, device=dev)
+    st = torch.empty((1, HV, DV, DK), dtype=torch.float32, device=dev)
+    ws = gdn.alloc_workspace(gdn.chunked_workspace_bytes(1, T, HQK, HV, DK, DV, gdn.GDN_DTYPE_BF16, CHUNK), dev)
+
+    def prefill():
+        gdn.prefill_chunked(q, k, v, g, beta, cu, None, out=out, state_out=st, chunk_size=CHUNK, workspace=ws)
+
+    # ------------------------------------------------------------ headline: chunked prefill
+    for _ in range(W):
+        prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        prefill()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    log(f"chunked prefill: {ms_step * 1e3:.1f} us per call (wall, {K} calls)")
+
+    gdn.profile_enable(True)
+    for _ in range(K):
+        prefill()
+    torch.cuda.synchronize()
+    gdn.profile_enable(False)
+    per_kernel = mean_by_name(gdn.profile_collect())
+    call_ms = sum(m for m, _ in per_kernel.values())
+    log("chunked kernels (HIP events): " + ", ".join(f"{n} {m * 1e3:.1f} us" for n, (m, _) in per_kernel.items()))
+    dom = max(per_kernel, key=lambda n: per_kernel[n][0])
+    dom_ms = per_kernel[dom][0]
+    dom_bytes = kernel_bytes(dom, T, 1, False)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    flops = prefill_flops(T)
+    mfma_util = flops / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+
+    # ------------------------------------------------------------ decode
+    def decode_leg(B, n_sets, steps_per_graph, seed):
+        dec = make_decode(n_sets, B, HQK, HV, DK, DV, "bf16", 2.0 if B > 1 else 0.0, 0.02, seed=seed)
+        dq, dk_, dv_ = io(dec.q), io(dec.k), io(dec.v)
+        dg = torch.from_numpy(dec.g).to(dev)
+        db = torch.from_numpy(dec.beta).to(dev)
+        states = [torch.from_numpy(dec.state).to(dev).clone() for _ in range(n_sets)]
+        dout = torch.empty((B, HV, DV), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            s = i % n_sets
+            gdn.decode_step(dq[s], dk_[s], dv_[s], dg[s], db[s], states[s], out=dout, state_out=states[s])
+
+        for i in range(2 * n_sets):
+            step(i)
+        torch.cuda.synchronize()
+        # per-kernel durations from HIP events
+        gdn.profile_enable(True)
+        for i in range(steps_per_graph):
+            step(i)
+        torch.cuda.synchronize()
+        gdn.profile_enable(False)
+        kern = mean_by_name(gdn.profile_collect())["decode"][0]
+        # launch-free step time: replay a captured graph of steps
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(steps_per_graph):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(2, 2000 // steps_per_graph)
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t1) * 1e6 / (reps * steps_per_graph)
+        nbytes = decode_bytes(B)
+        return {
+            "batch": B,
+            "state_sets": n_sets,
+            "us_per_step_graph": round(us, 3),
+            "kernel_us": round(kern * 1e3, 3),
+            "tokens_per_s": round(B / (us * 1e-6), 1),
+            "bytes_per_step": nbytes,
+            "hbm_gbs": round(nbytes / (kern * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+
+    log("decode legs")
+    dec_b1 = decode_leg(1, 1, 200, 1001)
+    dec_b32 = decode_leg(32, 8, 64, 1004)
+    log(f"decode B=1: {dec_b1}")
+    log(f"decode B=32 cold: {dec_b32}")
+
+    # ------------------------------------------------------------ direct scan
+    scan = None
+    if not args.no_scan:
+        outs, sts = torch.empty_like(out), torch.empty_like(st)
+        for _ in range(2):
+            gdn.prefill_scan(q, k, v, g, beta, cu, None, out=outs, state_out=sts)
+        torch.cuda.synchronize()
+        gdn.profile_enable(True)
+        n_scan = max(3, K // 10)
+        t2 = time.perf_counter()
+        for _ in range(n_scan):
+            gdn.prefill_scan(q, k, v, g, beta, cu, None, out=outs, state_out=sts)
+        torch.cuda.synchronize()
+        scan_wall = (time.perf_counter() - t2) * 1e3 / n_scan
+        gdn.profile_enable(False)
+        scan_ms = mean_by_name(gdn.profile_collect())["scan"][0]
+        scan = {"ms_per_call": round(scan_wall, 4), "kernel_ms": round(scan_ms, 4),
+                "tokens_per_s": round(T / (scan_wall * 1e-3), 1),
+                "chunked_speedup": round(scan_wall / ms_step, 2)}
+        log(f"direct scan: {scan}")
+
+    # ------------------------------------------------------------ CPU baseline: the oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gated_delta_recurrence
+        n_tok = 32
+        t3 = time.perf_counter()
+        gated_delta_recurrence(inp.q[:n_tok], inp.k[:n_tok], inp.v[:n_tok], inp.g[:n_tok], inp.beta[:n_tok])
+        per_tok = (time.perf_counter() - t3) / n_tok
+        n_tok = int(min(T, max(64, args.cpu_seconds / per_tok)))
+        t3 = time.perf_counter()
+        gated_delta_recurrence(inp.q[:n_tok], inp.k[:n_tok], inp.v[:n_tok], inp.g[:n_tok], inp.beta[:n_tok])
+        el = time.perf_counter() - t3
+        cpu = {"value": round(n_tok / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_tok} of the {T} prompt tokens, all 32 value heads, fp64 NumPy token loop "
+                         f"({el:.1f} s)",
+               "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": "GDN prefill tokens/s @T=4096 (MFMA util) + decode tokens/s (HBM GB/s frac)",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule chunked prefill, 1 x 4096 tokens, 16 qk / 32 v heads, "
+                               "d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 gate/state, zero initial state",
+                   "batch": 1, "seq_len": T, "h_qk": HQK, "h_v": HV, "d_k": DK, "d_v": DV, "chunk": CHUNK},
+        "mfma_util": round(mfma_util, 4),
+        "algorithmic_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "kernels_us": {n: round(m * 1e3, 2) for n, (m, _) in per_kernel.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
+        "decode": {"b1_warm": dec_b1, "b32_cold": dec_b32},
+        "scan": scan,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

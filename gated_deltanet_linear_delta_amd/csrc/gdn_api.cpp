@@ -5,9 +5,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "gdn_internal.hpp"
 
@@ -85,9 +88,72 @@ gdn_status_t check_prefill(const gdn_shape_t* s, const void* q, const void* k, c
   return GDN_OK;
 }
 
+// ---------------------------------------------------------------- profiling
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfRecord> g_prof;
+
 }  // namespace
 
+namespace gdn {
+
+Prof::Prof(const char* name, hipStream_t st) : name_(name), st_(st) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  if (hipEventCreate(&start_) != hipSuccess) {
+    start_ = nullptr;
+    return;
+  }
+  if (hipEventRecord(start_, st_) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    start_ = nullptr;
+  }
+}
+
+Prof::~Prof() {
+  if (!start_) return;
+  hipEvent_t stop = nullptr;
+  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, st_) != hipSuccess) {
+    if (stop) (void)hipEventDestroy(stop);
+    (void)hipEventDestroy(start_);
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({name_, start_, stop});
+}
+
+}  // namespace gdn
+
 extern "C" {
+
+gdn_status_t gdn_profile_enable(int enabled) {
+  g_prof_on.store(enabled != 0);
+  return ok();
+}
+
+int gdn_profile_collect(const char** names, float* ms, int cap) {
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  int n = int(recs.size()), rc = n;
+  for (int i = 0; i < n; ++i) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, recs[i].start, recs[i].stop) != hipSuccess) rc = -1;
+    if (i < cap) {
+      if (names) names[i] = recs[i].name;
+      if (ms) ms[i] = t;
+    }
+    (void)hipEventDestroy(recs[i].start);
+    (void)hipEventDestroy(recs[i].stop);
+  }
+  return rc;
+}
+
 
 const char* gdn_status_string(gdn_status_t status) {
   switch (status) {

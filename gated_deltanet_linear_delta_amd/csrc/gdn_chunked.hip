@@ -548,7 +548,11 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   int32_t* chunk_off = static_cast<int32_t*>(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace) + offsets_bytes(d);
   const size_t max_chunks = chunked_max_chunks(d, C);
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C, cu, chunk_off);
+  {
+    Prof prof("chunk_offsets", st);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C, cu,
+                       chunk_off);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (max_chunks > 0) {
@@ -558,6 +562,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
       if (e != hipSuccess) return e;
     }
+    Prof prof("chunk_prep", st);
     hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(256), lds,
                        st, d.num_seqs, d.total_tokens, d.h_qk, d.h_v, static_cast<const IO*>(q),
                        static_cast<const IO*>(k), g, beta, cu, chunk_off, ws);
@@ -573,6 +578,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
+  Prof prof("chunk_sweep", st);
   hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(256), lds, st, d.num_seqs,
                      d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(q),
                      static_cast<const IO*>(k), static_cast<const IO*>(v), cu, chunk_off, ws, s_in,

@@ -93,6 +93,7 @@ static hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, c
   const int rows = d.num_seqs * d.h_v * d.d_v;
   if (rows == 0) return hipSuccess;
   dim3 grid((rows + 15) / 16), block(16 * (DK / 8));
+  Prof prof("decode", st);
   hipLaunchKernelGGL((decode_kernel<IO, DK>), grid, block, 0, st, rows, d.h_qk, d.h_v, d.d_v,
                      static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g, beta,
                      s_in, static_cast<IO*>(out), s_out);

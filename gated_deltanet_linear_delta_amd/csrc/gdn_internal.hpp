@@ -8,6 +8,22 @@
 
 namespace gdn {
 
+// Optional per-kernel timing: while profiling is enabled, a Prof object
+// records a hipEvent on `st` when constructed and another when destroyed, so
+// a launch placed between the two is timed on its own stream.
+class Prof {
+ public:
+  Prof(const char* name, hipStream_t st);
+  ~Prof();
+  Prof(const Prof&) = delete;
+  Prof& operator=(const Prof&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t start_ = nullptr;
+};
+
 struct Dims {
   int num_seqs, total_tokens, h_qk, h_v, d_k, d_v;
   bool bf16;  // io dtype: bf16 if true, fp32 otherwise

@@ -153,6 +153,7 @@ static hipError_t launch_scan_t(const Dims& d, const void* q, const void* k, con
                                 float* s_out, hipStream_t st) {
   const int blocks = d.num_seqs * d.h_v * (d.d_v / 16);
   if (blocks == 0) return hipSuccess;
+  Prof prof("scan", st);
   hipLaunchKernelGGL((scan_kernel<IO, DK>), dim3(blocks), dim3(16 * (DK / 8)), 0, st, d.total_tokens, d.h_qk,
                      d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
                      static_cast<const IO*>(v), g, beta, cu, s_in, static_cast<IO*>(out), s_out);

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace", "gdn_decode_step",
-           "gdn_status_string", "gdn_last_error")
+           "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -57,6 +57,11 @@ def load_library(path: str | None = None):
     lib.gdn_prefill_chunked_workspace.restype = ctypes.c_size_t
     lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f, f, vp, f, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_profile_enable.argtypes = [ctypes.c_int]
+    lib.gdn_profile_enable.restype = ctypes.c_int
+    lib.gdn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                        ctypes.c_int]
+    lib.gdn_profile_collect.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -204,3 +209,20 @@ def decode_step(q, k, v, g, beta, state_in, out=None, state_out=None, stream=Non
     _check(lib.gdn_decode_step(B, h_qk, h_v, d_k, d_v, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
     return out, state_out
+
+
+def profile_enable(enabled: bool = True):
+    """Bracket every kernel the library enqueues with HIP events on its stream."""
+    _check(load_library().gdn_profile_enable(1 if enabled else 0))
+
+
+def profile_collect(cap: int = 1 << 16):
+    """[(kernel name, elapsed ms)] for the kernels recorded since the last
+    collect, in launch order; the caller synchronises first."""
+    lib = load_library()
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib.gdn_profile_collect(names, ms, cap)
+    if n < 0:
+        raise GdnError(GDN_ERR_LAUNCH, "gdn_profile_collect: an event query failed")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]

@@ -132,6 +132,23 @@ gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d
                              const float* g, const float* beta,
                              const float* state_in, void* out, float* state_out, void* stream);
 
+/*
+ * Kernel timing for benchmarks and profiling.  While enabled (process-wide),
+ * every kernel the library enqueues is bracketed by two hipEvents recorded on
+ * the stream it is launched on.  Off by default; when off, no events are
+ * created or recorded.
+ */
+gdn_status_t gdn_profile_enable(int enabled);
+
+/*
+ * Elapsed times of the kernels recorded since the last collect, in launch
+ * order.  The caller must have synchronised the streams involved.  Copies up
+ * to `cap` records (names are static strings owned by the library), frees
+ * every recorded event and returns the number of records available (which may
+ * exceed cap; the excess is dropped).  Returns -1 if an event query fails.
+ */
+int gdn_profile_collect(const char** names, float* ms, int cap);
+
 /* Static, human-readable name of a status code ("GDN_OK", ...). */
 const char* gdn_status_string(gdn_status_t status);
 
