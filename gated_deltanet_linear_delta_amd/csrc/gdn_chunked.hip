@@ -12,31 +12,35 @@
 //   A_ri = beta_r exp(G_r - G_i) (k_r . k_i)  (i < r),   T = (I + A)^{-1}
 //   QKm_ri = exp(G_r - G_i) (q_r . k_i)       (i <= r)
 //   Y   = diag(beta) V - diag(beta gamma) (K S0^T)
-//   U   = T Y
-//   O   = diag(gamma) (Q S0^T) + QKm U
-//   S1^T = gamma_{n-1} S0^T + K^T diag(dec) U
+//   O   = diag(gamma) (Q S0^T) + R Y,          R  = QKm T
+//   S1^T = gamma_{n-1} S0^T + K^T (T' Y),      T' = diag(dec) T
 //
-// Decays are always formed as exp of a non-positive difference of fp64
-// partial sums, so nothing overflows and nothing but true decay underflows.
+// (U = T Y is the block's matrix of delta updates; folding T into R and T'
+// leaves two block products between one state and the next.)  Decays are
+// always formed as exp of a non-positive difference of fp64 partial sums, so
+// nothing overflows and nothing but true decay underflows.
 //
 // Three launches:
-//   1. chunk_offsets_kernel: chunk_off[n] = chunks before sequence n.
+//   1. chunk_offsets_kernel: chunk_off[n] = chunks before sequence n, and a
+//      per-chunk table (first token, length).
 //   2. chunk_prep_kernel, one workgroup per (chunk, value head), fully
-//      parallel: stages the block's K and Q in LDS, forms the Gram products
-//      on MFMA, the gate prefix sums, A, and T = (I + A)^{-1} (16x16 diagonal
-//      blocks by forward substitution in registers, off-diagonal blocks by
-//      fp32 MFMA block products), and writes T, QKm and the per-token scalars
-//      to the workspace as ready-to-use MFMA A fragments.
+//      parallel: Gram products on MFMA, gate prefix sums, A, T = (I + A)^{-1}
+//      (16x16 diagonal blocks by forward substitution in registers,
+//      off-diagonal blocks by fp32 MFMA block products), R = QKm T, and the
+//      per-token scalars, written to the workspace as MFMA A fragments.
 //   3. chunk_sweep_kernel, one workgroup per (sequence, value head, 16 rows of
 //      the state): walks the chunks in order with its 16 x d_k slice of the
-//      fp32 state held in MFMA accumulators.  State rows are independent
-//      given the block's T, so the 16-row slices of one head never talk to
-//      each other.
+//      fp32 state in MFMA accumulators.  State rows are independent given the
+//      block's T, so slices of one head never talk to each other.  Chunk c+1's
+//      inputs are fetched into registers while chunk c is computed, and the
+//      barriers wait only for LDS traffic.
 //
-// Precision.  bf16 inputs (K, Q, V) enter MFMA exactly.  Every derived fp32
-// operand (S, Y, U, dec*U, T, QKm) is split into hi + lo bf16 halves, so the
-// block products keep about 16 mantissa bits per operand and fp32
-// accumulation.  fp32 inputs use fp32 MFMA throughout.
+// All block products use 16x16x32 fragments (see gdn_common.hpp).  Precision:
+// bf16 inputs (K, Q, V) enter MFMA exactly.  Y and T'Y are split into hi + lo
+// bf16 halves, as is R; the state (in K S^T, Q S^T) and T' enter rounded
+// once to bf16: their error reaches the outputs damped by the block decay
+// and stays well below the output's own bf16 rounding.  Every product
+// accumulates in fp32.  fp32 inputs use fp32 MFMA throughout.
 #include <type_traits>
 
 #include "gdn_common.hpp"
@@ -46,137 +50,177 @@ namespace gdn {
 
 namespace {
 
-template <int C>
+struct sp8 {  // hi + lo bf16 halves of eight fp32 values
+  uint4 hi, lo;
+};
+
+// Products on one 32-wide slab.  Split operands feed two accumulators (the
+// hi part and the small corrections) so that consecutive products do not
+// wait on each other.
+__device__ __forceinline__ void mm_es(uint4 a, const sp8& b, f4& ch, f4& cl) {
+  ch = mma32(a, b.hi, ch);
+  cl = mma32(a, b.lo, cl);
+}
+__device__ __forceinline__ void mm_es(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
+__device__ __forceinline__ void mm_ss(const sp8& a, const sp8& b, f4& ch, f4& cl) {
+  ch = mma32(a.hi, b.hi, ch);
+  cl = mma32(a.hi, b.lo, cl);
+  cl = mma32(a.lo, b.hi, cl);
+}
+__device__ __forceinline__ void mm_ss(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
+
+template <bool BF>
+struct Types {
+  using E = uint4;  // exact or once-rounded operand: 8 bf16
+  using S = sp8;    // split operand
+  using IO = uint16_t;
+};
+template <>
+struct Types<false> {
+  using E = f8;
+  using S = f8;
+  using IO = float;
+};
+
+__device__ __forceinline__ void zero(uint4& x) { x = uint4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ void zero(f8& x) { x.a = zero4(), x.b = zero4(); }
+__device__ __forceinline__ void zero(sp8& x) { zero(x.hi), zero(x.lo); }
+__device__ __forceinline__ void zero(float& x) { x = 0.f; }
+__device__ __forceinline__ void zero(uint16_t& x) { x = 0; }
+
+// 8 consecutive elements of an LDS/global row as an operand.
+__device__ __forceinline__ void ld8(uint4& d, const uint16_t* p) { d = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void ld8(f8& d, const float* p) {
+  d.a = *reinterpret_cast<const f4*>(p);
+  d.b = *reinterpret_cast<const f4*>(p + 4);
+}
+// 8 elements of a column (stride apart) as an operand.
+__device__ __forceinline__ void ld8col(uint4& d, const uint16_t* p, int stride) {
+  d = uint4{pack2(p[0], p[stride]), pack2(p[2 * stride], p[3 * stride]), pack2(p[4 * stride], p[5 * stride]),
+            pack2(p[6 * stride], p[7 * stride])};
+}
+__device__ __forceinline__ void ld8col(f8& d, const float* p, int stride) {
+  d.a = f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+  d.b = f4{p[4 * stride], p[5 * stride], p[6 * stride], p[7 * stride]};
+}
+
+// Exchange buffers: [16 rows][K + pad] arrays with K contiguous, written from
+// D blocks (4 consecutive k per lane) and read as B fragments (8 consecutive
+// k per lane).  bf16 buffers hold either the rounded value (single) or the
+// hi and lo halves in two planes; fp32 buffers hold the value.
+template <bool BF, int K>
+struct XBuf {
+  static constexpr int PAD = BF ? 8 : 4;  // 16 bytes
+  static constexpr int LD = K + PAD;      // row stride, elements
+  using El = std::conditional_t<BF, uint16_t, float>;
+  static constexpr size_t PLANE = 16 * LD * sizeof(El);
+};
+
+template <bool BF, int K>
+__device__ __forceinline__ void xb_write_single(uint8_t* buf, int n, int k0, f4 v) {
+  using X = XBuf<BF, K>;
+  if constexpr (BF) *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(buf) + n * X::LD + k0) = bf16x4(v);
+  else *reinterpret_cast<f4*>(reinterpret_cast<float*>(buf) + n * X::LD + k0) = v;
+}
+template <bool BF, int K>
+__device__ __forceinline__ void xb_write_split(uint8_t* buf, int n, int k0, f4 v) {
+  using X = XBuf<BF, K>;
+  if constexpr (BF) {
+    uint2 h, l;
+    split_bf16x4(v, h, l);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(buf) + n * X::LD + k0) = h;
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(buf + X::PLANE) + n * X::LD + k0) = l;
+  } else {
+    *reinterpret_cast<f4*>(reinterpret_cast<float*>(buf) + n * X::LD + k0) = v;
+  }
+}
+template <bool BF, int K>
+__device__ __forceinline__ void xb_read_single(typename Types<BF>::E& d, const uint8_t* buf, int n, int k0) {
+  using X = XBuf<BF, K>;
+  ld8(d, reinterpret_cast<const typename X::El*>(buf) + n * X::LD + k0);
+}
+template <bool BF, int K>
+__device__ __forceinline__ void xb_read_split(typename Types<BF>::S& d, const uint8_t* buf, int n, int k0) {
+  using X = XBuf<BF, K>;
+  if constexpr (BF) {
+    ld8(d.hi, reinterpret_cast<const uint16_t*>(buf) + n * X::LD + k0);
+    ld8(d.lo, reinterpret_cast<const uint16_t*>(buf + X::PLANE) + n * X::LD + k0);
+  } else {
+    ld8(d, reinterpret_cast<const float*>(buf) + n * X::LD + k0);
+  }
+}
+template <bool BF, int K>
+constexpr size_t xb_bytes_split() {
+  return (BF ? 2 : 1) * XBuf<BF, K>::PLANE;
+}
+
+// Workspace block of one (chunk, value head).  A fragments of 16 rows x 32
+// columns of the lower-triangular C x C matrices T' and R: fragment (r, s),
+// r = row block, s = 32-wide column slab, exists for s <= r / 2.  A fragment
+// is one (single) or two (split / fp32) planes of 64 lanes x 16 bytes.
+template <bool BF, int C>
 struct Geom {
-  static constexpr int NB = C / 16;                 // 16-token blocks per chunk
-  static constexpr int NBLK = NB * (NB + 1) / 2;    // lower-triangular 16x16 blocks
-  static constexpr size_t FRAG = 64 * 16;           // one 16x16 fragment: 64 lanes x 16 bytes
+  static constexpr int NB = C / 16;  // 16-token row blocks
+  static constexpr int NF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
+  static constexpr int TPL = BF ? 1 : 2;  // planes of a T' fragment
+  static constexpr size_t PLANE = 1024;
   static constexpr size_t T_OFF = 0;
-  static constexpr size_t QK_OFF = NBLK * FRAG;
-  static constexpr size_t SCAL_OFF = 2 * NBLK * FRAG;
-  static constexpr size_t BYTES = SCAL_OFF + 4 * C * sizeof(float);  // per (chunk, value head)
+  static constexpr size_t R_OFF = T_OFF + size_t(NF) * TPL * PLANE;
+  static constexpr size_t SCAL_OFF = R_OFF + size_t(NF) * 2 * PLANE;
+  static constexpr size_t BYTES = SCAL_OFF + 4 * C * sizeof(float);
   static_assert(BYTES % 256 == 0, "keep per-chunk blocks 256-byte aligned");
 };
+// first fragment of row block r: sum over r' < r of (r' / 2 + 1)
+__device__ __forceinline__ constexpr int frag_base(int r) { return r == 0 ? 0 : (r == 1 ? 1 : (r == 2 ? 2 : 4)); }
 
-__device__ __forceinline__ int blk_index(int r, int i) { return r * (r + 1) / 2 + i; }
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS (and scalar)
+// traffic only, so global loads and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void blk_decode(int p, int& r, int& i) {
-  r = 0;
-  while ((r + 1) * (r + 2) / 2 <= p) ++r;
-  i = p - r * (r + 1) / 2;
-}
-
-// 16-byte fragment in its workspace / LDS form: split bf16 (hi, lo) or fp32.
-template <bool BF>
-__device__ __forceinline__ uint4 pack_frag(f4 x) {
-  if constexpr (BF) {
-    sfrag s = split4(x);
-    uint4 r;
-    r.x = uint32_t(uint16_t(s.hi[0])) | (uint32_t(uint16_t(s.hi[1])) << 16);
-    r.y = uint32_t(uint16_t(s.hi[2])) | (uint32_t(uint16_t(s.hi[3])) << 16);
-    r.z = uint32_t(uint16_t(s.lo[0])) | (uint32_t(uint16_t(s.lo[1])) << 16);
-    r.w = uint32_t(uint16_t(s.lo[2])) | (uint32_t(uint16_t(s.lo[3])) << 16);
-    return r;
-  } else {
-    uint4 r;
-    r.x = __float_as_uint(x[0]);
-    r.y = __float_as_uint(x[1]);
-    r.z = __float_as_uint(x[2]);
-    r.w = __float_as_uint(x[3]);
-    return r;
-  }
-}
-
-__device__ __forceinline__ sfrag as_sfrag(uint4 u) {
-  sfrag s;
-  s.hi = pack4(uint16_t(u.x), uint16_t(u.x >> 16), uint16_t(u.y), uint16_t(u.y >> 16));
-  s.lo = pack4(uint16_t(u.z), uint16_t(u.z >> 16), uint16_t(u.w), uint16_t(u.w >> 16));
-  return s;
-}
-__device__ __forceinline__ f4 as_f4(uint4 u) {
-  return f4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
-}
-
-// derived (split) x derived (split)
-template <bool BF>
-__device__ __forceinline__ f4 mma_dd(uint4 a, uint4 b, f4 c) {
-  if constexpr (BF) return mma_s_s(as_sfrag(a), as_sfrag(b), c);
-  else return mma_f32(as_f4(a), as_f4(b), c);
-}
-
-// Four consecutive io elements from LDS as an exact operand fragment.
-template <typename IO>
-struct ExactFrag;
-template <>
-struct ExactFrag<uint16_t> {
-  s4 v;
-  __device__ __forceinline__ void load_row(const uint16_t* p) { v = *reinterpret_cast<const s4*>(p); }
-  __device__ __forceinline__ void load_col(const uint16_t* p, int stride) {
-    v = pack4(p[0], p[stride], p[2 * stride], p[3 * stride]);
-  }
-  // exact x derived
-  __device__ __forceinline__ f4 mma(uint4 b, f4 c) const { return mma_e_s(v, as_sfrag(b), c); }
-  __device__ __forceinline__ f4 mma_exact(const ExactFrag& b, f4 c) const { return mma_bf(v, b.v, c); }
-};
-template <>
-struct ExactFrag<float> {
-  f4 v;
-  __device__ __forceinline__ void load_row(const float* p) { v = *reinterpret_cast<const f4*>(p); }
-  __device__ __forceinline__ void load_col(const float* p, int stride) {
-    v = f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
-  }
-  __device__ __forceinline__ f4 mma(uint4 b, f4 c) const { return mma_f32(v, as_f4(b), c); }
-  __device__ __forceinline__ f4 mma_exact(const ExactFrag& b, f4 c) const { return mma_f32(v, b.v, c); }
-};
-
-// Stage rows [t0, t0 + nc) of head j of a [T, h, DK] tensor into LDS rows of
-// KP elements; rows nc..C-1 are zero-filled.
-template <typename IO, int DK, int C, int KP, int NT>
-__device__ __forceinline__ void stage_rows(IO* dst, const IO* __restrict__ src, int t0, int nc, int heads, int j,
-                                           int tid) {
-  constexpr int E16 = 16 / sizeof(IO);
-  constexpr int PER_ROW = DK / E16;
-  for (int x = tid; x < C * PER_ROW; x += NT) {
-    const int r = x / PER_ROW, cc = (x % PER_ROW) * E16;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (r < nc) val = *reinterpret_cast<const uint4*>(src + (size_t(t0 + r) * heads + j) * DK + cc);
-    *reinterpret_cast<uint4*>(dst + r * KP + cc) = val;
-  }
-}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <typename IO, int DK, int C>
 struct PrepLds {
   static constexpr int E16 = 16 / sizeof(IO);
-  static constexpr int KP = DK + E16;  // padded row, elements
-  static constexpr int AP = C + 4;     // padded fp32 row of A and T
-  static constexpr size_t KQ_BYTES = 2 * size_t(C) * KP * sizeof(IO);
-  static constexpr size_t T_BYTES = size_t(C) * AP * sizeof(float);
-  static constexpr size_t R0 = KQ_BYTES > T_BYTES ? KQ_BYTES : T_BYTES;  // K, Q; later T
-  static constexpr size_t A_OFF = R0;
-  static constexpr size_t G_OFF = A_OFF + T_BYTES;  // fp64 prefix sums
+  static constexpr int CP = C < 32 ? 32 : C;     // token rows, padded to a 32 slab
+  static constexpr int DKP = DK < 32 ? 32 : DK;  // key columns, padded to a 32 slab
+  static constexpr int KP = DKP + E16;           // row stride, elements
+  static constexpr int AP = C + 4;               // fp32 row stride of A, QKm, T, R
+  static constexpr size_t KQ_BYTES = 2 * size_t(CP) * KP * sizeof(IO);
+  static constexpr size_t M_BYTES = size_t(C) * AP * sizeof(float);
+  static constexpr size_t R0 = KQ_BYTES > M_BYTES ? KQ_BYTES : M_BYTES;  // K, Q; later T
+  static constexpr size_t A_OFF = R0;                                    // A; later R
+  static constexpr size_t QK_OFF = A_OFF + M_BYTES;
+  static constexpr size_t G_OFF = QK_OFF + M_BYTES;  // fp64 prefix sums
   static constexpr size_t B_OFF = G_OFF + C * sizeof(double);
-  static constexpr size_t BYTES = B_OFF + C * sizeof(float);
+  static constexpr size_t D_OFF = B_OFF + C * sizeof(float);
+  static constexpr size_t BYTES = D_OFF + C * sizeof(float);
 };
 
 template <typename IO, int DK, int C>
 struct SweepLds {
-  static constexpr int NB = C / 16, KB = DK / 16;
+  static constexpr bool BF = sizeof(IO) == 2;
   static constexpr int E16 = 16 / sizeof(IO);
-  static constexpr int KP = DK + E16;
-  static constexpr size_t Q_OFF = size_t(C) * KP * sizeof(IO);
-  static constexpr size_t S_OFF = 2 * Q_OFF;
-  static constexpr size_t Y_OFF = S_OFF + KB * 1024;
-  static constexpr size_t U_OFF = Y_OFF + NB * 1024;
-  static constexpr size_t UD_OFF = U_OFF + NB * 1024;
-  static constexpr size_t SC_OFF = UD_OFF + NB * 1024;
-  static constexpr size_t BYTES = SC_OFF + 4 * C * sizeof(float);
+  static constexpr int CP = C < 32 ? 32 : C;
+  static constexpr int DKP = DK < 32 ? 32 : DK;
+  static constexpr int KP = DKP + E16;
+  static constexpr size_t KBUF = size_t(CP) * KP * sizeof(IO);  // one K chunk
+  static constexpr size_t S_OFF = 2 * KBUF;                      // K is double-buffered
+  static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
+  static constexpr size_t UD_OFF = Y_OFF + xb_bytes_split<BF, CP>();
+  static constexpr size_t SC_OFF = UD_OFF + xb_bytes_split<BF, CP>();  // two buffers of 4 C floats
+  static constexpr size_t BYTES = SC_OFF + 2 * 4 * C * sizeof(float);
 };
 
 }  // namespace
 
-// chunk_off[n] = number of C-token chunks in sequences 0..n-1; chunk_off[N] = total.
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(int N, int T, int C, const int32_t* __restrict__ cu,
-                                                            int32_t* __restrict__ chunk_off) {
+// chunk_off[n] = number of C-token chunks in sequences 0..n-1, chunk_off[N] =
+// total; tab[gc] = (first token, length) of chunk gc for gc < total and
+// (0, 0) for total <= gc < max_chunks.
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(int N, int T, int C, int max_chunks,
+                                                            const int32_t* __restrict__ cu,
+                                                            int32_t* __restrict__ chunk_off,
+                                                            int2* __restrict__ tab) {
   __shared__ int part[256];
   const int tid = threadIdx.x;
   const int per = (N + 255) / 256;
@@ -200,51 +244,59 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(int N, int T, int C,
     chunk_off[n] = run;
     int b, e;
     seq_range(cu, n, T, b, e);
-    run += (e - b + C - 1) / C;
+    for (int t = b; t < e; t += C, ++run)
+      if (run < max_chunks) tab[run] = make_int2(t, min(C, e - t));
   }
-  if (tid == 255) chunk_off[N] = part[255];
+  const int total = part[255];
+  if (tid == 255) chunk_off[N] = total;
+  for (int gc = total + tid; gc < max_chunks; gc += 256) tab[gc] = make_int2(0, 0);
 }
 
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(int N, int T, int h_qk, int h_v,
-                                                         const IO* __restrict__ q, const IO* __restrict__ k,
-                                                         const float* __restrict__ g,
+__global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
+                                                         const IO* __restrict__ k, const float* __restrict__ g,
                                                          const float* __restrict__ beta,
-                                                         const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ chunk_off,
-                                                         uint8_t* __restrict__ ws) {
-  using Geo = Geom<C>;
-  using Lds = PrepLds<IO, DK, C>;
-  constexpr int NB = Geo::NB, NBLK = Geo::NBLK, KB = DK / 16;
+                                                         const int2* __restrict__ tab, uint8_t* __restrict__ ws) {
   constexpr bool BF = sizeof(IO) == 2;
-  constexpr int KP = Lds::KP, AP = Lds::AP;
+  using Geo = Geom<BF, C>;
+  using Lds = PrepLds<IO, DK, C>;
+  using E = typename Types<BF>::E;
+  constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, AP = Lds::AP;
+  constexpr int NKS = Lds::DKP / 32;
+  constexpr int NBLK = NB * (NB + 1) / 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
-  IO* sQ = sK + C * KP;
+  IO* sQ = sK + Lds::CP * KP;
   float* sT = reinterpret_cast<float*>(smem);  // reuses the K/Q region after the Gram products
   float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);
+  float* sR = sA;                              // reuses A after the inverse
+  float* sQK = reinterpret_cast<float*>(smem + Lds::QK_OFF);
   double* sG = reinterpret_cast<double*>(smem + Lds::G_OFF);
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
+  float* sDec = reinterpret_cast<float*>(smem + Lds::D_OFF);
 
   const int gc = blockIdx.x, h = blockIdx.y;
-  if (gc >= chunk_off[N]) return;
-  int lo = 0, hi = N - 1;  // last sequence whose first chunk is <= gc
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_off[mid] <= gc) lo = mid;
-    else hi = mid - 1;
-  }
-  int bos, eos;
-  seq_range(cu, lo, T, bos, eos);
-  const int t0 = bos + (gc - chunk_off[lo]) * C;
-  const int nc = min(C, eos - t0);
+  const int2 ch = tab[gc];
+  const int t0 = ch.x, nc = ch.y;
   if (nc <= 0) return;
   const int j = h / (h_v / h_qk);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = wave_id();
   uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
 
-  stage_rows<IO, DK, C, KP, 256>(sK, k, t0, nc, h_qk, j, tid);
-  stage_rows<IO, DK, C, KP, 256>(sQ, q, t0, nc, h_qk, j, tid);
+  // K and Q rows of the chunk (rows >= nc and columns >= DK are zero)
+  constexpr int PER_ROW = Lds::DKP / E16;
+  for (int x = tid; x < Lds::CP * PER_ROW; x += 256) {
+    const int r = x / PER_ROW, c16 = (x % PER_ROW) * E16;
+    uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (r < nc && c16 < DK) {
+      const size_t off = (size_t(t0 + r) * h_qk + j) * DK + c16;
+      kv = *reinterpret_cast<const uint4*>(k + off);
+      qv = *reinterpret_cast<const uint4*>(q + off);
+    }
+    *reinterpret_cast<uint4*>(sK + r * KP + c16) = kv;
+    *reinterpret_cast<uint4*>(sQ + r * KP + c16) = qv;
+  }
   if (wave == 0) {
     double gl = 0.0;
     float bl = 0.f;
@@ -259,10 +311,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int N, int T, int h_qk,
     }
     const double glast = __shfl(gl, nc - 1);
     if (lane < C) {
-      sG[lane] = gl;
-      sBeta[lane] = bl;
       const float gam = lane < nc ? float(exp(gl)) : 0.f;
       const float dec = lane < nc ? float(exp(glast - gl)) : 0.f;
+      sG[lane] = gl;
+      sBeta[lane] = bl;
+      sDec[lane] = dec;
       float* sc = reinterpret_cast<float*>(wsb + Geo::SCAL_OFF);
       sc[lane] = bl;
       sc[C + lane] = bl * gam;
@@ -270,45 +323,39 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int N, int T, int h_qk,
       sc[3 * C + lane] = dec;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Gram blocks.  p < NBLK: K K^T block (r, i) -> A (strictly lower, scaled) in LDS.
-  // p >= NBLK: K Q^T block (i, r), whose D layout is the A fragment of QK^T
-  // block (r, i) -> masked, decayed, written to the workspace.
+  // Gram blocks (r, i), i <= r:  p < NBLK: K K^T -> A (strictly lower, scaled);
+  // otherwise Q K^T -> QKm (lower, decayed).  Both kept in LDS as fp32 rows.
   for (int p = wave; p < 2 * NBLK; p += 4) {
     const bool isA = p < NBLK;
-    int r, i;
-    blk_decode(isA ? p : p - NBLK, r, i);
-    const int ra = isA ? r : i;
-    const IO* bsrc = isA ? sK + (16 * i + col) * KP : sQ + (16 * r + col) * KP;
-    const IO* asrc = sK + (16 * ra + col) * KP;
-    f4 acc = zero4();
+    const int pb = isA ? p : p - NBLK;
+    int r = 0;
+    while ((r + 1) * (r + 2) / 2 <= pb) ++r;
+    const int i = pb - r * (r + 1) / 2;
+    const IO* asrc = (isA ? sK : sQ) + (16 * r + col) * KP + 8 * grp;
+    const IO* bsrc = sK + (16 * i + col) * KP + 8 * grp;
+    f4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-    for (int s = 0; s < KB; ++s) {
-      ExactFrag<IO> a, b;
-      a.load_row(asrc + 16 * s + 4 * grp);
-      b.load_row(bsrc + 16 * s + 4 * grp);
-      acc = a.mma_exact(b, acc);
+    for (int s = 0; s < NKS; ++s) {
+      E a, b;
+      ld8(a, asrc + 32 * s);
+      ld8(b, bsrc + 32 * s);
+      if (s & 1) acc1 = mma32(a, b, acc1);
+      else acc0 = mma32(a, b, acc0);
     }
-    if (isA) {
+    const f4 acc = acc0 + acc1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
-        float val = 0.f;
-        if (cl < row) val = sBeta[row] * expf(float(sG[row] - sG[cl])) * acc[e];
-        sA[row * AP + cl] = val;
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
+      if (isA) {
+        sA[row * AP + cl] = cl < row ? sBeta[row] * expf(float(sG[row] - sG[cl])) * acc[e] : 0.f;
+      } else {
+        sQK[row * AP + cl] = cl <= row ? expf(float(sG[row] - sG[cl])) * acc[e] : 0.f;
       }
-    } else {
-      f4 m;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * r + col, cl = 16 * i + 4 * grp + e;
-        m[e] = cl <= row ? expf(float(sG[row] - sG[cl])) * acc[e] : 0.f;
-      }
-      *reinterpret_cast<uint4*>(wsb + Geo::QK_OFF + blk_index(r, i) * Geo::FRAG + lane * 16) = pack_frag<BF>(m);
     }
   }
-  __syncthreads();  // A complete; K and Q are dead, their space becomes T
+  lds_barrier();  // A and QKm complete; K and Q are dead, their space becomes T
 
   // Diagonal blocks: T_bb = (I + A_bb)^{-1}.  Lane 4c+s owns column c and the
   // rows congruent to s mod 4; each row is one quad reduction.
@@ -329,7 +376,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int N, int T, int h_qk,
 #pragma unroll
     for (int m = 0; m < 4; ++m) sT[(16 * b + 4 * m + s) * AP + 16 * b + c] = t[m];
   }
-  __syncthreads();
+  lds_barrier();
 
   // Off-diagonal blocks, one block row at a time:
   //   T(i, jj) = -T(i, i) * sum_{kk = jj}^{i-1} A(i, kk) T(kk, jj)
@@ -345,18 +392,70 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int N, int T, int h_qk,
         P = mma_f32(a, bt, P);
       }
       const f4 tii = *reinterpret_cast<const f4*>(&sT[(16 * i + col) * AP + 16 * i + 4 * grp]);
-      const f4 R = mma_f32(tii, P, zero4());
+      const f4 Rr = mma_f32(tii, P, zero4());
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * jj + col] = -R[e];
+      for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * jj + col] = -Rr[e];
     }
-    __syncthreads();
+    lds_barrier();
   }
 
+  // R = QKm T, lower-triangular blocks R(r, i) = sum_{k=i}^{r} QKm(r, k) T(k, i), in fp32.
   for (int p = wave; p < NBLK; p += 4) {
-    int r, i;
-    blk_decode(p, r, i);
-    const f4 x = *reinterpret_cast<const f4*>(&sT[(16 * r + col) * AP + 16 * i + 4 * grp]);
-    *reinterpret_cast<uint4*>(wsb + Geo::T_OFF + blk_index(r, i) * Geo::FRAG + lane * 16) = pack_frag<BF>(x);
+    int r = 0;
+    while ((r + 1) * (r + 2) / 2 <= p) ++r;
+    const int i = p - r * (r + 1) / 2;
+    f4 acc = zero4();
+    for (int kk = i; kk <= r; ++kk) {
+      const f4 a = *reinterpret_cast<const f4*>(&sQK[(16 * r + col) * AP + 16 * kk + 4 * grp]);
+      f4 bt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bt[e] = sT[(16 * kk + 4 * grp + e) * AP + 16 * i + col];
+      acc = mma_f32(a, bt, acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sR[(16 * r + 4 * grp + e) * AP + 16 * i + col] = acc[e];
+  }
+  lds_barrier();
+
+  // Fragments (r, s), s <= r / 2, of T' = diag(dec) T and R, lower-triangular
+  // (entries above the diagonal and beyond C are zero).
+  for (int p = wave; p < Geo::NF; p += 4) {
+    int r = 0;
+    while (r + 1 < NB && frag_base(r + 1) <= p) ++r;
+    const int s = p - frag_base(r);
+    const int row = 16 * r + col, k0 = 32 * s + 8 * grp;
+    f8 tv, rv;
+    zero(tv), zero(rv);
+    if (k0 < C) {
+      tv.a = *reinterpret_cast<const f4*>(&sT[row * AP + k0]);
+      tv.b = *reinterpret_cast<const f4*>(&sT[row * AP + k0 + 4]);
+      rv.a = *reinterpret_cast<const f4*>(&sR[row * AP + k0]);
+      rv.b = *reinterpret_cast<const f4*>(&sR[row * AP + k0 + 4]);
+    }
+    const float dr = sDec[row];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ka = k0 + e <= row, kb = k0 + 4 + e <= row;
+      tv.a[e] = ka ? dr * tv.a[e] : 0.f;
+      tv.b[e] = kb ? dr * tv.b[e] : 0.f;
+      rv.a[e] = ka ? rv.a[e] : 0.f;
+      rv.b[e] = kb ? rv.b[e] : 0.f;
+    }
+    uint8_t* tp = wsb + Geo::T_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
+    uint8_t* rp = wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16;
+    if constexpr (BF) {
+      uint4 th, tl, rh, rl;
+      split_bf16x8(tv, th, tl);
+      split_bf16x8(rv, rh, rl);
+      *reinterpret_cast<uint4*>(tp) = th;
+      *reinterpret_cast<uint4*>(rp) = rh;
+      *reinterpret_cast<uint4*>(rp + Geo::PLANE) = rl;
+    } else {
+      *reinterpret_cast<f4*>(tp) = tv.a;
+      *reinterpret_cast<f4*>(tp + Geo::PLANE) = tv.b;
+      *reinterpret_cast<f4*>(rp) = rv.a;
+      *reinterpret_cast<f4*>(rp + Geo::PLANE) = rv.b;
+    }
   }
 }
 
@@ -367,19 +466,21 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
                                                           const int32_t* __restrict__ chunk_off,
                                                           const uint8_t* __restrict__ ws, const float* s_in,
                                                           IO* __restrict__ out, float* s_out) {
-  using Geo = Geom<C>;
-  using Lds = SweepLds<IO, DK, C>;
-  constexpr int NB = Geo::NB, KB = DK / 16, KP = Lds::KP;
-  constexpr int SB = (KB + 3) / 4;  // state blocks per wave
   constexpr bool BF = sizeof(IO) == 2;
+  using Geo = Geom<BF, C>;
+  using Lds = SweepLds<IO, DK, C>;
+  using E = typename Types<BF>::E;
+  using Sp = typename Types<BF>::S;
+  constexpr int NB = Geo::NB, KB = DK / 16, KP = Lds::KP, CP = Lds::CP, DKP = Lds::DKP;
+  constexpr int NKS = DKP / 32, NTS = CP / 32;  // 32-wide slabs along d_k and along the chunk
+  constexpr int SB = (KB + 3) / 4;              // state blocks per wave
+  constexpr int NTF = (NB + 1) / 2;             // T' / R fragments per row block, at most
+  constexpr int E16 = Lds::E16, PER_ROW = DK / E16;
+  constexpr int NIT = (C * PER_ROW + 255) / 256;  // 16-byte K pieces per thread per chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  IO* sK = reinterpret_cast<IO*>(smem);
-  IO* sQ = reinterpret_cast<IO*>(smem + Lds::Q_OFF);
-  uint4* sS = reinterpret_cast<uint4*>(smem + Lds::S_OFF);
-  uint4* sY = reinterpret_cast<uint4*>(smem + Lds::Y_OFF);
-  uint4* sU = reinterpret_cast<uint4*>(smem + Lds::U_OFF);
-  uint4* sUd = reinterpret_cast<uint4*>(smem + Lds::UD_OFF);
-  float* sSc = reinterpret_cast<float*>(smem + Lds::SC_OFF);
+  uint8_t* sS = smem + Lds::S_OFF;
+  uint8_t* sY = smem + Lds::Y_OFF;
+  uint8_t* sUd = smem + Lds::UD_OFF;
 
   // Workgroups are dealt to the 8 XCDs round-robin; give the 16-row slices of
   // one head consecutive chain numbers on one XCD so they share its L2.
@@ -391,123 +492,218 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   const int tl = L % ntile, nh = L / ntile, h = nh % h_v, n = nh / h_v;
   const int j = h / (h_v / h_qk);
   const int dv0 = 16 * tl;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = wave_id();
+
+  // zero the LDS padding that K = 32 slabs read past C tokens or d_k columns
+  for (int x = tid; x < int(Lds::Y_OFF / 16); x += 256) reinterpret_cast<uint4*>(smem)[x] = uint4{0u, 0u, 0u, 0u};
+  for (int x = tid; x < int((Lds::SC_OFF - Lds::Y_OFF) / 16); x += 256)
+    reinterpret_cast<uint4*>(sY)[x] = uint4{0u, 0u, 0u, 0u};
+  lds_barrier();
 
   f4 st[SB];
 #pragma unroll
   for (int bi = 0; bi < SB; ++bi) {
     const int b = wave + 4 * bi;
+    st[bi] = zero4();
     if (b < KB) {
-      st[bi] = s_in ? *reinterpret_cast<const f4*>(s_in + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp)
-                    : zero4();
-      sS[b * 64 + lane] = pack_frag<BF>(st[bi]);
+      if (s_in) st[bi] = *reinterpret_cast<const f4*>(s_in + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp);
+      xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
     }
   }
   int bos, eos;
   seq_range(cu, n, T, bos, eos);
-  const int nchunk = (eos - bos + C - 1) / C;
+  int nchunk = (eos - bos + C - 1) / C;
   const int gc0 = chunk_off[n];
+  nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
 
-  for (int cc = 0; cc < nchunk; ++cc) {
-    const int gc = gc0 + cc;
-    if (gc >= max_chunks) break;
-    const int t0 = bos + cc * C;
-    const int nc = min(C, eos - t0);
-    const uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
-
-    // (a) stage the chunk; fetch this wave's T and QKm fragments and V values
-    stage_rows<IO, DK, C, KP, 256>(sK, k, t0, nc, h_qk, j, tid);
-    stage_rows<IO, DK, C, KP, 256>(sQ, q, t0, nc, h_qk, j, tid);
-    for (int x = tid; x < 4 * C; x += 256) sSc[x] = reinterpret_cast<const float*>(wsb + Geo::SCAL_OFF)[x];
-    uint4 tf[NB], qf[NB];
-    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+  // Everything chunk cc needs from global memory, fetched one chunk ahead.
+  // Loads are unconditional (indices clamped into the chunk) so that no
+  // result is consumed before the chunk that uses it.
+  struct Pre {
+    uint4 kp[NIT];       // K rows, 16-byte pieces, for LDS
+    float sc;            // one of the 4 C per-token scalars, for LDS
+    E tf[NTF];           // T' fragments of row block `wave`
+    Sp rf[NTF];          // R fragments of row block `wave`
+    E aq[NKS];           // Q rows of block `wave` as A fragments
+    IO vr[4];            // V values of block `wave` (raw io values)
+  };
+  auto fetch = [&](Pre& P, int cc) {
+    const int t0 = bos + cc * C, nc = min(C, eos - t0);
+    const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int x = tid + 256 * it;
+      const int r = min(x / PER_ROW, nc - 1), c16 = (x % PER_ROW) * E16;
+      if (x < C * PER_ROW) P.kp[it] = *reinterpret_cast<const uint4*>(k + (size_t(t0 + r) * h_qk + j) * DK + c16);
+    }
+    P.sc = reinterpret_cast<const float*>(wsb + Geo::SCAL_OFF)[tid % (4 * C)];
     if (wave < NB) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (i <= wave) {
-          tf[i] = *reinterpret_cast<const uint4*>(wsb + Geo::T_OFF + blk_index(wave, i) * Geo::FRAG + lane * 16);
-          qf[i] = *reinterpret_cast<const uint4*>(wsb + Geo::QK_OFF + blk_index(wave, i) * Geo::FRAG + lane * 16);
+      for (int s = 0; s < NTF; ++s) {
+        if (2 * s <= wave) {
+          const uint8_t* tp = wsb + Geo::T_OFF + size_t(frag_base(wave) + s) * Geo::TPL * Geo::PLANE + lane * 16;
+          const uint8_t* rp = wsb + Geo::R_OFF + size_t(frag_base(wave) + s) * 2 * Geo::PLANE + lane * 16;
+          if constexpr (BF) {
+            P.tf[s] = *reinterpret_cast<const uint4*>(tp);
+            P.rf[s].hi = *reinterpret_cast<const uint4*>(rp);
+            P.rf[s].lo = *reinterpret_cast<const uint4*>(rp + Geo::PLANE);
+          } else {
+            P.tf[s].a = *reinterpret_cast<const f4*>(tp);
+            P.tf[s].b = *reinterpret_cast<const f4*>(tp + Geo::PLANE);
+            P.rf[s].a = *reinterpret_cast<const f4*>(rp);
+            P.rf[s].b = *reinterpret_cast<const f4*>(rp + Geo::PLANE);
+          }
         }
+      }
+      const int qrow = min(16 * wave + col, nc - 1);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        zero(P.aq[s]);
+        if (32 * s + 8 * grp < DK) ld8(P.aq[s], q + (size_t(t0 + qrow) * h_qk + j) * DK + 32 * s + 8 * grp);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * wave + 4 * grp + e;
-        if (tok < nc) vv[e] = io_traits<IO>::load(v + (size_t(t0 + tok) * h_v + h) * d_v + dv0 + col);
+        const int tok = min(16 * wave + 4 * grp + e, nc - 1);
+        P.vr[e] = v[(size_t(t0 + tok) * h_v + h) * d_v + dv0 + col];
       }
     }
-    __syncthreads();
+  };
+  auto commit = [&](const Pre& P, int cc, int buf) {
+    const int nc = min(C, eos - (bos + cc * C));
+    IO* sK = reinterpret_cast<IO*>(smem + buf * Lds::KBUF);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int x = tid + 256 * it;
+      if (x < C * PER_ROW) {
+        const int r = x / PER_ROW;
+        *reinterpret_cast<uint4*>(sK + r * KP + (x % PER_ROW) * E16) = r < nc ? P.kp[it] : uint4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < 4 * C) reinterpret_cast<float*>(smem + Lds::SC_OFF)[buf * 4 * C + tid] = P.sc;
+  };
+
+  auto step = [&](int cc, const Pre& P, Pre& Pn) {
+    const int buf = cc & 1;
+    const int t0 = bos + cc * C, nc = min(C, eos - t0);
+    const IO* sK = reinterpret_cast<const IO*>(smem + buf * Lds::KBUF);
+    const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF) + buf * 4 * C;
+    const bool more = cc + 1 < nchunk;
+    if (more) fetch(Pn, cc + 1);
+
+    // K^T fragments of the owned state blocks (for the state update), read early
+    E kt[SB][NTS];
+#pragma unroll
+    for (int bi = 0; bi < SB; ++bi) {
+      const int b = wave + 4 * bi;
+      if (b < KB) {
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) ld8col(kt[bi][s], sK + (32 * s + 8 * grp) * KP + 16 * b + col, KP);
+      }
+    }
 
     // (b) X = K S^T and Z = Q S^T for token block r = wave; Y = beta V - beta gamma X
     f4 z = zero4();
     if (wave < NB) {
       const int r = wave;
-      f4 x = zero4();
+      const bool qok = 16 * r + col < nc;
+      f4 x0 = zero4(), x1 = zero4(), z1 = zero4();
 #pragma unroll
-      for (int s = 0; s < KB; ++s) {
-        const uint4 sb = sS[s * 64 + lane];
-        ExactFrag<IO> ak, aq;
-        ak.load_row(sK + (16 * r + col) * KP + 16 * s + 4 * grp);
-        aq.load_row(sQ + (16 * r + col) * KP + 16 * s + 4 * grp);
-        x = ak.mma(sb, x);
-        z = aq.mma(sb, z);
+      for (int s = 0; s < NKS; ++s) {
+        E ak, bs, aq = P.aq[s];
+        ld8(ak, sK + (16 * r + col) * KP + 32 * s + 8 * grp);
+        xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
+        if (!qok) zero(aq);
+        if (s & 1) {
+          x1 = mma32(ak, bs, x1);
+          z1 = mma32(aq, bs, z1);
+        } else {
+          x0 = mma32(ak, bs, x0);
+          z = mma32(aq, bs, z);
+        }
       }
+      const f4 x = x0 + x1;
+      z = z + z1;
       f4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * r + 4 * grp + e;
-        y[e] = sSc[tok] * vv[e] - sSc[C + tok] * x[e];
+        float vv;
+        if constexpr (BF) vv = bf2f(P.vr[e]);
+        else vv = P.vr[e];
+        y[e] = tok < nc ? sSc[tok] * vv - sSc[C + tok] * x[e] : 0.f;
       }
-      sY[r * 64 + lane] = pack_frag<BF>(y);
+      xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // (c) U = T Y for block row r; also dec * U for the state update
+    // (c) Ud = T' Y for block row r
     if (wave < NB) {
       const int r = wave;
-      f4 u = zero4();
+      f4 uh = zero4(), ul = zero4();
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i <= r) u = mma_dd<BF>(tf[i], sY[i * 64 + lane], u);
-      sU[r * 64 + lane] = pack_frag<BF>(u);
-      f4 ud;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ud[e] = sSc[3 * C + 16 * r + 4 * grp + e] * u[e];
-      sUd[r * 64 + lane] = pack_frag<BF>(ud);
+      for (int s = 0; s < NTF; ++s) {
+        if (2 * s <= r) {
+          Sp yb;
+          xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
+          mm_es(P.tf[s], yb, uh, ul);
+        }
+      }
+      xb_write_split<BF, CP>(sUd, col, 16 * r + 4 * grp, uh + ul);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // (d) O = gamma Z + QKm U for block row r; S^T <- gamma_last S^T + K^T (dec U)
+    // (d) S^T <- gamma_last S^T + K^T Ud for the owned state blocks (the
+    // chain's critical path), then O = gamma Z + R Y for block row r.
+    const float glast = sSc[2 * C + nc - 1];
+#pragma unroll
+    for (int bi = 0; bi < SB; ++bi) {
+      const int b = wave + 4 * bi;
+      if (b < KB) {
+        f4 ah = st[bi] * glast, al = zero4();
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) {
+          Sp ub;
+          xb_read_split<BF, CP>(ub, sUd, col, 32 * s + 8 * grp);
+          mm_es(kt[bi][s], ub, ah, al);
+        }
+        st[bi] = ah + al;
+        xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
+      }
+    }
     if (wave < NB) {
       const int r = wave;
-      f4 o;
+      f4 oh, ol = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
+      for (int e = 0; e < 4; ++e) oh[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i <= r) o = mma_dd<BF>(qf[i], sU[i * 64 + lane], o);
+      for (int s = 0; s < NTF; ++s) {
+        if (2 * s <= r) {
+          Sp yb;
+          xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
+          mm_ss(P.rf[s], yb, oh, ol);
+        }
+      }
+      const f4 o = oh + ol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * r + 4 * grp + e;
         if (tok < nc) io_traits<IO>::store(out + (size_t(t0 + tok) * h_v + h) * d_v + dv0 + col, o[e]);
       }
     }
-    const float glast = sSc[2 * C + nc - 1];
-#pragma unroll
-    for (int bi = 0; bi < SB; ++bi) {
-      const int b = wave + 4 * bi;
-      if (b < KB) {
-        f4 acc = st[bi] * glast;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          ExactFrag<IO> a;
-          a.load_col(sK + (16 * i + 4 * grp) * KP + 16 * b + col, KP);
-          acc = a.mma(sUd[i * 64 + lane], acc);
-        }
-        st[bi] = acc;
-        sS[b * 64 + lane] = pack_frag<BF>(acc);
-      }
-    }
-    __syncthreads();
+    if (more) commit(Pn, cc + 1, buf ^ 1);
+    lds_barrier();
+  };
+
+  Pre PA, PB;
+  if (nchunk > 0) {
+    fetch(PA, 0);
+    commit(PA, 0, 0);
+  }
+  lds_barrier();
+  for (int cc = 0; cc < nchunk; cc += 2) {
+    step(cc, PA, PB);
+    if (cc + 1 < nchunk) step(cc + 1, PB, PA);
   }
 
 #pragma unroll
@@ -524,34 +720,38 @@ size_t chunked_max_chunks(const Dims& d, int chunk) {
   return (size_t(d.total_tokens) + size_t(d.num_seqs) * size_t(chunk - 1)) / size_t(chunk);
 }
 
-static size_t chunk_bytes(int chunk) {
+static size_t chunk_bytes(bool bf16, int chunk) {
   switch (chunk) {
-    case 16: return Geom<16>::BYTES;
-    case 32: return Geom<32>::BYTES;
-    case 64: return Geom<64>::BYTES;
+    case 16: return bf16 ? Geom<true, 16>::BYTES : Geom<false, 16>::BYTES;
+    case 32: return bf16 ? Geom<true, 32>::BYTES : Geom<false, 32>::BYTES;
+    case 64: return bf16 ? Geom<true, 64>::BYTES : Geom<false, 64>::BYTES;
   }
   return 0;
 }
 
-static size_t offsets_bytes(const Dims& d) { return (size_t(d.num_seqs + 1) * 4 + 255) / 256 * 256; }
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t offsets_bytes(const Dims& d) { return round256(size_t(d.num_seqs + 1) * 4); }
+static size_t table_bytes(const Dims& d, int chunk) { return round256(chunked_max_chunks(d, chunk) * 8); }
 
 size_t chunked_workspace_bytes(const Dims& d, int chunk) {
-  const size_t cb = chunk_bytes(chunk);
+  const size_t cb = chunk_bytes(d.bf16, chunk);
   if (cb == 0) return 0;
-  return offsets_bytes(d) + chunked_max_chunks(d, chunk) * size_t(d.h_v) * cb;
+  return offsets_bytes(d) + table_bytes(d, chunk) + chunked_max_chunks(d, chunk) * size_t(d.h_v) * cb;
 }
 
 template <typename IO, int DK, int C>
 static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                                    const float* beta, const int32_t* cu, const float* s_in, void* out,
                                    float* s_out, void* workspace, hipStream_t st) {
-  int32_t* chunk_off = static_cast<int32_t*>(workspace);
-  uint8_t* ws = static_cast<uint8_t*>(workspace) + offsets_bytes(d);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
+  int2* tab = reinterpret_cast<int2*>(base + offsets_bytes(d));
+  uint8_t* ws = base + offsets_bytes(d) + table_bytes(d, C);
   const size_t max_chunks = chunked_max_chunks(d, C);
   {
     Prof prof("chunk_offsets", st);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C, cu,
-                       chunk_off);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C,
+                       int(max_chunks), cu, chunk_off, tab);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -564,8 +764,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
     }
     Prof prof("chunk_prep", st);
     hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(256), lds,
-                       st, d.num_seqs, d.total_tokens, d.h_qk, d.h_v, static_cast<const IO*>(q),
-                       static_cast<const IO*>(k), g, beta, cu, chunk_off, ws);
+                       st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, tab, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -119,6 +119,53 @@ __device__ __forceinline__ f4 mma_f32(f4 a, f4 b, f4 c) {
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------- K = 32 slabs
+// Same convention with a contraction slab of 32: the A fragment lane holds
+// A[row = col][k = 8*grp + q] and the B fragment lane holds
+// B[k = 8*grp + q][n = col], q = 0..7; the D block layout is unchanged.  bf16
+// slabs are one v_mfma_f32_16x16x32_bf16 on 8 packed bf16 (a uint4); fp32
+// slabs are eight v_mfma_f32_16x16x4_f32, the q-th carrying k = 8*grp + q.
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+struct f8 {  // eight fp32 operand values of one lane
+  f4 a, b;
+};
+
+__device__ __forceinline__ f4 mma32(uint4 a, uint4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma32(const f8& a, const f8& b, f4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[0], b.a[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[1], b.a[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[2], b.a[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[3], b.a[3], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[0], b.b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[1], b.b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[2], b.b[2], c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[3], b.b[3], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return uint32_t(lo) | (uint32_t(hi) << 16); }
+
+// Round 4 fp32 to bf16 (8 bytes) and, optionally, the rounding residues (8 bytes).
+__device__ __forceinline__ uint2 bf16x4(f4 x) {
+  return uint2{pack2(f2bf(x[0]), f2bf(x[1])), pack2(f2bf(x[2]), f2bf(x[3]))};
+}
+__device__ __forceinline__ void split_bf16x4(f4 x, uint2& hi, uint2& lo) {
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split_bf16(x[i], h[i], l[i]);
+  hi = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+  lo = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+}
+__device__ __forceinline__ void split_bf16x8(const f8& x, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split_bf16x4(x.a, h0, l0);
+  split_bf16x4(x.b, h1, l1);
+  hi = uint4{h0.x, h0.y, h1.x, h1.y};
+  lo = uint4{l0.x, l0.y, l1.x, l1.y};
+}
+
 // ---------------------------------------------------------------- io element access
 template <typename IO>
 struct io_traits;

@@ -46,18 +46,32 @@ def shape(**kw):
     return gdn.GdnShape(**base)
 
 
+def expected_workspace(n, t, h_v, c, bf16=True):
+    """Chunk offsets (N+1 int32) and the per-chunk (first token, length)
+    table, each padded to 256 bytes, then per (chunk, value head): the
+    16-row x 32-column fragments of the lower triangles of T' and R (1, 2 or
+    6 per matrix for C = 16, 32, 64), each one 1 KiB plane per 8 values per
+    lane (T' rounded once to bf16: 1 plane; R split, or fp32: 2 planes), and
+    4 C scalars."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    max_chunks = (t + n * (c - 1)) // c
+    nf = {16: 1, 32: 2, 64: 6}[c]
+    per = nf * (1 if bf16 else 2) * 1024 + nf * 2 * 1024 + 4 * c * 4
+    return r256(4 * (n + 1)) + r256(8 * max_chunks) + max_chunks * h_v * per
+
+
 def test_workspace_size(lib):
     s = shape()
-    # offsets (N+1 int32, padded to 256) + ceil-bound chunks * h_v * per-chunk bytes
-    per = 2 * 10 * 1024 + 4 * 64 * 4
-    max_chunks = (4096 + 1 * 63) // 64
-    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64) == 256 + max_chunks * 32 * per
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64) == expected_workspace(1, 4096, 32, 64)
+    assert expected_workspace(1, 4096, 32, 64) == 256 + 512 + 64 * 32 * 19456
+    s32 = shape(io_dtype=gdn.GDN_DTYPE_F32)
+    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s32), 64) == expected_workspace(1, 4096, 32, 64, False)
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 48) == 0
     assert lib.gdn_prefill_chunked_workspace(None, 64) == 0
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(shape(h_v=24)), 64) == 0
     s2 = shape(num_seqs=32, total_tokens=73000)
-    assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s2), 32) == \
-        (33 * 4 + 255) // 256 * 256 + (73000 + 32 * 31) // 32 * 32 * (2 * 3 * 1024 + 4 * 32 * 4)
+    for c in (16, 32, 64):
+        assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s2), c) == expected_workspace(32, 73000, 32, c)
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
