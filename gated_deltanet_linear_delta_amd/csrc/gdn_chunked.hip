@@ -200,46 +200,26 @@ struct PrepLds {
 template <typename IO, int DK, int C>
 struct SweepLds {
   static constexpr bool BF = sizeof(IO) == 2;
-  static constexpr int CP = C < 32 ? 32 : C;           // token rows of a staged K / Q tile
-  static constexpr int DKP = DK < 32 ? 32 : DK;        // columns of a staged tile
-  static constexpr int RPP = DKP * int(sizeof(IO)) / 16;  // 16-byte pieces per tile row
-  static constexpr int CPR = DK * int(sizeof(IO)) / 16;   // pieces that hold data
-  static constexpr int SWZ = (RPP < 16 ? RPP : 16) - 1;   // stored piece = piece ^ (row & SWZ)
-  static constexpr int PPT = int(sizeof(IO));             // pieces per token of a 16-wide V row
-  // One stage holds every input of one chunk, each region a whole number of
-  // 1 KiB blocks (one global_load_lds_dwordx4 of 64 lanes fills one block).
-  static constexpr int NK = CP * RPP / 64;  // blocks of the K tile (and of Q)
-  static constexpr int NV = (C * PPT + 63) / 64;
-  static constexpr int NS = 1;              // 4 C scalars: C <= 64 pieces
-  static constexpr int NT = Geom<BF, C>::NF * Geom<BF, C>::TPL;
-  static constexpr int NR = Geom<BF, C>::NF * 2;
-  static constexpr int NBLK = 2 * NK + NV + NS + NT + NR;
-  static constexpr size_t K_OFF = 0;
-  static constexpr size_t Q_OFF = K_OFF + NK * 1024;
-  static constexpr size_t V_OFF = Q_OFF + NK * 1024;
-  static constexpr size_t SC_OFF = V_OFF + NV * 1024;
-  static constexpr size_t T_OFF = SC_OFF + NS * 1024;
-  static constexpr size_t R_OFF = T_OFF + NT * 1024;
-  static constexpr size_t STAGE = R_OFF + NR * 1024;
-  // exchange buffers: state (B fragments of S^T), Y and T'Y
-  static constexpr size_t XS = XBuf<BF, DKP>::PLANE;
-  static constexpr size_t XY = xb_bytes_split<BF, CP>();
-  static constexpr int NSTAGE = (2 * STAGE + XS + 2 * XY <= 160 * 1024) ? 2 : 1;
-  static constexpr size_t S_OFF = NSTAGE * STAGE;
-  static constexpr size_t Y_OFF = S_OFF + XS;
-  static constexpr size_t UD_OFF = Y_OFF + XY;
-  static constexpr size_t BYTES = UD_OFF + XY;
+  static constexpr int ESZ = int(sizeof(IO));
+  static constexpr int E16 = 16 / ESZ;
+  static constexpr int CP = C < 32 ? 32 : C;     // token rows of the staged K tile
+  static constexpr int DKP = DK < 32 ? 32 : DK;  // its columns
+  static constexpr int KP = DKP + E16;           // row stride (elements): 16-byte pad
+  static constexpr size_t KBUF = size_t(CP) * KP * ESZ;
+  static constexpr size_t K_OFF = 0;             // two K buffers
+  static constexpr size_t S_OFF = 2 * KBUF;      // state (B fragments of S^T)
+  static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
+  static constexpr size_t UD_OFF = Y_OFF + xb_bytes_split<BF, CP>();
+  static constexpr size_t SC_OFF = UD_OFF + xb_bytes_split<BF, CP>();  // two buffers of 4 C scalars
+  static constexpr size_t BYTES = SC_OFF + 2 * 4 * C * sizeof(float);
 };
 
-// One asynchronous global -> LDS copy of 64 x 16 bytes: lane l copies the 16
-// bytes at base + voff into LDS bytes [lds + 16 l, lds + 16 l + 16).  Issued
-// from inline assembly so that the compiler's wait-count bookkeeping does
-// not see it; completion is awaited explicitly with s_waitcnt vmcnt(0).
-__device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
-               : "memory", "m0");
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace
 
@@ -500,17 +480,17 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   using Lds = SweepLds<IO, DK, C>;
   using E = typename Types<BF>::E;
   using Sp = typename Types<BF>::S;
-  constexpr int NB = Geo::NB, KB = DK / 16, CP = Lds::CP, DKP = Lds::DKP;
-  constexpr int RPP = Lds::RPP, SWZ = Lds::SWZ, CPR = Lds::CPR, PPT = Lds::PPT;
+  constexpr int NB = Geo::NB, KB = DK / 16, CP = Lds::CP, DKP = Lds::DKP, KP = Lds::KP, E16 = Lds::E16;
   constexpr int NKS = DKP / 32, NTS = CP / 32;  // 32-wide slabs along d_k and along the chunk
   constexpr int SB = (KB + 3) / 4;              // state blocks per wave
   constexpr int NTF = (NB + 1) / 2;             // T' / R fragments per row block, at most
-  constexpr int ESZ = int(sizeof(IO));
+  constexpr int PER_ROW = DK / E16;             // 16-byte pieces per K row
+  constexpr int NIT = (C * PER_ROW + 255) / 256;
+  constexpr int QL = BF ? 1 : 2;                // loads per operand fragment (16 or 32 bytes)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sS = smem + Lds::S_OFF;
   uint8_t* sY = smem + Lds::Y_OFF;
   uint8_t* sUd = smem + Lds::UD_OFF;
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
 
   // Workgroups are dealt to the 8 XCDs round-robin; give the 16-row slices of
   // one head consecutive chain numbers on one XCD so they share its L2.
@@ -525,9 +505,9 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = wave_id();
 
-  // zero the exchange buffers: columns past C tokens or d_k are read as zero
-  for (int x = tid; x < int((Lds::BYTES - Lds::S_OFF) / 16); x += 256)
-    reinterpret_cast<uint4*>(sS)[x] = uint4{0u, 0u, 0u, 0u};
+  // zero LDS once: K rows / columns past C or d_k, and exchange columns past
+  // C or d_k, are read as zeros
+  for (int x = tid; x < int(Lds::SC_OFF / 16); x += 256) reinterpret_cast<uint4*>(smem)[x] = uint4{0u, 0u, 0u, 0u};
   lds_barrier();
 
   f4 st[SB];
@@ -546,146 +526,178 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   const int gc0 = chunk_off[n];
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
 
-  const uint32_t krow = uint32_t(h_qk * DK * ESZ);  // bytes between consecutive tokens of q / k
-  const uint32_t vrow = uint32_t(h_v * d_v * ESZ);  // and of v
+  const int kstride = h_qk * DK;  // elements between consecutive tokens of q / k
+  const int vstride = h_v * d_v;  // and of v
 
-  // Issue this wave's share of the copies of chunk cc into stage `stage`.
-  // Rows past the chunk's last token are clamped to it (their products are
-  // multiplied by zeros); columns past d_k copy real data that only ever
-  // meets zeros in the exchange buffers.
-  auto dma = [&](int cc, int stage) {
+  // Everything one chunk needs from global memory.  Loads are unconditional
+  // (token indices clamped into the chunk) so that each wave issues a fixed
+  // number of them, which the explicit wait after each prefetch relies on.
+  struct Pre {
+    uint4 kp[NIT];  // K rows, 16-byte pieces, for the LDS tile
+    float sc;       // one of the 4 C per-token scalars, for LDS
+    E tf[NTF];      // T' fragments of row block `wave`
+    Sp rf[NTF];     // R fragments of row block `wave`
+    E aq[NKS];      // Q rows of block `wave` as A fragments
+    IO vr[4];       // V values of block `wave` (raw)
+  };
+  auto fetch = [&](Pre& P, int cc) {
     const int t0 = bos + cc * C, nc = min(C, eos - t0);
-    const uint32_t sl = lds0 + uint32_t(stage * Lds::STAGE);
     const IO* kb = k + (size_t(t0) * h_qk + j) * DK;
-    const IO* qb = q + (size_t(t0) * h_qk + j) * DK;
-    const IO* vb = v + (size_t(t0) * h_v + h) * d_v + dv0;
     const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
 #pragma unroll
-    for (int b = 0; b < Lds::NBLK; ++b) {
-      if ((b & 3) != wave) continue;
-      const uint32_t dst = sl + uint32_t(b) * 1024u;
-      if (b < 2 * Lds::NK) {
-        const int bb = b < Lds::NK ? b : b - Lds::NK;
-        const int p = bb * 64 + lane;
-        const int row = p / RPP;
-        int piece = (p % RPP) ^ (row & SWZ);
-        piece = piece < CPR ? piece : 0;
-        const uint32_t voff = uint32_t(min(row, nc - 1)) * krow + uint32_t(piece * 16);
-        dma16(dst, b < Lds::NK ? static_cast<const void*>(kb) : static_cast<const void*>(qb), voff);
-      } else if (b < 2 * Lds::NK + Lds::NV) {
-        const int p = (b - 2 * Lds::NK) * 64 + lane;
-        const int tok = min(p / PPT, nc - 1);
-        dma16(dst, vb, uint32_t(tok) * vrow + uint32_t((p % PPT) * 16));
-      } else if (b < 2 * Lds::NK + Lds::NV + Lds::NS) {
-        dma16(dst, wsb + Geo::SCAL_OFF, uint32_t(min(lane, C - 1) * 16));
-      } else if (b < 2 * Lds::NK + Lds::NV + Lds::NS + Lds::NT) {
-        const int f = b - (2 * Lds::NK + Lds::NV + Lds::NS);
-        dma16(dst, wsb + Geo::T_OFF + size_t(f) * 1024, uint32_t(lane * 16));
-      } else {
-        const int f = b - (2 * Lds::NK + Lds::NV + Lds::NS + Lds::NT);
-        dma16(dst, wsb + Geo::R_OFF + size_t(f) * 1024, uint32_t(lane * 16));
+    for (int it = 0; it < NIT; ++it) {
+      const int x = min(tid + 256 * it, C * PER_ROW - 1);
+      const int r = min(x / PER_ROW, nc - 1);
+      P.kp[it] = *reinterpret_cast<const uint4*>(kb + r * kstride + (x % PER_ROW) * E16);
+    }
+    P.sc = reinterpret_cast<const float*>(wsb + Geo::SCAL_OFF)[tid % (4 * C)];
+    if (wave < NB) {
+      const uint8_t* tp = wsb + Geo::T_OFF + size_t(frag_base(wave)) * Geo::TPL * Geo::PLANE + lane * 16;
+      const uint8_t* rp = wsb + Geo::R_OFF + size_t(frag_base(wave)) * 2 * Geo::PLANE + lane * 16;
+#pragma unroll
+      for (int s = 0; s < NTF; ++s) {
+        if (2 * s <= wave) {
+          if constexpr (BF) {
+            P.tf[s] = *reinterpret_cast<const uint4*>(tp + s * Geo::PLANE);
+            P.rf[s].hi = *reinterpret_cast<const uint4*>(rp + s * 2 * Geo::PLANE);
+            P.rf[s].lo = *reinterpret_cast<const uint4*>(rp + s * 2 * Geo::PLANE + Geo::PLANE);
+          } else {
+            P.tf[s].a = *reinterpret_cast<const f4*>(tp + s * 2 * Geo::PLANE);
+            P.tf[s].b = *reinterpret_cast<const f4*>(tp + s * 2 * Geo::PLANE + Geo::PLANE);
+            P.rf[s].a = *reinterpret_cast<const f4*>(rp + s * 2 * Geo::PLANE);
+            P.rf[s].b = *reinterpret_cast<const f4*>(rp + s * 2 * Geo::PLANE + Geo::PLANE);
+          }
+        }
       }
+      const IO* qrow = q + (size_t(t0) * h_qk + j) * DK + min(16 * wave + col, nc - 1) * kstride + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        // lanes whose columns lie past d_k (d_k = 16) reread the row's first
+        // 8 columns, which stays in bounds; those products meet zeros of S
+        ld8(P.aq[s], qrow + (32 * s + 8 * grp < DK ? 32 * s : -8 * grp));
+      }
+      const IO* vrow = v + (size_t(t0) * h_v + h) * d_v + dv0 + col;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) P.vr[e] = vrow[min(16 * wave + 4 * grp + e, nc - 1) * vstride];
     }
   };
-
-  // LDS address of element (row, column e) of a staged K or Q tile
-  auto tile_at = [&](const uint8_t* tile, int row, int e) {
-    const int piece = (e * ESZ) >> 4;
-    return tile + (row * RPP + (piece ^ (row & SWZ))) * 16 + ((e * ESZ) & 15);
+  // vector-memory operations one fetch issues, per wave (the waits below count them)
+  constexpr auto fetch_ops = [](int w) {
+    int n = NIT + 1;
+    if (w < NB) n += (w / 2 + 1) * (QL + 2) + NKS * QL + 4;
+    return n;
+  };
+  auto wait_fetch = [&]() {
+    // everything older than the fetch just issued has completed
+    switch (wave) {
+      case 0: vm_wait<fetch_ops(0)>(); break;
+      case 1: vm_wait<fetch_ops(1)>(); break;
+      case 2: vm_wait<fetch_ops(2)>(); break;
+      default: vm_wait<fetch_ops(3)>(); break;
+    }
+  };
+  auto commit = [&](const Pre& P, int cc, int buf) {
+    const int nc = min(C, eos - (bos + cc * C));
+    IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int x = tid + 256 * it;
+      if (x < C * PER_ROW) {
+        const int r = x / PER_ROW;
+        *reinterpret_cast<uint4*>(sK + r * KP + (x % PER_ROW) * E16) = r < nc ? P.kp[it] : uint4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < 4 * C) reinterpret_cast<float*>(smem + Lds::SC_OFF)[buf * 4 * C + tid] = P.sc;
   };
 
   f4 o_prev = zero4();
   int o_t0 = 0, o_nc = 0;
   auto store_o = [&]() {
     if (wave < NB) {
+      IO* ob = out + (size_t(o_t0) * h_v + h) * d_v + dv0 + col;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * wave + 4 * grp + e;
-        if (tok < o_nc) io_traits<IO>::store(out + (size_t(o_t0 + tok) * h_v + h) * d_v + dv0 + col, o_prev[e]);
+        if (tok < o_nc) io_traits<IO>::store(ob + tok * vstride, o_prev[e]);
       }
     }
   };
 
-  if (nchunk > 0) {
-    dma(0, 0);
-    vm_wait_all();
-  }
-  lds_barrier();
+  // per-lane LDS offsets (elements) within a K tile
+  const int arow = col * KP + 8 * grp;        // A fragment: row col of a 16-row block, columns 8 grp ..
+  const int tcol = 8 * grp * KP + col;        // K^T fragment: tokens 8 grp .., column col of a block
 
-  for (int cc = 0; cc < nchunk; ++cc) {
-    const int stage = Lds::NSTAGE == 2 ? (cc & 1) : 0;
+  auto step = [&](int cc, const Pre& P, Pre& Pn) {
+    const int buf = cc & 1;
     const int t0 = bos + cc * C, nc = min(C, eos - t0);
-    const uint8_t* sg = smem + stage * Lds::STAGE;
-    const uint8_t* tK = sg + Lds::K_OFF;
-    const uint8_t* tQ = sg + Lds::Q_OFF;
-    const float* sSc = reinterpret_cast<const float*>(sg + Lds::SC_OFF);
+    const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
+    const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF) + buf * 4 * C;
     const bool more = cc + 1 < nchunk;
+    if (more) {
+      fetch(Pn, cc + 1);
+      wait_fetch();
+    } else {
+      vm_wait<0>();
+    }
     if (cc > 0) store_o();
-    if (Lds::NSTAGE == 2 && more) dma(cc + 1, stage ^ 1);
 
     // (b) X = K S^T and Z = Q S^T for token block r = wave; Y = beta V - beta gamma X
-    f4 z = zero4();
+    f4 z = zero4(), x = zero4();
     if (wave < NB) {
       const int r = wave;
-      f4 x0 = zero4(), x1 = zero4(), z1 = zero4();
+      const bool qok = 16 * r + col < nc;
+      f4 x1 = zero4(), z1 = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        E ak, aq, bs;
-        if constexpr (BF) {
-          ak = *reinterpret_cast<const uint4*>(tile_at(tK, 16 * r + col, 32 * s + 8 * grp));
-          aq = *reinterpret_cast<const uint4*>(tile_at(tQ, 16 * r + col, 32 * s + 8 * grp));
-        } else {
-          ak.a = *reinterpret_cast<const f4*>(tile_at(tK, 16 * r + col, 32 * s + 8 * grp));
-          ak.b = *reinterpret_cast<const f4*>(tile_at(tK, 16 * r + col, 32 * s + 8 * grp + 4));
-          aq.a = *reinterpret_cast<const f4*>(tile_at(tQ, 16 * r + col, 32 * s + 8 * grp));
-          aq.b = *reinterpret_cast<const f4*>(tile_at(tQ, 16 * r + col, 32 * s + 8 * grp + 4));
-        }
+        E ak, bs, aq = P.aq[s];
+        ld8(ak, sK + 16 * r * KP + arow + 32 * s);
         xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
+        if (!qok) zero(aq);
         if (s & 1) {
           x1 = mma32(ak, bs, x1);
           z1 = mma32(aq, bs, z1);
         } else {
-          x0 = mma32(ak, bs, x0);
+          x = mma32(ak, bs, x);
           z = mma32(aq, bs, z);
         }
       }
-      const f4 x = x0 + x1;
+      x = x + x1;
       z = z + z1;
       f4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * r + 4 * grp + e;
-        const IO vraw = *reinterpret_cast<const IO*>(sg + Lds::V_OFF + (tok * 16 + col) * ESZ);
         float vv;
-        if constexpr (BF) vv = bf2f(vraw);
-        else vv = vraw;
+        if constexpr (BF) vv = bf2f(P.vr[e]);
+        else vv = P.vr[e];
         y[e] = tok < nc ? sSc[tok] * vv - sSc[C + tok] * x[e] : 0.f;
       }
       xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
     }
     lds_barrier();
 
-    // (c) Ud = T' Y for block row r
+    // (c) Ud = T' Y for block row r (Y fragments kept for O); K^T fragments for (d)
+    Sp yb[NTF];
     if (wave < NB) {
       const int r = wave;
       f4 uh = zero4(), ul = zero4();
 #pragma unroll
       for (int s = 0; s < NTF; ++s) {
         if (2 * s <= r) {
-          const uint8_t* tp = sg + Lds::T_OFF + size_t(frag_base(r) + s) * Geo::TPL * 1024 + lane * 16;
-          E tf;
-          if constexpr (BF) {
-            tf = *reinterpret_cast<const uint4*>(tp);
-          } else {
-            tf.a = *reinterpret_cast<const f4*>(tp);
-            tf.b = *reinterpret_cast<const f4*>(tp + 1024);
-          }
-          Sp yb;
-          xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
-          mm_es(tf, yb, uh, ul);
+          xb_read_split<BF, CP>(yb[s], sY, col, 32 * s + 8 * grp);
+          mm_es(P.tf[s], yb[s], uh, ul);
         }
       }
       xb_write_split<BF, CP>(sUd, col, 16 * r + 4 * grp, uh + ul);
+    }
+    E kt[SB][NTS];
+#pragma unroll
+    for (int bi = 0; bi < SB; ++bi) {
+      const int b = wave + 4 * bi;
+      if (b < KB) {
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
+      }
     }
     lds_barrier();
 
@@ -699,24 +711,9 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
         f4 ah = st[bi] * glast, al = zero4();
 #pragma unroll
         for (int s = 0; s < NTS; ++s) {
-          E kt;
-          if constexpr (BF) {
-            uint16_t e8[8];
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq)
-              e8[qq] = *reinterpret_cast<const uint16_t*>(tile_at(tK, 32 * s + 8 * grp + qq, 16 * b + col));
-            kt = uint4{pack2(e8[0], e8[1]), pack2(e8[2], e8[3]), pack2(e8[4], e8[5]), pack2(e8[6], e8[7])};
-          } else {
-            float e8[8];
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq)
-              e8[qq] = *reinterpret_cast<const float*>(tile_at(tK, 32 * s + 8 * grp + qq, 16 * b + col));
-            kt.a = f4{e8[0], e8[1], e8[2], e8[3]};
-            kt.b = f4{e8[4], e8[5], e8[6], e8[7]};
-          }
           Sp ub;
           xb_read_split<BF, CP>(ub, sUd, col, 32 * s + 8 * grp);
-          mm_es(kt, ub, ah, al);
+          mm_es(kt[bi][s], ub, ah, al);
         }
         st[bi] = ah + al;
         xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
@@ -728,33 +725,28 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
 #pragma unroll
       for (int e = 0; e < 4; ++e) oh[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
 #pragma unroll
-      for (int s = 0; s < NTF; ++s) {
-        if (2 * s <= r) {
-          const uint8_t* rp = sg + Lds::R_OFF + size_t(frag_base(r) + s) * 2048 + lane * 16;
-          Sp rf;
-          if constexpr (BF) {
-            rf.hi = *reinterpret_cast<const uint4*>(rp);
-            rf.lo = *reinterpret_cast<const uint4*>(rp + 1024);
-          } else {
-            rf.a = *reinterpret_cast<const f4*>(rp);
-            rf.b = *reinterpret_cast<const f4*>(rp + 1024);
-          }
-          Sp yb;
-          xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
-          mm_ss(rf, yb, oh, ol);
-        }
-      }
+      for (int s = 0; s < NTF; ++s)
+        if (2 * s <= r) mm_ss(P.rf[s], yb[s], oh, ol);
       o_prev = oh + ol;
     }
     o_t0 = t0;
     o_nc = nc;
-    if (Lds::NSTAGE == 1 && more) {
-      lds_barrier();  // every wave is done with the single stage
-      dma(cc + 1, 0);
-    }
-    vm_wait_all();
+    if (more) commit(Pn, cc + 1, buf ^ 1);
     lds_barrier();
+  };
+
+  Pre PA, PB;
+  if (nchunk > 0) {
+    fetch(PA, 0);
+    vm_wait<0>();
+    commit(PA, 0, 0);
   }
+  lds_barrier();
+  for (int cc = 0; cc < nchunk; cc += 2) {
+    step(cc, PA, PB);
+    if (cc + 1 < nchunk) step(cc + 1, PB, PA);
+  }
+  vm_wait<0>();
   if (nchunk > 0) store_o();
 
 #pragma unroll

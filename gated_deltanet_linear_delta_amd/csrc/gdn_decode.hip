@@ -33,25 +33,32 @@ __device__ __forceinline__ void load4(const IO* p, float* x) {
   }
 }
 
-template <typename IO, int DK>
+// RPL rows per lane group: each lane keeps 2 * RPL float4 loads of the state
+// in flight, enough bytes per wave to keep HBM busy at large batch.
+template <typename IO, int DK, int RPL>
 __global__ __launch_bounds__(16 * (DK / 8)) void decode_kernel(
     int total_rows, int h_qk, int h_v, int d_v, const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     const float* s_in, IO* __restrict__ out, float* s_out) {
   constexpr int LPR = DK / 8;
   const int l = threadIdx.x % LPR;
-  const int row = blockIdx.x * 16 + threadIdx.x / LPR;
-  if (row >= total_rows) return;  // whole row groups leave together
-  const int i = row % d_v;
-  const int bh = row / d_v;  // b * h_v + h
+  // 16 * RPL consecutive rows per workgroup; d_v is a multiple of 16 * RPL, so
+  // they all belong to one (sequence, head)
+  const int row0 = (blockIdx.x * 16 + threadIdx.x / LPR) * RPL;
+  if (row0 >= total_rows) return;  // whole row groups leave together
+  const int bh = row0 / d_v;  // b * h_v + h
   const int h = bh % h_v;
   const int b = bh / h_v;
   const int j = h / (h_v / h_qk);
   const int c0 = 4 * l, c1 = DK / 2 + 4 * l;
 
-  const float* sr = s_in + size_t(row) * DK;
-  f4 sa = *reinterpret_cast<const f4*>(sr + c0);
-  f4 sb = *reinterpret_cast<const f4*>(sr + c1);
+  f4 sa[RPL], sb[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const float* sr = s_in + size_t(row0 + r) * DK;
+    sa[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c0));
+    sb[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c1));
+  }
   const IO* kp = k + (size_t(b) * h_qk + j) * DK;
   const IO* qp = q + (size_t(b) * h_qk + j) * DK;
   float kv[8], qv[8];
@@ -61,42 +68,58 @@ __global__ __launch_bounds__(16 * (DK / 8)) void decode_kernel(
   load4(qp + c1, qv + 4);
   const float alpha = expf(g[bh]);
   const float bt = beta[bh];
-  const float vi = io_traits<IO>::load(v + size_t(bh) * d_v + i);
-
-  float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-  float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f, kq0 = 0.f, kq1 = 0.f;
+  float vi[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) vi[r] = io_traits<IO>::load(v + size_t(row0 + r));
+  float kq0 = 0.f, kq1 = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    p0 = fmaf(s[e], kv[e], p0);
-    p1 = fmaf(s[e + 4], kv[e + 4], p1);
-    r0 = fmaf(s[e], qv[e], r0);
-    r1 = fmaf(s[e + 4], qv[e + 4], r1);
     kq0 = fmaf(kv[e], qv[e], kq0);
     kq1 = fmaf(kv[e + 4], qv[e + 4], kq1);
   }
-  const float p = sum_lanes<LPR>(p0 + p1);
-  const float r = sum_lanes<LPR>(r0 + r1);
   const float kq = sum_lanes<LPR>(kq0 + kq1);
-  const float u = bt * (vi - alpha * p);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], u * kv[e]);
-  float* so = s_out + size_t(row) * DK;
-  *reinterpret_cast<f4*>(so + c0) = f4{s[0], s[1], s[2], s[3]};
-  *reinterpret_cast<f4*>(so + c1) = f4{s[4], s[5], s[6], s[7]};
-  if (l == 0) io_traits<IO>::store(out + size_t(bh) * d_v + i, fmaf(alpha, r, u * kq));
+  for (int r = 0; r < RPL; ++r) {
+    float s[8] = {sa[r][0], sa[r][1], sa[r][2], sa[r][3], sb[r][0], sb[r][1], sb[r][2], sb[r][3]};
+    float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p0 = fmaf(s[e], kv[e], p0);
+      p1 = fmaf(s[e + 4], kv[e + 4], p1);
+      r0 = fmaf(s[e], qv[e], r0);
+      r1 = fmaf(s[e + 4], qv[e + 4], r1);
+    }
+    const float p = sum_lanes<LPR>(p0 + p1);
+    const float rq = sum_lanes<LPR>(r0 + r1);
+    const float u = bt * (vi[r] - alpha * p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], u * kv[e]);
+    float* so = s_out + size_t(row0 + r) * DK;
+    __builtin_nontemporal_store(f4{s[0], s[1], s[2], s[3]}, reinterpret_cast<f4*>(so + c0));
+    __builtin_nontemporal_store(f4{s[4], s[5], s[6], s[7]}, reinterpret_cast<f4*>(so + c1));
+    if (l == 0) io_traits<IO>::store(out + size_t(row0 + r), fmaf(alpha, rq, u * kq));
+  }
 }
 
+// Large batches use 4 rows per lane group (more bytes in flight per wave);
+// small ones 1, to spread the few rows over more compute units.
 template <typename IO, int DK>
 static hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, const float* s_in, void* out, float* s_out,
                                   hipStream_t st) {
   const int rows = d.num_seqs * d.h_v * d.d_v;
   if (rows == 0) return hipSuccess;
-  dim3 grid((rows + 15) / 16), block(16 * (DK / 8));
+  dim3 block(16 * (DK / 8));
   Prof prof("decode", st);
-  hipLaunchKernelGGL((decode_kernel<IO, DK>), grid, block, 0, st, rows, d.h_qk, d.h_v, d.d_v,
-                     static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g, beta,
-                     s_in, static_cast<IO*>(out), s_out);
+  if (rows >= 65536 && d.d_v % 64 == 0) {
+    hipLaunchKernelGGL((decode_kernel<IO, DK, 4>), dim3((rows + 63) / 64), block, 0, st, rows, d.h_qk, d.h_v,
+                       d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g,
+                       beta, s_in, static_cast<IO*>(out), s_out);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<IO, DK, 1>), dim3((rows + 15) / 16), block, 0, st, rows, d.h_qk, d.h_v,
+                       d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g,
+                       beta, s_in, static_cast<IO*>(out), s_out);
+  }
   return hipGetLastError();
 }
 
