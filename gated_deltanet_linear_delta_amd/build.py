@@ -24,9 +24,11 @@ ROOT = os.path.dirname(PKG)
 SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_scan.hip", "gdn_chunked.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU instructions are kept out of the device code.
+# Packed fp32 VALU instructions are kept out of the device code.  MFMA
+# accumulators live in ordinary VGPRs (no copies out of AGPRs).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -94,6 +94,17 @@ __device__ __forceinline__ void ld8(f8& d, const float* p) {
   d.a = *reinterpret_cast<const f4*>(p);
   d.b = *reinterpret_cast<const f4*>(p + 4);
 }
+// LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// result lane i, element m is element i % 4 of the 8 bytes addressed by lane
+// 4 m + i / 4 of the group.  So if lane 4 m + a addresses row m, columns
+// 4 a .. 4 a + 3 of a row-major bf16 tile, lane i receives rows 0..3 of
+// column i: four consecutive rows of one column, as an operand wants them.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4v lds_s4v;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p)));
+}
+
 // 8 elements of a column (stride apart) as an operand.
 __device__ __forceinline__ void ld8col(uint4& d, const uint16_t* p, int stride) {
   d = uint4{pack2(p[0], p[stride]), pack2(p[2 * stride], p[3 * stride]), pack2(p[4 * stride], p[5 * stride]),
@@ -219,6 +230,45 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Raw buffer resources (stride 0): a load whose bytes lie at or past `bytes`
+// returns zeros and such a store is dropped, per dword.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ void bload_op(uint4& d, Rsrc r, uint32_t off) { d = bload16(r, off); }
+__device__ __forceinline__ void bload_op(f8& d, Rsrc r, uint32_t off) {
+  const uint4 a = bload16(r, off), b = bload16(r, off + 16);
+  d.a = f4{__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
+  d.b = f4{__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
+}
+template <typename IO>
+__device__ __forceinline__ IO bload_el(Rsrc r, uint32_t off) {
+  if constexpr (sizeof(IO) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <typename IO>
+__device__ __forceinline__ void bstore_el(Rsrc r, uint32_t off, float x) {
+  if constexpr (sizeof(IO) == 2) __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), r, off, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+__device__ __forceinline__ float io_val(uint16_t x) { return bf2f(x); }
+__device__ __forceinline__ float io_val(float x) { return x; }
+// A split (bf16 hi + lo, two planes `plane` bytes apart) or fp32 operand from global memory.
+__device__ __forceinline__ void ld_split(sp8& d, const uint8_t* p, int plane) {
+  d.hi = *reinterpret_cast<const uint4*>(p);
+  d.lo = *reinterpret_cast<const uint4*>(p + plane);
+}
+__device__ __forceinline__ void ld_split(f8& d, const uint8_t* p, int plane) {
+  d.a = *reinterpret_cast<const f4*>(p);
+  d.b = *reinterpret_cast<const f4*>(p + plane);
 }
 
 }  // namespace
@@ -526,139 +576,139 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   const int gc0 = chunk_off[n];
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
 
+  constexpr int ESZ = int(sizeof(IO));
   const int kstride = h_qk * DK;  // elements between consecutive tokens of q / k
   const int vstride = h_v * d_v;  // and of v
 
-  // Everything one chunk needs from global memory.  Loads are unconditional
-  // (token indices clamped into the chunk) so that each wave issues a fixed
-  // number of them, which the explicit wait after each prefetch relies on.
+  // Everything one chunk needs from global memory, fetched one chunk ahead
+  // in three parts spread over the step.  Token rows of q, k, v (and of the
+  // output) go through buffer resources whose range ends with the chunk's
+  // last token, so rows past it read as zeros and stores there are dropped.
+  // Every wave issues the same loads in the same order whatever its role (a
+  // lane whose value is not needed reads one shared 16-byte line instead),
+  // so the waits below can count them.
   struct Pre {
-    uint4 kp[NIT];  // K rows, 16-byte pieces, for the LDS tile
-    float sc;       // one of the 4 C per-token scalars, for LDS
-    E tf[NTF];      // T' fragments of row block `wave`
-    Sp rf[NTF];     // R fragments of row block `wave`
-    E aq[NKS];      // Q rows of block `wave` as A fragments
-    IO vr[4];       // V values of block `wave` (raw)
+    uint4 kp[NIT];  // K rows, 16-byte pieces, for the LDS tile     (part A)
+    float sc;       // one of the 4 C per-token scalars, for LDS    (part A)
+    E tf[NTF];      // T' fragments of row block `wave`             (part B)
+    Sp rf[NTF];     // R fragments of row block `wave`              (part B)
+    E aq[NKS];      // Q rows of block `wave` as A fragments        (part C)
+    IO vr[4];       // V values of block `wave`                     (part C)
   };
-  auto fetch = [&](Pre& P, int cc) {
-    const int t0 = bos + cc * C, nc = min(C, eos - t0);
-    const IO* kb = k + (size_t(t0) * h_qk + j) * DK;
+  constexpr int NA = NIT + 1, NBL = NTF * (QL + 2), NCL = NKS * QL + 4;
+  (void)NBL;
+  (void)NCL;
+  const bool rowblk = NB >= 4 || wave < NB;
+
+  // per-lane byte offsets, relative to a chunk's first token row
+  uint32_t koff[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int x = tid + 256 * it;
+    koff[it] = x < C * PER_ROW ? uint32_t(((x / PER_ROW) * kstride + (x % PER_ROW) * E16) * ESZ) : 0x80000000u;
+  }
+  uint32_t qoff[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+    qoff[s] = uint32_t(((16 * wave + col) * kstride + (32 * s + 8 * grp < DK ? 32 * s + 8 * grp : 0)) * ESZ);
+  uint32_t voff[4];  // also the output's
+#pragma unroll
+  for (int e = 0; e < 4; ++e) voff[e] = uint32_t(((16 * wave + 4 * grp + e) * vstride + col) * ESZ);
+  const uint32_t kq_tail = uint32_t(DK * ESZ), v_tail = uint32_t(16 * ESZ);
+
+  auto chunk_t0 = [&](int cc) { return bos + cc * C; };
+  auto chunk_nc = [&](int cc) { return min(C, eos - chunk_t0(cc)); };
+  auto fetchA = [&](Pre& P, int cc) {
+    const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
+    const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) P.kp[it] = bload16(rk, koff[it]);
     const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int x = min(tid + 256 * it, C * PER_ROW - 1);
-      const int r = min(x / PER_ROW, nc - 1);
-      P.kp[it] = *reinterpret_cast<const uint4*>(kb + r * kstride + (x % PER_ROW) * E16);
-    }
     P.sc = reinterpret_cast<const float*>(wsb + Geo::SCAL_OFF)[tid % (4 * C)];
-    if (wave < NB) {
-      const uint8_t* tp = wsb + Geo::T_OFF + size_t(frag_base(wave)) * Geo::TPL * Geo::PLANE + lane * 16;
-      const uint8_t* rp = wsb + Geo::R_OFF + size_t(frag_base(wave)) * 2 * Geo::PLANE + lane * 16;
+  };
+  auto fetchB = [&](Pre& P, int cc) {
+    const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
+    const int rb = rowblk ? wave : 0;
+    const uint8_t* tp = wsb + Geo::T_OFF + size_t(frag_base(rb)) * Geo::TPL * Geo::PLANE;
+    const uint8_t* rp = wsb + Geo::R_OFF + size_t(frag_base(rb)) * 2 * Geo::PLANE;
 #pragma unroll
-      for (int s = 0; s < NTF; ++s) {
-        if (2 * s <= wave) {
-          if constexpr (BF) {
-            P.tf[s] = *reinterpret_cast<const uint4*>(tp + s * Geo::PLANE);
-            P.rf[s].hi = *reinterpret_cast<const uint4*>(rp + s * 2 * Geo::PLANE);
-            P.rf[s].lo = *reinterpret_cast<const uint4*>(rp + s * 2 * Geo::PLANE + Geo::PLANE);
-          } else {
-            P.tf[s].a = *reinterpret_cast<const f4*>(tp + s * 2 * Geo::PLANE);
-            P.tf[s].b = *reinterpret_cast<const f4*>(tp + s * 2 * Geo::PLANE + Geo::PLANE);
-            P.rf[s].a = *reinterpret_cast<const f4*>(rp + s * 2 * Geo::PLANE);
-            P.rf[s].b = *reinterpret_cast<const f4*>(rp + s * 2 * Geo::PLANE + Geo::PLANE);
-          }
-        }
+    for (int s = 0; s < NTF; ++s) {
+      const bool need = rowblk && 2 * s <= wave;
+      const uint8_t* t = tp + (need ? s * Geo::TPL * Geo::PLANE + lane * 16 : 0);
+      const uint8_t* r = rp + (need ? s * 2 * Geo::PLANE + lane * 16 : 0);
+      if constexpr (BF) {
+        P.tf[s] = *reinterpret_cast<const uint4*>(t);
+      } else {
+        P.tf[s].a = *reinterpret_cast<const f4*>(t);
+        P.tf[s].b = *reinterpret_cast<const f4*>(t + (need ? Geo::PLANE : 0));
       }
-      const IO* qrow = q + (size_t(t0) * h_qk + j) * DK + min(16 * wave + col, nc - 1) * kstride + 8 * grp;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        // lanes whose columns lie past d_k (d_k = 16) reread the row's first
-        // 8 columns, which stays in bounds; those products meet zeros of S
-        ld8(P.aq[s], qrow + (32 * s + 8 * grp < DK ? 32 * s : -8 * grp));
-      }
-      const IO* vrow = v + (size_t(t0) * h_v + h) * d_v + dv0 + col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) P.vr[e] = vrow[min(16 * wave + 4 * grp + e, nc - 1) * vstride];
+      ld_split(P.rf[s], r, need ? Geo::PLANE : 0);
     }
   };
-  // vector-memory operations one fetch issues, per wave (the waits below count them)
-  constexpr auto fetch_ops = [](int w) {
-    int n = NIT + 1;
-    if (w < NB) n += (w / 2 + 1) * (QL + 2) + NKS * QL + 4;
-    return n;
+  auto fetchC = [&](Pre& P, int cc) {
+    const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
+    const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) bload_op(P.aq[s], rq, qoff[s]);
+    const Rsrc rv = make_rsrc(v + (size_t(t0) * h_v + h) * d_v + dv0, uint32_t((nc - 1) * vstride * ESZ) + v_tail);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) P.vr[e] = bload_el<IO>(rv, voff[e]);
   };
-  auto wait_fetch = [&]() {
-    // everything older than the fetch just issued has completed
-    switch (wave) {
-      case 0: vm_wait<fetch_ops(0)>(); break;
-      case 1: vm_wait<fetch_ops(1)>(); break;
-      case 2: vm_wait<fetch_ops(2)>(); break;
-      default: vm_wait<fetch_ops(3)>(); break;
-    }
-  };
-  auto commit = [&](const Pre& P, int cc, int buf) {
-    const int nc = min(C, eos - (bos + cc * C));
+  auto commit = [&](const Pre& P, int buf) {
     IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int x = tid + 256 * it;
-      if (x < C * PER_ROW) {
-        const int r = x / PER_ROW;
-        *reinterpret_cast<uint4*>(sK + r * KP + (x % PER_ROW) * E16) = r < nc ? P.kp[it] : uint4{0u, 0u, 0u, 0u};
-      }
+      if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
     }
     if (tid < 4 * C) reinterpret_cast<float*>(smem + Lds::SC_OFF)[buf * 4 * C + tid] = P.sc;
   };
 
+  // O of the previous chunk; stored at the start of the next step, after the
+  // next prefetch is under way
   f4 o_prev = zero4();
-  int o_t0 = 0, o_nc = 0;
+  int o_cc = -1;  // none yet: an empty range drops the stores
   auto store_o = [&]() {
-    if (wave < NB) {
-      IO* ob = out + (size_t(o_t0) * h_v + h) * d_v + dv0 + col;
+    const int t0 = chunk_t0(max(o_cc, 0)), nc = chunk_nc(max(o_cc, 0));
+    const uint32_t bytes = o_cc < 0 ? 0u : uint32_t((nc - 1) * vstride * ESZ) + v_tail;
+    const Rsrc ro = make_rsrc(out + (size_t(t0) * h_v + h) * d_v + dv0, bytes);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * wave + 4 * grp + e;
-        if (tok < o_nc) io_traits<IO>::store(ob + tok * vstride, o_prev[e]);
-      }
-    }
+    for (int e = 0; e < 4; ++e) bstore_el<IO>(ro, voff[e], o_prev[e]);
   };
 
   // per-lane LDS offsets (elements) within a K tile
-  const int arow = col * KP + 8 * grp;        // A fragment: row col of a 16-row block, columns 8 grp ..
-  const int tcol = 8 * grp * KP + col;        // K^T fragment: tokens 8 grp .., column col of a block
+  const int arow = col * KP + 8 * grp;  // A fragment: row col of a 16-row block, columns 8 grp ..
+  const int tcol = 8 * grp * KP + col;  // K^T fragment: tokens 8 grp .., column col of a block
+  // the same fragment by two transpose reads: this lane addresses token
+  // 8 grp + col / 4 (+ 4), columns 4 (col % 4) .. + 3 of the block
+  const int trow = (8 * grp + col / 4) * KP + 4 * (col % 4);
 
   auto step = [&](int cc, const Pre& P, Pre& Pn) {
     const int buf = cc & 1;
-    const int t0 = bos + cc * C, nc = min(C, eos - t0);
+    const int nc = chunk_nc(cc);
+    const int cn = min(cc + 1, nchunk - 1);  // the last step refetches its own chunk, unused
     const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
     const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF) + buf * 4 * C;
-    const bool more = cc + 1 < nchunk;
-    if (more) {
-      fetch(Pn, cc + 1);
-      wait_fetch();
-    } else {
-      vm_wait<0>();
-    }
-    if (cc > 0) store_o();
+    fetchA(Pn, cn);
+    store_o();
+    vm_wait<NA + 4>();  // parts B and C of this chunk have landed
 
     // (b) X = K S^T and Z = Q S^T for token block r = wave; Y = beta V - beta gamma X
     f4 z = zero4(), x = zero4();
-    if (wave < NB) {
+    if (rowblk) {
       const int r = wave;
-      const bool qok = 16 * r + col < nc;
       f4 x1 = zero4(), z1 = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        E ak, bs, aq = P.aq[s];
+        E ak, bs;
         ld8(ak, sK + 16 * r * KP + arow + 32 * s);
         xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
-        if (!qok) zero(aq);
         if (s & 1) {
           x1 = mma32(ak, bs, x1);
-          z1 = mma32(aq, bs, z1);
+          z1 = mma32(P.aq[s], bs, z1);
         } else {
           x = mma32(ak, bs, x);
-          z = mma32(aq, bs, z);
+          z = mma32(P.aq[s], bs, z);
         }
       }
       x = x + x1;
@@ -667,18 +717,17 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * r + 4 * grp + e;
-        float vv;
-        if constexpr (BF) vv = bf2f(P.vr[e]);
-        else vv = P.vr[e];
-        y[e] = tok < nc ? sSc[tok] * vv - sSc[C + tok] * x[e] : 0.f;
+        const float b = sSc[tok], bg = sSc[C + tok];
+        y[e] = tok < nc ? b * io_val(P.vr[e]) - bg * x[e] : 0.f;
       }
       xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
     }
+    fetchB(Pn, cn);
     lds_barrier();
 
     // (c) Ud = T' Y for block row r (Y fragments kept for O); K^T fragments for (d)
     Sp yb[NTF];
-    if (wave < NB) {
+    if (rowblk) {
       const int r = wave;
       f4 uh = zero4(), ul = zero4();
 #pragma unroll
@@ -696,9 +745,18 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
       const int b = wave + 4 * bi;
       if (b < KB) {
 #pragma unroll
-        for (int s = 0; s < NTS; ++s) ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
+        for (int s = 0; s < NTS; ++s) {
+          if constexpr (BF) {
+            const uint2 lo = lds_tr16(sK + 32 * s * KP + trow + 16 * b);
+            const uint2 hi = lds_tr16(sK + 32 * s * KP + 4 * KP + trow + 16 * b);
+            kt[bi][s] = uint4{lo.x, lo.y, hi.x, hi.y};
+          } else {
+            ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
+          }
+        }
       }
     }
+    fetchC(Pn, cn);
     lds_barrier();
 
     // (d) S^T <- gamma_last S^T + K^T Ud for the owned state blocks (the
@@ -719,7 +777,7 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
         xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
       }
     }
-    if (wave < NB) {
+    if (rowblk) {
       const int r = wave;
       f4 oh, ol = zero4();
 #pragma unroll
@@ -729,25 +787,26 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
         if (2 * s <= r) mm_ss(P.rf[s], yb[s], oh, ol);
       o_prev = oh + ol;
     }
-    o_t0 = t0;
-    o_nc = nc;
-    if (more) commit(Pn, cc + 1, buf ^ 1);
+    o_cc = cc;
+    commit(Pn, buf ^ 1);
     lds_barrier();
   };
 
   Pre PA, PB;
   if (nchunk > 0) {
-    fetch(PA, 0);
+    fetchA(PA, 0);
+    fetchB(PA, 0);
+    fetchC(PA, 0);
     vm_wait<0>();
-    commit(PA, 0, 0);
+    commit(PA, 0);
   }
   lds_barrier();
-  for (int cc = 0; cc < nchunk; cc += 2) {
+  for (int cc = 0; cc + 1 < nchunk; cc += 2) {
     step(cc, PA, PB);
-    if (cc + 1 < nchunk) step(cc + 1, PB, PA);
+    step(cc + 1, PB, PA);
   }
-  vm_wait<0>();
-  if (nchunk > 0) store_o();
+  if (nchunk & 1) step(nchunk - 1, PA, PB);
+  store_o();
 
 #pragma unroll
   for (int bi = 0; bi < SB; ++bi) {

@@ -23,18 +23,24 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// fp32 -> bf16 with round to nearest even (NaN stays NaN), by the
+// hardware conversion v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {  // a in the low half
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{a, b}, bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // Split x into hi + lo, both bf16: hi = rne(x), lo = rne(x - hi).  |x - hi - lo| <= 2^-17 |x|.
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   hi = f2bf(x);
   lo = f2bf(x - bf2f(hi));
+}
+// The same for a pair: hi and lo packed two to a word, a in the low halves.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // ---------------------------------------------------------------- DPP lane reductions
@@ -148,15 +154,10 @@ __device__ __forceinline__ f4 mma32(const f8& a, const f8& b, f4 c) {
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return uint32_t(lo) | (uint32_t(hi) << 16); }
 
 // Round 4 fp32 to bf16 (8 bytes) and, optionally, the rounding residues (8 bytes).
-__device__ __forceinline__ uint2 bf16x4(f4 x) {
-  return uint2{pack2(f2bf(x[0]), f2bf(x[1])), pack2(f2bf(x[2]), f2bf(x[3]))};
-}
+__device__ __forceinline__ uint2 bf16x4(f4 x) { return uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}; }
 __device__ __forceinline__ void split_bf16x4(f4 x, uint2& hi, uint2& lo) {
-  uint16_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) split_bf16(x[i], h[i], l[i]);
-  hi = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-  lo = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+  split_bf16x2(x[0], x[1], hi.x, lo.x);
+  split_bf16x2(x[2], x[3], hi.y, lo.y);
 }
 __device__ __forceinline__ void split_bf16x8(const f8& x, uint4& hi, uint4& lo) {
   uint2 h0, l0, h1, l1;
