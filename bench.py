@@ -20,6 +20,12 @@ same JSON line also carries:
               library records on the launch stream while profiling is on;
   cpu_baseline  the fp64 oracle timed on this host on a prefix of the same
               prompt.
+  traffic     HBM bytes per launch of that kernel as the FETCH_SIZE and
+              WRITE_SIZE counters saw them (profiles/, scaled by the same
+              counters on a copy of known size), or null once the kernel
+              source differs from the one the counters were taken on.
+--prefill-only runs just the headline calls and one 512 MiB device copy (the
+counter calibration), for counter runs under rocprofv3.
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 
@@ -37,6 +43,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s
 
 T, HQK, HV, DK, DV, CHUNK = 4096, 16, 32, 128, 128, 64
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_sweep_T4096_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_deltanet_linear_delta_amd", "csrc", "gdn_chunked.hip")
 
 
 def log(msg):
@@ -74,6 +83,25 @@ def decode_bytes(b):
     return b * (2 * HV * DV * DK * 4 + 2 * HQK * DK * 2 + 2 * HV * DV * 2 + 2 * HV * 4)
 
 
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the sweep kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            fields = dict(line.strip("- \n").split(": ", 1) for line in fh if line.startswith("- ") and ": " in line)
+        if fields.get("source_sha256") != source_digest(KERNEL_SOURCE):
+            return None
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -100,6 +128,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no multi-GPU path "
@@ -158,6 +187,17 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     flops = prefill_flops(T)
     mfma_util = flops / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+
+    if args.prefill_only:
+        # counter calibration: one device copy of exactly 512 MiB each way
+        src = torch.ones(1 << 28, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 536870912 bytes read, 536870912 written")
+        print(json.dumps({"prefill_only": True, "ms_per_step": round(ms_step, 5),
+                          "kernels_us": {n: round(m * 1e3, 2) for n, (m, _) in per_kernel.items()}}), flush=True)
+        return
 
     # ------------------------------------------------------------ decode
     def decode_leg(B, n_sets, steps_per_graph, seed):
@@ -277,7 +317,7 @@ def main():
         "algorithmic_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {n: round(m * 1e3, 2) for n, (m, _) in per_kernel.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
         "decode": {"b1_warm": dec_b1, "b32_cold": dec_b32},
         "scan": scan,
