@@ -183,10 +183,16 @@ struct Geom {
 };
 // first fragment of row block r: sum over r' < r of (r' / 2 + 1)
 __device__ __forceinline__ constexpr int frag_base(int r) { return r == 0 ? 0 : (r == 1 ? 1 : (r == 2 ? 2 : 4)); }
+// row of the p-th block of a lower-triangular block matrix (blocks (r, i), i <= r, row-major)
+__device__ __forceinline__ constexpr int tri_row(int p) { return p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)); }
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS (and scalar)
 // traffic only, so global loads and stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// exp(x) by the hardware base-2 exponential; relative error about |x| 2^-24
+// from rounding x log2(e), far inside what the decays need.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -199,17 +205,20 @@ constexpr int frag_row_stride(int row_bytes) { return (row_bytes + 95) / 128 * 1
 template <typename IO, int DK, int C>
 struct PrepLds {
   static constexpr int E16 = 16 / sizeof(IO);
+  static constexpr int NB = C / 16;
   static constexpr int CP = C < 32 ? 32 : C;     // token rows, padded to a 32 slab
   static constexpr int DKP = DK < 32 ? 32 : DK;  // key columns, padded to a 32 slab
-  static constexpr int KP = frag_row_stride(DKP * int(sizeof(IO))) / int(sizeof(IO));  // row stride, elements
+  static constexpr int KP = DKP + E16;           // row stride, elements (16-byte pad)
   static constexpr int AP = C + 4;               // fp32 row stride of A, QKm, T, R
   static constexpr size_t KQ_BYTES = 2 * size_t(CP) * KP * sizeof(IO);
   static constexpr size_t M_BYTES = size_t(C) * AP * sizeof(float);
-  static constexpr size_t R0 = KQ_BYTES > M_BYTES ? KQ_BYTES : M_BYTES;  // K, Q; later T
-  static constexpr size_t A_OFF = R0;                                    // A; later R
-  static constexpr size_t QK_OFF = A_OFF + M_BYTES;
-  static constexpr size_t G_OFF = QK_OFF + M_BYTES;  // fp64 prefix sums
-  static constexpr size_t B_OFF = G_OFF + C * sizeof(double);
+  // K and Q tiles until the Gram products are in registers; then A (later R) and QKm
+  static constexpr size_t U_BYTES = KQ_BYTES > 2 * M_BYTES ? KQ_BYTES : 2 * M_BYTES;
+  static constexpr size_t A_OFF = 0, QK_OFF = M_BYTES;
+  static constexpr size_t T_OFF = U_BYTES;
+  static constexpr size_t GB_OFF = T_OFF + M_BYTES;   // fp64 prefix sum before each 16-token block
+  static constexpr size_t GL_OFF = GB_OFF + 8 * 4;    // fp32 prefix sum within the token's block
+  static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);
   static constexpr size_t D_OFF = B_OFF + C * sizeof(float);
   static constexpr size_t BYTES = D_OFF + C * sizeof(float);
 };
@@ -329,14 +338,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, AP = Lds::AP;
   constexpr int NKS = Lds::DKP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
+  constexpr int NGR = (2 * NBLK + 3) / 4;  // Gram blocks per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
-  float* sT = reinterpret_cast<float*>(smem);  // reuses the K/Q region after the Gram products
-  float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);
-  float* sR = sA;                              // reuses A after the inverse
+  float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);   // after the Gram products
+  float* sR = sA;                                            // after the inverse
   float* sQK = reinterpret_cast<float*>(smem + Lds::QK_OFF);
-  double* sG = reinterpret_cast<double*>(smem + Lds::G_OFF);
+  float* sT = reinterpret_cast<float*>(smem + Lds::T_OFF);
+  double* sGb = reinterpret_cast<double*>(smem + Lds::GB_OFF);
+  float* sGl = reinterpret_cast<float*>(smem + Lds::GL_OFF);
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
   float* sDec = reinterpret_cast<float*>(smem + Lds::D_OFF);
 
@@ -362,6 +373,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
     *reinterpret_cast<uint4*>(sK + r * KP + c16) = kv;
     *reinterpret_cast<uint4*>(sQ + r * KP + c16) = qv;
   }
+  // Gate prefix sums in fp64: G_t = sum_{i<=t} g_i.  Kept as the sum before
+  // each 16-token block (fp64) plus the part within the block (fp32, small),
+  // so that every decay exp(G_r - G_i) is formed from a short fp32 argument.
   if (wave == 0) {
     double gl = 0.0;
     float bl = 0.f;
@@ -375,10 +389,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
       if (lane >= off) gl += y;
     }
     const double glast = __shfl(gl, nc - 1);
+    const double gbase = __shfl(gl, max((lane & ~15) - 1, 0));  // sum before the token's block
+    const double gb = lane >= 16 ? gbase : 0.0;
     if (lane < C) {
-      const float gam = lane < nc ? float(exp(gl)) : 0.f;
-      const float dec = lane < nc ? float(exp(glast - gl)) : 0.f;
-      sG[lane] = gl;
+      const float gam = lane < nc ? fast_exp(float(gl)) : 0.f;
+      const float dec = lane < nc ? fast_exp(float(glast - gl)) : 0.f;
+      if ((lane & 15) == 0) sGb[lane >> 4] = gb;
+      sGl[lane] = float(gl - gb);
       sBeta[lane] = bl;
       sDec[lane] = dec;
       float* sc = reinterpret_cast<float*>(wsb + Geo::SCAL_OFF);
@@ -390,37 +407,55 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // Gram blocks (r, i), i <= r:  p < NBLK: K K^T -> A (strictly lower, scaled);
-  // otherwise Q K^T -> QKm (lower, decayed).  Both kept in LDS as fp32 rows.
-  for (int p = wave; p < 2 * NBLK; p += 4) {
-    const bool isA = p < NBLK;
-    const int pb = isA ? p : p - NBLK;
-    int r = 0;
-    while ((r + 1) * (r + 2) / 2 <= pb) ++r;
-    const int i = pb - r * (r + 1) / 2;
-    const IO* asrc = (isA ? sK : sQ) + (16 * r + col) * KP + 8 * grp;
-    const IO* bsrc = sK + (16 * i + col) * KP + 8 * grp;
-    f4 acc0 = zero4(), acc1 = zero4();
+  // Gram blocks (r, i), i <= r, dealt round-robin to the waves: index p <
+  // NBLK is K K^T (-> A), the rest Q K^T (-> QKm).  Products stay in
+  // registers until every wave is done with the K and Q tiles.
+  f4 gram[NGR];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      E a, b;
-      ld8(a, asrc + 32 * s);
-      ld8(b, bsrc + 32 * s);
-      if (s & 1) acc1 = mma32(a, b, acc1);
-      else acc0 = mma32(a, b, acc0);
+  for (int n = 0; n < NGR; ++n) {
+    const int p = wave + 4 * n;
+    gram[n] = zero4();
+    if (p < 2 * NBLK) {
+      const bool isA = p < NBLK;
+      const int pb = isA ? p : p - NBLK;
+      const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
+      const IO* asrc = (isA ? sK : sQ) + (16 * r + col) * KP + 8 * grp;
+      const IO* bsrc = sK + (16 * i + col) * KP + 8 * grp;
+      f4 acc1 = zero4();
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        E a, b;
+        ld8(a, asrc + 32 * s);
+        ld8(b, bsrc + 32 * s);
+        if (s & 1) acc1 = mma32(a, b, acc1);
+        else gram[n] = mma32(a, b, gram[n]);
+      }
+      gram[n] = gram[n] + acc1;
     }
-    const f4 acc = acc0 + acc1;
+  }
+  lds_barrier();  // K and Q are dead; their space becomes A and QKm
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
-      if (isA) {
-        sA[row * AP + cl] = cl < row ? sBeta[row] * expf(float(sG[row] - sG[cl])) * acc[e] : 0.f;
-      } else {
-        sQK[row * AP + cl] = cl <= row ? expf(float(sG[row] - sG[cl])) * acc[e] : 0.f;
+  for (int n = 0; n < NGR; ++n) {
+    const int p = wave + 4 * n;
+    if (p < 2 * NBLK) {
+      const bool isA = p < NBLK;
+      const int pb = isA ? p : p - NBLK;
+      const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
+      const float dblk = float(sGb[r] - sGb[i]);
+      const f4 glr = *reinterpret_cast<const f4*>(sGl + 16 * r + 4 * grp);
+      const f4 btr = *reinterpret_cast<const f4*>(sBeta + 16 * r + 4 * grp);
+      const float glc = sGl[16 * i + col];
+      float* dst = isA ? sA : sQK;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
+        const float dcy = fast_exp(cl <= row ? dblk + glr[e] - glc : 0.f);
+        const float v = isA ? (cl < row ? btr[e] * dcy * gram[n][e] : 0.f) : (cl <= row ? dcy * gram[n][e] : 0.f);
+        dst[row * AP + cl] = v;
       }
     }
   }
-  lds_barrier();  // A and QKm complete; K and Q are dead, their space becomes T
+  lds_barrier();
 
   // Diagonal blocks: T_bb = (I + A_bb)^{-1}.  Lane 4c+s owns column c and the
   // rows congruent to s mod 4; each row is one quad reduction.
