@@ -72,8 +72,8 @@ def kernel_bytes(name, t, n_seqs, state_in):
         return qk + 2 * vo + st * (2 if state_in else 1)
     if name == "chunk_prep":
         return qk + gb
-    if name == "chunk_offsets":
-        return 4 * (n_seqs + 1) * 2
+    if name == "chunk_table":
+        return 4 * (n_seqs + 1)
     if name == "scan":
         return qk + 2 * vo + gb + st * (2 if state_in else 1)
     raise KeyError(name)

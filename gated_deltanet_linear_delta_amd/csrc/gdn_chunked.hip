@@ -20,9 +20,15 @@
 // always formed as exp of a non-positive difference of fp64 partial sums, so
 // nothing overflows and nothing but true decay underflows.
 //
-// Three launches:
-//   1. chunk_offsets_kernel: chunk_off[n] = chunks before sequence n, and a
-//      per-chunk table (first token, length).
+// Workspace slots: chunk j of sequence n uses slot (bos_n + n (C - 1)) / C + j
+// (bos_n = its first token).  Consecutive sequences get disjoint slot ranges
+// and every slot is below (T + N (C - 1)) / C, so no prefix sum over
+// sequences is needed to place a chunk.
+//
+// Launches:
+//   1. chunk_table_kernel (only for more than one sequence): per slot, the
+//      chunk's (first token, length), or (0, 0) for an unused slot.  With one
+//      sequence slot j is simply tokens [j C, min(T, j C + C)).
 //   2. chunk_prep_kernel, one workgroup per (chunk, value head), fully
 //      parallel: Gram products on MFMA, gate prefix sums, A, T = (I + A)^{-1}
 //      (16x16 diagonal blocks by forward substitution in registers,
@@ -288,48 +294,30 @@ __device__ __forceinline__ void ld_split(f8& d, const uint8_t* p, int plane) {
 
 }  // namespace
 
-// chunk_off[n] = number of C-token chunks in sequences 0..n-1, chunk_off[N] =
-// total; tab[gc] = (first token, length) of chunk gc for gc < total and
-// (0, 0) for total <= gc < max_chunks.
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(int N, int T, int C, int max_chunks,
-                                                            const int32_t* __restrict__ cu,
-                                                            int32_t* __restrict__ chunk_off,
-                                                            int2* __restrict__ tab) {
-  __shared__ int part[256];
-  const int tid = threadIdx.x;
-  const int per = (N + 255) / 256;
-  const int lo = min(N, tid * per), hi = min(N, lo + per);
-  int sum = 0;
-  for (int n = lo; n < hi; ++n) {
+// Slot table: tab[slot] = (first token, length) of the chunk in that slot,
+// (0, 0) for slots no chunk uses.  Thread n % 256 fills the slots from
+// sequence n's first slot up to the next sequence's first slot.
+__device__ __forceinline__ int first_slot(int bos, int n, int C) { return (bos + n * (C - 1)) / C; }
+
+__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int C, int max_chunks,
+                                                          const int32_t* __restrict__ cu, int2* __restrict__ tab) {
+  for (int n = threadIdx.x; n < N; n += 256) {
     int b, e;
     seq_range(cu, n, T, b, e);
-    sum += (e - b + C - 1) / C;
+    const int s0 = first_slot(b, n, C);
+    const int s1 = min(first_slot(e, n + 1, C), max_chunks);
+    int t = b;
+    for (int sl = max(s0, 0); sl < s1; ++sl, t += C) tab[sl] = t < e ? make_int2(t, min(C, e - t)) : make_int2(0, 0);
   }
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int x = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += x;
-    __syncthreads();
-  }
-  int run = part[tid] - sum;
-  for (int n = lo; n < hi; ++n) {
-    chunk_off[n] = run;
-    int b, e;
-    seq_range(cu, n, T, b, e);
-    for (int t = b; t < e; t += C, ++run)
-      if (run < max_chunks) tab[run] = make_int2(t, min(C, e - t));
-  }
-  const int total = part[255];
-  if (tid == 255) chunk_off[N] = total;
-  for (int gc = total + tid; gc < max_chunks; gc += 256) tab[gc] = make_int2(0, 0);
+  int bN, eN;
+  seq_range(cu, N - 1, T, bN, eN);
+  for (int sl = max(first_slot(eN, N, C), 0) + int(threadIdx.x); sl < max_chunks; sl += 256) tab[sl] = make_int2(0, 0);
 }
 
 template <typename IO, int DK, int C>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
                                                          const IO* __restrict__ k, const float* __restrict__ g,
-                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ beta, int num_seqs, int T,
                                                          const int2* __restrict__ tab, uint8_t* __restrict__ ws) {
   constexpr bool BF = sizeof(IO) == 2;
   using Geo = Geom<BF, C>;
@@ -352,7 +340,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   float* sDec = reinterpret_cast<float*>(smem + Lds::D_OFF);
 
   const int gc = blockIdx.x, h = blockIdx.y;
-  const int2 ch = tab[gc];
+  const int2 ch = num_seqs == 1 ? make_int2(gc * C, min(C, T - gc * C)) : tab[gc];
   const int t0 = ch.x, nc = ch.y;
   if (nc <= 0) return;
   const int j = h / (h_v / h_qk);
@@ -563,7 +551,6 @@ template <typename IO, int DK, int C>
 __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
                                                           const IO* __restrict__ q, const IO* __restrict__ k,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
-                                                          const int32_t* __restrict__ chunk_off,
                                                           const uint8_t* __restrict__ ws, const float* s_in,
                                                           IO* __restrict__ out, float* s_out) {
   constexpr bool BF = sizeof(IO) == 2;
@@ -614,7 +601,7 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   int bos, eos;
   seq_range(cu, n, T, bos, eos);
   int nchunk = (eos - bos + C - 1) / C;
-  const int gc0 = chunk_off[n];
+  const int gc0 = first_slot(bos, n, C);
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
 
   constexpr int ESZ = int(sizeof(IO));
@@ -875,13 +862,12 @@ static size_t chunk_bytes(bool bf16, int chunk) {
 }
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-static size_t offsets_bytes(const Dims& d) { return round256(size_t(d.num_seqs + 1) * 4); }
 static size_t table_bytes(const Dims& d, int chunk) { return round256(chunked_max_chunks(d, chunk) * 8); }
 
 size_t chunked_workspace_bytes(const Dims& d, int chunk) {
   const size_t cb = chunk_bytes(d.bf16, chunk);
   if (cb == 0) return 0;
-  return offsets_bytes(d) + table_bytes(d, chunk) + chunked_max_chunks(d, chunk) * size_t(d.h_v) * cb;
+  return table_bytes(d, chunk) + chunked_max_chunks(d, chunk) * size_t(d.h_v) * cb;
 }
 
 template <typename IO, int DK, int C>
@@ -889,17 +875,17 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
                                    const float* beta, const int32_t* cu, const float* s_in, void* out,
                                    float* s_out, void* workspace, hipStream_t st) {
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  int32_t* chunk_off = reinterpret_cast<int32_t*>(base);
-  int2* tab = reinterpret_cast<int2*>(base + offsets_bytes(d));
-  uint8_t* ws = base + offsets_bytes(d) + table_bytes(d, C);
+  int2* tab = reinterpret_cast<int2*>(base);
+  uint8_t* ws = base + table_bytes(d, C);
   const size_t max_chunks = chunked_max_chunks(d, C);
-  {
-    Prof prof("chunk_offsets", st);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C,
-                       int(max_chunks), cu, chunk_off, tab);
+  hipError_t e = hipSuccess;
+  if (d.num_seqs > 1) {
+    Prof prof("chunk_table", st);
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, st, d.num_seqs, d.total_tokens, C,
+                       int(max_chunks), cu, tab);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (max_chunks > 0) {
     constexpr size_t lds = PrepLds<IO, DK, C>::BYTES;
     if (lds > 65536) {
@@ -909,7 +895,8 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
     }
     Prof prof("chunk_prep", st);
     hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(256), lds,
-                       st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, tab, ws);
+                       st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, d.num_seqs,
+                       d.total_tokens, tab, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -925,7 +912,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   Prof prof("chunk_sweep", st);
   hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(256), lds, st, d.num_seqs,
                      d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(q),
-                     static_cast<const IO*>(k), static_cast<const IO*>(v), cu, chunk_off, ws, s_in,
+                     static_cast<const IO*>(k), static_cast<const IO*>(v), cu, ws, s_in,
                      static_cast<IO*>(out), s_out);
   return hipGetLastError();
 }

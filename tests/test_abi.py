@@ -47,8 +47,8 @@ def shape(**kw):
 
 
 def expected_workspace(n, t, h_v, c, bf16=True):
-    """Chunk offsets (N+1 int32) and the per-chunk (first token, length)
-    table, each padded to 256 bytes, then per (chunk, value head): the
+    """The per-slot (first token, length) table, padded to 256 bytes, then
+    per (slot, value head), for (T + N (C - 1)) / C slots: the
     16-row x 32-column fragments of the lower triangles of T' and R (1, 2 or
     6 per matrix for C = 16, 32, 64), each one 1 KiB plane per 8 values per
     lane (T' rounded once to bf16: 1 plane; R split, or fp32: 2 planes), and
@@ -57,13 +57,13 @@ def expected_workspace(n, t, h_v, c, bf16=True):
     max_chunks = (t + n * (c - 1)) // c
     nf = {16: 1, 32: 2, 64: 6}[c]
     per = nf * (1 if bf16 else 2) * 1024 + nf * 2 * 1024 + 4 * c * 4
-    return r256(4 * (n + 1)) + r256(8 * max_chunks) + max_chunks * h_v * per
+    return r256(8 * max_chunks) + max_chunks * h_v * per
 
 
 def test_workspace_size(lib):
     s = shape()
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64) == expected_workspace(1, 4096, 32, 64)
-    assert expected_workspace(1, 4096, 32, 64) == 256 + 512 + 64 * 32 * 19456
+    assert expected_workspace(1, 4096, 32, 64) == 512 + 64 * 32 * 19456
     s32 = shape(io_dtype=gdn.GDN_DTYPE_F32)
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s32), 64) == expected_workspace(1, 4096, 32, 64, False)
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 48) == 0
