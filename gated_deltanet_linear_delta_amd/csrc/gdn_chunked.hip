@@ -121,15 +121,20 @@ __device__ __forceinline__ void ld8col(f8& d, const float* p, int stride) {
   d.b = f4{p[4 * stride], p[5 * stride], p[6 * stride], p[7 * stride]};
 }
 
+// Row stride (bytes) of an LDS tile read by 16-byte fragment rows (lane
+// col of each 16-lane group reads row col): strides of 32 mod 128 bytes keep
+// those ds_read_b128 free of bank conflicts on gfx950 (measured: 288 B rows
+// run at about 205 B/clk per CU, 272 B rows at 128).
+constexpr int frag_row_stride(int row_bytes) { return (row_bytes + 95) / 128 * 128 + 32; }
+
 // Exchange buffers: [16 rows][K + pad] arrays with K contiguous, written from
 // D blocks (4 consecutive k per lane) and read as B fragments (8 consecutive
 // k per lane).  bf16 buffers hold either the rounded value (single) or the
 // hi and lo halves in two planes; fp32 buffers hold the value.
 template <bool BF, int K>
 struct XBuf {
-  static constexpr int PAD = BF ? 8 : 4;  // 16 bytes
-  static constexpr int LD = K + PAD;      // row stride, elements
   using El = std::conditional_t<BF, uint16_t, float>;
+  static constexpr int LD = frag_row_stride(K * int(sizeof(El))) / int(sizeof(El));  // row stride, elements
   static constexpr size_t PLANE = 16 * LD * sizeof(El);
 };
 
@@ -202,11 +207,6 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Row stride (bytes) of an LDS tile read by 16-byte fragment rows (lane
-// col of each 16-lane group reads row col): strides of 32 mod 128 bytes keep
-// those ds_read_b128 free of bank conflicts on gfx950 (measured: 288 B rows
-// run at about 205 B/clk per CU, 272 B rows at 128).
-constexpr int frag_row_stride(int row_bytes) { return (row_bytes + 95) / 128 * 128 + 32; }
 
 template <typename IO, int DK, int C>
 struct PrepLds {
@@ -238,12 +238,19 @@ struct SweepLds {
   static constexpr int DKP = DK < 32 ? 32 : DK;  // its columns
   static constexpr int KP = frag_row_stride(DKP * ESZ) / ESZ;  // row stride, elements
   static constexpr size_t KBUF = size_t(CP) * KP * ESZ;
-  static constexpr size_t K_OFF = 0;             // two K buffers
-  static constexpr size_t S_OFF = 2 * KBUF;      // state (B fragments of S^T)
+  static constexpr size_t VBUF = size_t(C) * 16 * ESZ;                       // V slice: C tokens x 16 values
+  static constexpr size_t TBUF = size_t(Geom<BF, C>::NF) * Geom<BF, C>::TPL * Geom<BF, C>::PLANE;  // T' fragments
+  static constexpr size_t SCBUF = 4 * C * sizeof(float);                     // beta, beta gamma, gamma, dec
+  // every staged input has two buffers (chunk parity)
+  static constexpr size_t K_OFF = 0;
+  static constexpr size_t V_OFF = K_OFF + 2 * KBUF;
+  static constexpr size_t T_OFF = V_OFF + 2 * VBUF;
+  static constexpr size_t SC_OFF = T_OFF + 2 * TBUF;
+  static constexpr size_t S_OFF = SC_OFF + 2 * SCBUF;  // state (B fragments of S^T)
   static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
   static constexpr size_t UD_OFF = Y_OFF + xb_bytes_split<BF, CP>();
-  static constexpr size_t SC_OFF = UD_OFF + xb_bytes_split<BF, CP>();  // two buffers of 4 C scalars
-  static constexpr size_t BYTES = SC_OFF + 2 * 4 * C * sizeof(float);
+  static constexpr size_t BYTES = UD_OFF + xb_bytes_split<BF, CP>();
+  static_assert(BYTES % 16 == 0, "zeroed in 16-byte pieces");
 };
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
 }
 
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
+__global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
                                                           const IO* __restrict__ q, const IO* __restrict__ k,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
                                                           const uint8_t* __restrict__ ws, const float* s_in,
@@ -559,12 +566,14 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   using E = typename Types<BF>::E;
   using Sp = typename Types<BF>::S;
   constexpr int NB = Geo::NB, KB = DK / 16, CP = Lds::CP, DKP = Lds::DKP, KP = Lds::KP, E16 = Lds::E16;
+  constexpr int ESZ = Lds::ESZ;
   constexpr int NKS = DKP / 32, NTS = CP / 32;  // 32-wide slabs along d_k and along the chunk
-  constexpr int SB = (KB + 3) / 4;              // state blocks per wave
+  constexpr int SB = (KB + 3) / 4;              // state blocks per chain wave
   constexpr int NTF = (NB + 1) / 2;             // T' / R fragments per row block, at most
   constexpr int PER_ROW = DK / E16;             // 16-byte pieces per K row
-  constexpr int NIT = (C * PER_ROW + 255) / 256;
-  constexpr int QL = BF ? 1 : 2;                // loads per operand fragment (16 or 32 bytes)
+  constexpr int NKP = (C * PER_ROW + 255) / 256;                                 // K pieces per helper lane
+  constexpr int NVP = int(Lds::VBUF / 16), NTP = int(Lds::TBUF / 16), NSP = int(Lds::SCBUF / 16);
+  constexpr int NVT = (NVP + NTP + NSP + 255) / 256;                             // other pieces per helper lane
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sS = smem + Lds::S_OFF;
   uint8_t* sY = smem + Lds::Y_OFF;
@@ -582,266 +591,308 @@ __global__ __launch_bounds__(256) void chunk_sweep_kernel(int N, int T, int h_qk
   const int dv0 = 16 * tl;
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = wave_id();
+  const int r = wave & 3;                    // row block (and state-block group) of this wave
+  const bool rowblk = NB >= 4 || r < NB;
 
-  // zero LDS once: K rows / columns past C or d_k, and exchange columns past
-  // C or d_k, are read as zeros
-  for (int x = tid; x < int(Lds::SC_OFF / 16); x += 256) reinterpret_cast<uint4*>(smem)[x] = uint4{0u, 0u, 0u, 0u};
-  lds_barrier();
-
-  f4 st[SB];
-#pragma unroll
-  for (int bi = 0; bi < SB; ++bi) {
-    const int b = wave + 4 * bi;
-    st[bi] = zero4();
-    if (b < KB) {
-      if (s_in) st[bi] = *reinterpret_cast<const f4*>(s_in + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp);
-      xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
-    }
-  }
   int bos, eos;
   seq_range(cu, n, T, bos, eos);
   int nchunk = (eos - bos + C - 1) / C;
   const int gc0 = first_slot(bos, n, C);
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
-
-  constexpr int ESZ = int(sizeof(IO));
   const int kstride = h_qk * DK;  // elements between consecutive tokens of q / k
   const int vstride = h_v * d_v;  // and of v
-
-  // Everything one chunk needs from global memory, fetched one chunk ahead
-  // in three parts spread over the step.  Token rows of q, k, v (and of the
-  // output) go through buffer resources whose range ends with the chunk's
-  // last token, so rows past it read as zeros and stores there are dropped.
-  // Every wave issues the same loads in the same order whatever its role (a
-  // lane whose value is not needed reads one shared 16-byte line instead),
-  // so the waits below can count them.
-  struct Pre {
-    uint4 kp[NIT];  // K rows, 16-byte pieces, for the LDS tile     (part A)
-    float sc;       // one of the 4 C per-token scalars, for LDS    (part A)
-    E tf[NTF];      // T' fragments of row block `wave`             (part B)
-    Sp rf[NTF];     // R fragments of row block `wave`              (part B)
-    E aq[NKS];      // Q rows of block `wave` as A fragments        (part C)
-    IO vr[4];       // V values of block `wave`                     (part C)
-  };
-  constexpr int NA = NIT + 1, NBL = NTF * (QL + 2), NCL = NKS * QL + 4;
-  (void)NBL;
-  (void)NCL;
-  const bool rowblk = NB >= 4 || wave < NB;
-
-  // per-lane byte offsets, relative to a chunk's first token row
-  uint32_t koff[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int x = tid + 256 * it;
-    koff[it] = x < C * PER_ROW ? uint32_t(((x / PER_ROW) * kstride + (x % PER_ROW) * E16) * ESZ) : 0x80000000u;
-  }
-  uint32_t qoff[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s)
-    qoff[s] = uint32_t(((16 * wave + col) * kstride + (32 * s + 8 * grp < DK ? 32 * s + 8 * grp : 0)) * ESZ);
-  uint32_t voff[4];  // also the output's
-#pragma unroll
-  for (int e = 0; e < 4; ++e) voff[e] = uint32_t(((16 * wave + 4 * grp + e) * vstride + col) * ESZ);
-  const uint32_t kq_tail = uint32_t(DK * ESZ), v_tail = uint32_t(16 * ESZ);
-
   auto chunk_t0 = [&](int cc) { return bos + cc * C; };
   auto chunk_nc = [&](int cc) { return min(C, eos - chunk_t0(cc)); };
-  auto fetchA = [&](Pre& P, int cc) {
-    const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-    const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) P.kp[it] = bload16(rk, koff[it]);
-    const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
-    P.sc = reinterpret_cast<const float*>(wsb + Geo::SCAL_OFF)[tid % (4 * C)];
-  };
-  auto fetchB = [&](Pre& P, int cc) {
-    const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
-    const int rb = rowblk ? wave : 0;
-    const uint8_t* tp = wsb + Geo::T_OFF + size_t(frag_base(rb)) * Geo::TPL * Geo::PLANE;
-    const uint8_t* rp = wsb + Geo::R_OFF + size_t(frag_base(rb)) * 2 * Geo::PLANE;
-#pragma unroll
-    for (int s = 0; s < NTF; ++s) {
-      const bool need = rowblk && 2 * s <= wave;
-      const uint8_t* t = tp + (need ? s * Geo::TPL * Geo::PLANE + lane * 16 : 0);
-      const uint8_t* r = rp + (need ? s * 2 * Geo::PLANE + lane * 16 : 0);
-      if constexpr (BF) {
-        P.tf[s] = *reinterpret_cast<const uint4*>(t);
-      } else {
-        P.tf[s].a = *reinterpret_cast<const f4*>(t);
-        P.tf[s].b = *reinterpret_cast<const f4*>(t + (need ? Geo::PLANE : 0));
-      }
-      ld_split(P.rf[s], r, need ? Geo::PLANE : 0);
-    }
-  };
-  auto fetchC = [&](Pre& P, int cc) {
-    const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-    const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) bload_op(P.aq[s], rq, qoff[s]);
-    const Rsrc rv = make_rsrc(v + (size_t(t0) * h_v + h) * d_v + dv0, uint32_t((nc - 1) * vstride * ESZ) + v_tail);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) P.vr[e] = bload_el<IO>(rv, voff[e]);
-  };
-  auto commit = [&](const Pre& P, int buf) {
-    IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int x = tid + 256 * it;
-      if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
-    }
-    if (tid < 4 * C) reinterpret_cast<float*>(smem + Lds::SC_OFF)[buf * 4 * C + tid] = P.sc;
-  };
 
-  // O of the previous chunk; stored at the start of the next step, after the
-  // next prefetch is under way
-  f4 o_prev = zero4();
-  int o_cc = -1;  // none yet: an empty range drops the stores
-  auto store_o = [&]() {
-    const int t0 = chunk_t0(max(o_cc, 0)), nc = chunk_nc(max(o_cc, 0));
-    const uint32_t bytes = o_cc < 0 ? 0u : uint32_t((nc - 1) * vstride * ESZ) + v_tail;
-    const Rsrc ro = make_rsrc(out + (size_t(t0) * h_v + h) * d_v + dv0, bytes);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bstore_el<IO>(ro, voff[e], o_prev[e]);
-  };
+  // zero LDS once: K rows / columns past C or d_k, and exchange columns past
+  // C or d_k, are read as zeros
+  for (int x = tid; x < int(Lds::BYTES / 16); x += 512) reinterpret_cast<uint4*>(smem)[x] = uint4{0u, 0u, 0u, 0u};
+  lds_barrier();
 
-  // per-lane LDS offsets (elements) within a K tile
-  const int arow = col * KP + 8 * grp;  // A fragment: row col of a 16-row block, columns 8 grp ..
-  const int tcol = 8 * grp * KP + col;  // K^T fragment: tokens 8 grp .., column col of a block
-  // the same fragment by two transpose reads: this lane addresses token
-  // 8 grp + col / 4 (+ 4), columns 4 (col % 4) .. + 3 of the block
-  const int trow = (8 * grp + col / 4) * KP + 4 * (col % 4);
-
-  auto step = [&](int cc, const Pre& P, Pre& Pn) {
-    const int buf = cc & 1;
-    const int nc = chunk_nc(cc);
-    const int cn = min(cc + 1, nchunk - 1);  // the last step refetches its own chunk, unused
-    const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
-    const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF) + buf * 4 * C;
-    fetchA(Pn, cn);
-    store_o();
-    vm_wait<NA + 4>();  // parts B and C of this chunk have landed
-
-    // (b) X = K S^T and Z = Q S^T for token block r = wave; Y = beta V - beta gamma X
-    // (X is on the chain from one state to the next; Z waits until Y is out)
-    f4 z = zero4(), x = zero4();
-    if (rowblk) {
-      const int r = wave;
-      f4 x1 = zero4(), z1 = zero4();
-      E bs[NKS];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        E ak;
-        ld8(ak, sK + 16 * r * KP + arow + 32 * s);
-        xb_read_single<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
-        if (s & 1) x1 = mma32(ak, bs[s], x1);
-        else x = mma32(ak, bs[s], x);
-      }
-      x = x + x1;
-      f4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * r + 4 * grp + e;
-        const float b = sSc[tok], bg = sSc[C + tok];
-        y[e] = tok < nc ? b * io_val(P.vr[e]) - bg * x[e] : 0.f;
-      }
-      xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        if (s & 1) z1 = mma32(P.aq[s], bs[s], z1);
-        else z = mma32(P.aq[s], bs[s], z);
-      }
-      z = z + z1;
-    }
-    fetchB(Pn, cn);
-    lds_barrier();
-
-    // (c) Ud = T' Y for block row r (Y fragments kept for O); K^T fragments for (d)
-    Sp yb[NTF];
-    if (rowblk) {
-      const int r = wave;
-      f4 uh = zero4(), ul = zero4();
-#pragma unroll
-      for (int s = 0; s < NTF; ++s) {
-        if (2 * s <= r) {
-          xb_read_split<BF, CP>(yb[s], sY, col, 32 * s + 8 * grp);
-          mm_es(P.tf[s], yb[s], uh, ul);
-        }
-      }
-      xb_write_split<BF, CP>(sUd, col, 16 * r + 4 * grp, uh + ul);
-    }
-    E kt[SB][NTS];
+  if (wave < 4) {
+    // ============================================================ chain waves
+    // The recurrence proper: per chunk X = K S^T, Y, T'Y and the state
+    // update, touching only LDS and the matrix cores.
+    f4 st[SB];
 #pragma unroll
     for (int bi = 0; bi < SB; ++bi) {
-      const int b = wave + 4 * bi;
+      const int b = r + 4 * bi;
+      st[bi] = zero4();
       if (b < KB) {
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-          if constexpr (BF) {
-            const uint2 lo = lds_tr16(sK + 32 * s * KP + trow + 16 * b);
-            const uint2 hi = lds_tr16(sK + 32 * s * KP + 4 * KP + trow + 16 * b);
-            kt[bi][s] = uint4{lo.x, lo.y, hi.x, hi.y};
-          } else {
-            ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
-          }
-        }
-      }
-    }
-    fetchC(Pn, cn);
-    lds_barrier();
-
-    // (d) S^T <- gamma_last S^T + K^T Ud for the owned state blocks (the
-    // chain's critical path), then O = gamma Z + R Y for block row r.
-    const float glast = sSc[2 * C + nc - 1];
-#pragma unroll
-    for (int bi = 0; bi < SB; ++bi) {
-      const int b = wave + 4 * bi;
-      if (b < KB) {
-        f4 ah = st[bi] * glast, al = zero4();
-#pragma unroll
-        for (int s = 0; s < NTS; ++s) {
-          Sp ub;
-          xb_read_split<BF, CP>(ub, sUd, col, 32 * s + 8 * grp);
-          mm_es(kt[bi][s], ub, ah, al);
-        }
-        st[bi] = ah + al;
+        if (s_in) st[bi] = *reinterpret_cast<const f4*>(s_in + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp);
         xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
       }
     }
-    if (rowblk) {
-      const int r = wave;
-      f4 oh, ol = zero4();
+    lds_barrier();  // chunk 0 staged, state written
+
+    const int arow = col * KP + 8 * grp;                       // A fragment rows of the K tile
+    const int tcol = 8 * grp * KP + col;                       // K^T fragment, element reads
+    const int trow = (8 * grp + col / 4) * KP + 4 * (col % 4);  // K^T fragment, transpose reads
+    for (int cc = 0; cc < nchunk; ++cc) {
+      const int buf = cc & 1, nc = chunk_nc(cc);
+      const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
+      const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF + buf * Lds::VBUF);
+      const uint8_t* sTp = smem + Lds::T_OFF + buf * Lds::TBUF;
+      const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
+
+      // (1) X = K S^T for token block r; Y = beta V - beta gamma X
+      if (rowblk) {
+        f4 x = zero4(), x1 = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) oh[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
+        for (int s = 0; s < NKS; ++s) {
+          E ak, bs;
+          ld8(ak, sK + 16 * r * KP + arow + 32 * s);
+          xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
+          if (s & 1) x1 = mma32(ak, bs, x1);
+          else x = mma32(ak, bs, x);
+        }
+        x = x + x1;
+        float vv[4];
+        if constexpr (BF) {
+          // rows 16 r + 4 grp .. + 3 of column col by one transpose read
+          const uint2 t = lds_tr16(sV + (16 * r + 4 * grp + col / 4) * 16 + 4 * (col % 4));
+          vv[0] = __uint_as_float(t.x << 16), vv[1] = __uint_as_float(t.x & 0xffff0000u);
+          vv[2] = __uint_as_float(t.y << 16), vv[3] = __uint_as_float(t.y & 0xffff0000u);
+        } else {
 #pragma unroll
-      for (int s = 0; s < NTF; ++s)
-        if (2 * s <= r) mm_ss(P.rf[s], yb[s], oh, ol);
-      o_prev = oh + ol;
+          for (int e = 0; e < 4; ++e) vv[e] = sV[(16 * r + 4 * grp + e) * 16 + col];
+        }
+        f4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = 16 * r + 4 * grp + e;
+          const float b = sSc[tok], bg = sSc[C + tok];
+          y[e] = tok < nc ? b * vv[e] - bg * x[e] : 0.f;
+        }
+        xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
+      }
+      lds_barrier();
+
+      // (2) Ud = T' Y for token block r; K^T fragments for (3)
+      if (rowblk) {
+        const uint8_t* tf = sTp + size_t(frag_base(r)) * Geo::TPL * Geo::PLANE + lane * 16;
+        f4 uh = zero4(), ul = zero4();
+#pragma unroll
+        for (int s = 0; s < NTF; ++s) {
+          if (2 * s <= r) {
+            Sp yb;
+            E tv;
+            xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
+            if constexpr (BF) {
+              tv = *reinterpret_cast<const uint4*>(tf + s * Geo::PLANE);
+            } else {
+              tv.a = *reinterpret_cast<const f4*>(tf + s * 2 * Geo::PLANE);
+              tv.b = *reinterpret_cast<const f4*>(tf + s * 2 * Geo::PLANE + Geo::PLANE);
+            }
+            mm_es(tv, yb, uh, ul);
+          }
+        }
+        xb_write_split<BF, CP>(sUd, col, 16 * r + 4 * grp, uh + ul);
+      }
+      E kt[SB][NTS];
+#pragma unroll
+      for (int bi = 0; bi < SB; ++bi) {
+        const int b = r + 4 * bi;
+        if (b < KB) {
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            if constexpr (BF) {
+              const uint2 lo = lds_tr16(sK + 32 * s * KP + trow + 16 * b);
+              const uint2 hi = lds_tr16(sK + 32 * s * KP + 4 * KP + trow + 16 * b);
+              kt[bi][s] = uint4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+              ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
+            }
+          }
+        }
+      }
+      lds_barrier();
+
+      // (3) S^T <- gamma_last S^T + K^T Ud for the owned state blocks
+      const float glast = sSc[2 * C + nc - 1];
+#pragma unroll
+      for (int bi = 0; bi < SB; ++bi) {
+        const int b = r + 4 * bi;
+        if (b < KB) {
+          f4 ah = st[bi] * glast, al = zero4();
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            Sp ub;
+            xb_read_split<BF, CP>(ub, sUd, col, 32 * s + 8 * grp);
+            mm_es(kt[bi][s], ub, ah, al);
+          }
+          st[bi] = ah + al;
+          xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
+        }
+      }
+      lds_barrier();
     }
-    o_cc = cc;
-    commit(Pn, buf ^ 1);
-    lds_barrier();
-  };
-
-  Pre PA, PB;
-  if (nchunk > 0) {
-    fetchA(PA, 0);
-    fetchB(PA, 0);
-    fetchC(PA, 0);
-    vm_wait<0>();
-    commit(PA, 0);
-  }
-  lds_barrier();
-  for (int cc = 0; cc + 1 < nchunk; cc += 2) {
-    step(cc, PA, PB);
-    step(cc + 1, PB, PA);
-  }
-  if (nchunk & 1) step(nchunk - 1, PA, PB);
-  store_o();
 
 #pragma unroll
-  for (int bi = 0; bi < SB; ++bi) {
-    const int b = wave + 4 * bi;
-    if (b < KB) *reinterpret_cast<f4*>(s_out + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp) = st[bi];
+    for (int bi = 0; bi < SB; ++bi) {
+      const int b = r + 4 * bi;
+      if (b < KB) *reinterpret_cast<f4*>(s_out + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp) = st[bi];
+    }
+  } else {
+    // ============================================================ helper waves
+    // Everything off the recurrence: fetch chunk c+1 while chunk c runs and
+    // stage it in the other LDS buffers, and compute and store the output
+    // O = gamma (Q S^T) + R Y of token block r.
+    const int ht = tid - 256;  // 0..255
+    // per-lane byte offsets relative to a chunk's first token row
+    uint32_t koff[NKP];
+#pragma unroll
+    for (int it = 0; it < NKP; ++it) {
+      const int x = ht + 256 * it;
+      koff[it] = x < C * PER_ROW ? uint32_t(((x / PER_ROW) * kstride + (x % PER_ROW) * E16) * ESZ) : 0x80000000u;
+    }
+    uint32_t qoff[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+      qoff[s] = uint32_t(((16 * r + col) * kstride + (32 * s + 8 * grp < DK ? 32 * s + 8 * grp : 0)) * ESZ);
+    uint32_t ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ooff[e] = uint32_t(((16 * r + 4 * grp + e) * vstride + col) * ESZ);
+    const uint32_t kq_tail = uint32_t(DK * ESZ), v_tail = uint32_t(16 * ESZ);
+
+    // Staged inputs (K tile, V slice, T' fragments, scalars) are fetched two
+    // chunks ahead into registers and written to LDS one chunk ahead, so the
+    // loads have a whole chunk to land; the Q and R fragments of the next
+    // chunk stay in registers.  Loads are spread over the three windows so
+    // that no window waits behind a full memory queue.
+    struct Staged {
+      uint4 kp[NKP];  // K rows, 16-byte pieces
+      uint4 vt[NVT];  // V slice, T' fragments and scalars, 16-byte pieces
+    };
+    struct Frags {
+      E aq[NKS];   // Q rows of block r (A fragments)
+      Sp rf[NTF];  // R fragments of block r
+    };
+    auto fetch_k = [&](Staged& P, int cc) {
+      const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
+      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
+#pragma unroll
+      for (int it = 0; it < NKP; ++it) P.kp[it] = bload16(rk, koff[it]);
+    };
+    auto fetch_vt = [&](Staged& P, int cc) {
+      // one plain load per piece, its address chosen per lane: V rows past
+      // the chunk's end are clamped to its last row (those tokens are masked
+      // where V is used)
+      const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
+      const IO* vb = v + (size_t(t0) * h_v + h) * d_v + dv0;
+      const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
+      constexpr int PPT = 16 / E16;  // pieces per token row of the V slice
+#pragma unroll
+      for (int it = 0; it < NVT; ++it) {
+        const int x = min(ht + 256 * it, NVP + NTP + NSP - 1);
+        const int tok = min(x / PPT, nc - 1);
+        const uint8_t* src = x < NVP ? reinterpret_cast<const uint8_t*>(vb + tok * vstride + (x % PPT) * E16)
+                           : x < NVP + NTP ? wsb + Geo::T_OFF + size_t(x - NVP) * 16
+                                           : wsb + Geo::SCAL_OFF + size_t(x - NVP - NTP) * 16;
+        P.vt[it] = *reinterpret_cast<const uint4*>(src);
+      }
+    };
+    auto fetch_frags = [&](Frags& F, int cc) {
+      // every helper wave issues the same loads (a lane whose fragment is not
+      // needed reads one shared line instead)
+      const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
+      const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) bload_op(F.aq[s], rq, qoff[s]);
+      const int rb = rowblk ? r : 0;
+      const uint8_t* rp = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES + Geo::R_OFF +
+                          size_t(frag_base(rb)) * 2 * Geo::PLANE;
+#pragma unroll
+      for (int s = 0; s < NTF; ++s) {
+        const bool need = rowblk && 2 * s <= r;
+        ld_split(F.rf[s], rp + (need ? s * 2 * Geo::PLANE + lane * 16 : 0), need ? Geo::PLANE : 0);
+      }
+    };
+    auto commit = [&](const Staged& P, int buf) {
+      IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
+#pragma unroll
+      for (int it = 0; it < NKP; ++it) {
+        const int x = ht + 256 * it;
+        if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
+      }
+#pragma unroll
+      for (int it = 0; it < NVT; ++it) {
+        const int x = ht + 256 * it;
+        uint8_t* dst = x < NVP ? smem + Lds::V_OFF + buf * Lds::VBUF + size_t(x) * 16
+                     : x < NVP + NTP ? smem + Lds::T_OFF + buf * Lds::TBUF + size_t(x - NVP) * 16
+                                     : smem + Lds::SC_OFF + buf * Lds::SCBUF + size_t(x - NVP - NTP) * 16;
+        if (x < NVP + NTP + NSP) *reinterpret_cast<uint4*>(dst) = P.vt[it];
+      }
+    };
+
+    // S_c = staged inputs of chunk c (in registers until committed), F = Q / R fragments
+    Staged SA, SB;
+    Frags F, Fn;
+    if (nchunk > 0) {
+      fetch_k(SA, 0);
+      fetch_vt(SA, 0);
+      fetch_frags(F, 0);
+      fetch_k(SB, min(1, nchunk - 1));
+      fetch_vt(SB, min(1, nchunk - 1));
+      commit(SA, 0);
+    }
+    lds_barrier();  // chunk 0 staged, state written
+
+    auto step = [&](int cc, Staged& next, Staged& after) {
+      // next = chunk cc+1 (loaded, not yet committed); after = free, receives chunk cc+2
+      const int buf = cc & 1, nc = chunk_nc(cc);
+      const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
+
+      // (1) Z = Q S^T of block r (S is the chunk's initial state); K of chunk cc+2
+      f4 z = zero4();
+      if (rowblk) {
+        f4 z1 = zero4();
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          E bs;
+          xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
+          if (s & 1) z1 = mma32(F.aq[s], bs, z1);
+          else z = mma32(F.aq[s], bs, z);
+        }
+        z = z + z1;
+      }
+      const int c2 = min(cc + 2, nchunk - 1), c1 = min(cc + 1, nchunk - 1);  // past the end: harmless refetch
+      fetch_k(after, c2);
+      lds_barrier();
+
+      // (2) O = gamma Z + R Y for block r, stored straight from the D layout;
+      // Q and R fragments of chunk cc+1
+      if (rowblk) {
+        f4 oh, ol = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oh[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
+#pragma unroll
+        for (int s = 0; s < NTF; ++s) {
+          if (2 * s <= r) {
+            Sp yb;
+            xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
+            mm_ss(F.rf[s], yb, oh, ol);
+          }
+        }
+        const f4 o = oh + ol;
+        const int t0 = chunk_t0(cc);
+        const Rsrc ro = make_rsrc(out + (size_t(t0) * h_v + h) * d_v + dv0, uint32_t((nc - 1) * vstride * ESZ) + v_tail);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bstore_el<IO>(ro, ooff[e], o[e]);
+      }
+      fetch_frags(Fn, c1);
+      lds_barrier();
+
+      // (3) V, T', scalars of chunk cc+2; stage chunk cc+1 in the other buffers
+      fetch_vt(after, c2);
+      commit(next, buf ^ 1);  // after the last chunk this fills buffers nobody reads
+      F = Fn;
+      lds_barrier();
+    };
+    for (int cc = 0; cc < nchunk; cc += 2) {
+      step(cc, SB, SA);
+      if (cc + 1 < nchunk) step(cc + 1, SA, SB);
+    }
   }
 }
 
@@ -910,7 +961,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
     if (e != hipSuccess) return e;
   }
   Prof prof("chunk_sweep", st);
-  hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(256), lds, st, d.num_seqs,
+  hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
                      d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(q),
                      static_cast<const IO*>(k), static_cast<const IO*>(v), cu, ws, s_in,
                      static_cast<IO*>(out), s_out);
