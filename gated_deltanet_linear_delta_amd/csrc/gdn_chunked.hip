@@ -241,11 +241,14 @@ struct SweepLds {
   static constexpr size_t VBUF = size_t(C) * 16 * ESZ;                       // V slice: C tokens x 16 values
   static constexpr size_t TBUF = size_t(Geom<BF, C>::NF) * Geom<BF, C>::TPL * Geom<BF, C>::PLANE;  // T' fragments
   static constexpr size_t SCBUF = 4 * C * sizeof(float);                     // beta, beta gamma, gamma, dec
-  // every staged input has two buffers (chunk parity)
+  // K, Q, V and T' have one buffer each: a chunk's copies are written after
+  // the last read of the previous chunk's (the second barrier of a step).
+  // The scalars are read until the end of a step and have two (chunk parity).
   static constexpr size_t K_OFF = 0;
-  static constexpr size_t V_OFF = K_OFF + 2 * KBUF;
-  static constexpr size_t T_OFF = V_OFF + 2 * VBUF;
-  static constexpr size_t SC_OFF = T_OFF + 2 * TBUF;
+  static constexpr size_t Q_OFF = K_OFF + KBUF;  // Q tile, same layout as K
+  static constexpr size_t V_OFF = Q_OFF + KBUF;
+  static constexpr size_t T_OFF = V_OFF + VBUF;
+  static constexpr size_t SC_OFF = T_OFF + TBUF;
   static constexpr size_t S_OFF = SC_OFF + 2 * SCBUF;  // state (B fragments of S^T)
   static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
   static constexpr size_t UD_OFF = Y_OFF + xb_bytes_split<BF, CP>();
@@ -630,9 +633,9 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     const int trow = (8 * grp + col / 4) * KP + 4 * (col % 4);  // K^T fragment, transpose reads
     for (int cc = 0; cc < nchunk; ++cc) {
       const int buf = cc & 1, nc = chunk_nc(cc);
-      const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
-      const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF + buf * Lds::VBUF);
-      const uint8_t* sTp = smem + Lds::T_OFF + buf * Lds::TBUF;
+      const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF);
+      const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF);
+      const uint8_t* sTp = smem + Lds::T_OFF;
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
 
       // (1) X = K S^T for token block r; Y = beta V - beta gamma X
@@ -746,10 +749,6 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       const int x = ht + 256 * it;
       koff[it] = x < C * PER_ROW ? uint32_t(((x / PER_ROW) * kstride + (x % PER_ROW) * E16) * ESZ) : 0x80000000u;
     }
-    uint32_t qoff[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-      qoff[s] = uint32_t(((16 * r + col) * kstride + (32 * s + 8 * grp < DK ? 32 * s + 8 * grp : 0)) * ESZ);
     uint32_t ooff[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) ooff[e] = uint32_t(((16 * r + 4 * grp + e) * vstride + col) * ESZ);
@@ -760,19 +759,26 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     // loads have a whole chunk to land; the Q and R fragments of the next
     // chunk stay in registers.  Loads are spread over the three windows so
     // that no window waits behind a full memory queue.
+    // Q goes through LDS like K: loading whole rows (4 rows of 256 bytes
+    // per instruction) runs about four times faster than loading the 16-row
+    // fragments directly, whose rows sit a power-of-two stride apart.
     struct Staged {
       uint4 kp[NKP];  // K rows, 16-byte pieces
+      uint4 qp[NKP];  // Q rows, 16-byte pieces
       uint4 vt[NVT];  // V slice, T' fragments and scalars, 16-byte pieces
     };
     struct Frags {
-      E aq[NKS];   // Q rows of block r (A fragments)
       Sp rf[NTF];  // R fragments of block r
     };
     auto fetch_k = [&](Staged& P, int cc) {
       const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
+      const uint32_t rows = uint32_t((nc - 1) * kstride * ESZ) + kq_tail;
+      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, rows);
+      const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, rows);
 #pragma unroll
       for (int it = 0; it < NKP; ++it) P.kp[it] = bload16(rk, koff[it]);
+#pragma unroll
+      for (int it = 0; it < NKP; ++it) P.qp[it] = bload16(rq, koff[it]);
     };
     auto fetch_vt = [&](Staged& P, int cc) {
       // one plain load per piece, its address chosen per lane: V rows past
@@ -795,10 +801,6 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     auto fetch_frags = [&](Frags& F, int cc) {
       // every helper wave issues the same loads (a lane whose fragment is not
       // needed reads one shared line instead)
-      const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-      const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) bload_op(F.aq[s], rq, qoff[s]);
       const int rb = rowblk ? r : 0;
       const uint8_t* rp = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES + Geo::R_OFF +
                           size_t(frag_base(rb)) * 2 * Geo::PLANE;
@@ -809,17 +811,21 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       }
     };
     auto commit = [&](const Staged& P, int buf) {
-      IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF + buf * Lds::KBUF);
+      IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF);
+      IO* sQ = reinterpret_cast<IO*>(smem + Lds::Q_OFF);
 #pragma unroll
       for (int it = 0; it < NKP; ++it) {
         const int x = ht + 256 * it;
-        if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
+        if (x < C * PER_ROW) {
+          *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
+          *reinterpret_cast<uint4*>(sQ + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.qp[it];
+        }
       }
 #pragma unroll
       for (int it = 0; it < NVT; ++it) {
         const int x = ht + 256 * it;
-        uint8_t* dst = x < NVP ? smem + Lds::V_OFF + buf * Lds::VBUF + size_t(x) * 16
-                     : x < NVP + NTP ? smem + Lds::T_OFF + buf * Lds::TBUF + size_t(x - NVP) * 16
+        uint8_t* dst = x < NVP ? smem + Lds::V_OFF + size_t(x) * 16
+                     : x < NVP + NTP ? smem + Lds::T_OFF + size_t(x - NVP) * 16
                                      : smem + Lds::SC_OFF + buf * Lds::SCBUF + size_t(x - NVP - NTP) * 16;
         if (x < NVP + NTP + NSP) *reinterpret_cast<uint4*>(dst) = P.vt[it];
       }
@@ -842,6 +848,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       // next = chunk cc+1 (loaded, not yet committed); after = free, receives chunk cc+2
       const int buf = cc & 1, nc = chunk_nc(cc);
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
+      const IO* sQ = reinterpret_cast<const IO*>(smem + Lds::Q_OFF);
 
       // (1) Z = Q S^T of block r (S is the chunk's initial state); K of chunk cc+2
       f4 z = zero4();
@@ -849,10 +856,11 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         f4 z1 = zero4();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          E bs;
+          E aq, bs;
+          ld8(aq, sQ + (16 * r + col) * KP + 8 * grp + 32 * s);
           xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
-          if (s & 1) z1 = mma32(F.aq[s], bs, z1);
-          else z = mma32(F.aq[s], bs, z);
+          if (s & 1) z1 = mma32(aq, bs, z1);
+          else z = mma32(aq, bs, z);
         }
         z = z + z1;
       }
