@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int C, i
 }
 
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
+__global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
                                                          const IO* __restrict__ k, const float* __restrict__ g,
                                                          const float* __restrict__ beta, int num_seqs, int T,
                                                          const int2* __restrict__ tab, uint8_t* __restrict__ ws) {
@@ -336,7 +336,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, AP = Lds::AP;
   constexpr int NKS = Lds::DKP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
-  constexpr int NGR = (2 * NBLK + 3) / 4;  // Gram blocks per wave
+  constexpr int NW = 8;                         // waves per workgroup
+  constexpr int NGR = (2 * NBLK + NW - 1) / NW;  // Gram blocks per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
 
   // K and Q rows of the chunk (rows >= nc and columns >= DK are zero)
   constexpr int PER_ROW = Lds::DKP / E16;
-  for (int x = tid; x < Lds::CP * PER_ROW; x += 256) {
+  for (int x = tid; x < Lds::CP * PER_ROW; x += 64 * NW) {
     const int r = x / PER_ROW, c16 = (x % PER_ROW) * E16;
     uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
     if (r < nc && c16 < DK) {
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   f4 gram[NGR];
 #pragma unroll
   for (int n = 0; n < NGR; ++n) {
-    const int p = wave + 4 * n;
+    const int p = wave + NW * n;
     gram[n] = zero4();
     if (p < 2 * NBLK) {
       const bool isA = p < NBLK;
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   lds_barrier();  // K and Q are dead; their space becomes A and QKm
 #pragma unroll
   for (int n = 0; n < NGR; ++n) {
-    const int p = wave + 4 * n;
+    const int p = wave + NW * n;
     if (p < 2 * NBLK) {
       const bool isA = p < NBLK;
       const int pb = isA ? p : p - NBLK;
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
 
   // R = QKm T, lower-triangular blocks R(r, i) = sum_{k=i}^{r} QKm(r, k) T(k, i), in fp32.
-  for (int p = wave; p < NBLK; p += 4) {
+  for (int p = wave; p < NBLK; p += NW) {
     int r = 0;
     while ((r + 1) * (r + 2) / 2 <= p) ++r;
     const int i = p - r * (r + 1) / 2;
@@ -517,7 +518,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int h_qk, int h_v, cons
 
   // Fragments (r, s), s <= r / 2, of T' = diag(dec) T and R, lower-triangular
   // (entries above the diagonal and beyond C are zero).
-  for (int p = wave; p < Geo::NF; p += 4) {
+  for (int p = wave; p < Geo::NF; p += NW) {
     int r = 0;
     while (r + 1 < NB && frag_base(r + 1) <= p) ++r;
     const int s = p - frag_base(r);
@@ -953,7 +954,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
       if (e != hipSuccess) return e;
     }
     Prof prof("chunk_prep", st);
-    hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(256), lds,
+    hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(512), lds,
                        st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, d.num_seqs,
                        d.total_tokens, tab, ws);
     e = hipGetLastError();
