@@ -336,8 +336,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, AP = Lds::AP;
   constexpr int NKS = Lds::DKP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
-  constexpr int NW = 8;                         // waves per workgroup
-  constexpr int NGR = (2 * NBLK + NW - 1) / NW;  // Gram blocks per wave
+  constexpr int NW = 8;                     // waves per workgroup
+  constexpr int NGP = (NBLK + NW - 1) / NW;  // Gram blocks per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
@@ -406,51 +406,55 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // Gram blocks (r, i), i <= r, dealt round-robin to the waves: index p <
-  // NBLK is K K^T (-> A), the rest Q K^T (-> QKm).  Products stay in
-  // registers until every wave is done with the K and Q tiles.
-  f4 gram[NGR];
+  // Gram blocks (r, i), i <= r, dealt round-robin to the waves: each wave
+  // computes K K^T (-> A) and Q K^T (-> QKm) of the same block, which share
+  // the decays.  Products stay in registers until every wave is done with
+  // the K and Q tiles.
+  f4 gk[NGP], gq[NGP];
 #pragma unroll
-  for (int n = 0; n < NGR; ++n) {
-    const int p = wave + NW * n;
-    gram[n] = zero4();
-    if (p < 2 * NBLK) {
-      const bool isA = p < NBLK;
-      const int pb = isA ? p : p - NBLK;
+  for (int n = 0; n < NGP; ++n) {
+    const int pb = wave + NW * n;
+    gk[n] = zero4(), gq[n] = zero4();
+    if (pb < NBLK) {
       const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
-      const IO* asrc = (isA ? sK : sQ) + (16 * r + col) * KP + 8 * grp;
+      const IO* ksrc = sK + (16 * r + col) * KP + 8 * grp;
+      const IO* qsrc = sQ + (16 * r + col) * KP + 8 * grp;
       const IO* bsrc = sK + (16 * i + col) * KP + 8 * grp;
-      f4 acc1 = zero4();
+      f4 k1 = zero4(), q1 = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        E a, b;
-        ld8(a, asrc + 32 * s);
+        E ak, aq, b;
+        ld8(ak, ksrc + 32 * s);
+        ld8(aq, qsrc + 32 * s);
         ld8(b, bsrc + 32 * s);
-        if (s & 1) acc1 = mma32(a, b, acc1);
-        else gram[n] = mma32(a, b, gram[n]);
+        if (s & 1) {
+          k1 = mma32(ak, b, k1);
+          q1 = mma32(aq, b, q1);
+        } else {
+          gk[n] = mma32(ak, b, gk[n]);
+          gq[n] = mma32(aq, b, gq[n]);
+        }
       }
-      gram[n] = gram[n] + acc1;
+      gk[n] = gk[n] + k1;
+      gq[n] = gq[n] + q1;
     }
   }
   lds_barrier();  // K and Q are dead; their space becomes A and QKm
 #pragma unroll
-  for (int n = 0; n < NGR; ++n) {
-    const int p = wave + NW * n;
-    if (p < 2 * NBLK) {
-      const bool isA = p < NBLK;
-      const int pb = isA ? p : p - NBLK;
+  for (int n = 0; n < NGP; ++n) {
+    const int pb = wave + NW * n;
+    if (pb < NBLK) {
       const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
       const float dblk = float(sGb[r] - sGb[i]);
       const f4 glr = *reinterpret_cast<const f4*>(sGl + 16 * r + 4 * grp);
       const f4 btr = *reinterpret_cast<const f4*>(sBeta + 16 * r + 4 * grp);
       const float glc = sGl[16 * i + col];
-      float* dst = isA ? sA : sQK;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
         const float dcy = fast_exp(cl <= row ? dblk + glr[e] - glc : 0.f);
-        const float v = isA ? (cl < row ? btr[e] * dcy * gram[n][e] : 0.f) : (cl <= row ? dcy * gram[n][e] : 0.f);
-        dst[row * AP + cl] = v;
+        sA[row * AP + cl] = cl < row ? btr[e] * dcy * gk[n][e] : 0.f;
+        sQK[row * AP + cl] = cl <= row ? dcy * gq[n][e] : 0.f;
       }
     }
   }
@@ -477,26 +481,42 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // Off-diagonal blocks, one block row at a time:
-  //   T(i, jj) = -T(i, i) * sum_{kk = jj}^{i-1} A(i, kk) T(kk, jj)
-  for (int i = 1; i < NB; ++i) {
-    if (wave < i) {
-      const int jj = wave;
-      f4 P = zero4();
-      for (int kk = jj; kk < i; ++kk) {
-        const f4 a = *reinterpret_cast<const f4*>(&sA[(16 * i + col) * AP + 16 * kk + 4 * grp]);
-        f4 bt;
+  // Off-diagonal blocks in two rounds, T being block lower triangular:
+  //   T(i, i-1) = -T(i, i) A(i, i-1) T(i-1, i-1)             (i odd)
+  // then, with the 32 x 32 halves T1 (blocks 0-1) and T2 (blocks 2-3),
+  //   X = -T2 A21 T1,  X(i, j) = -sum_{l=2}^{i} T(i, l) M(l, j),
+  //   M(l, j) = sum_{k=j}^{1} A(l, k) T(k, j),
+  // each X block by one wave with M in registers.
+  auto tcol = [&](int kk, int jj) {  // B operand: block (kk, jj) of T, rows 4 grp .., column col
+    f4 bt;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bt[e] = sT[(16 * kk + 4 * grp + e) * AP + 16 * jj + col];
-        P = mma_f32(a, bt, P);
-      }
-      const f4 tii = *reinterpret_cast<const f4*>(&sT[(16 * i + col) * AP + 16 * i + 4 * grp]);
-      const f4 Rr = mma_f32(tii, P, zero4());
+    for (int e = 0; e < 4; ++e) bt[e] = sT[(16 * kk + 4 * grp + e) * AP + 16 * jj + col];
+    return bt;
+  };
+  auto arow = [&](const float* m, int ii, int kk) {  // A operand: block (ii, kk), row col, columns 4 grp ..
+    return *reinterpret_cast<const f4*>(&m[(16 * ii + col) * AP + 16 * kk + 4 * grp]);
+  };
+  if (NB >= 2 && wave < NB / 2) {
+    const int i = 2 * wave + 1;
+    const f4 P = mma_f32(arow(sA, i, i - 1), tcol(i - 1, i - 1), zero4());
+    const f4 Rr = mma_f32(arow(sT, i, i), P, zero4());
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * jj + col] = -Rr[e];
-    }
-    lds_barrier();
+    for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * (i - 1) + col] = -Rr[e];
   }
+  lds_barrier();
+  if (NB == 4 && wave < 4) {
+    const int i = 2 + (wave >> 1), jj = wave & 1;
+    auto mlj = [&](int l) {
+      f4 m = mma_f32(arow(sA, l, 1), tcol(1, jj), zero4());
+      if (jj == 0) m = mma_f32(arow(sA, l, 0), tcol(0, 0), m);
+      return m;
+    };
+    f4 X = mma_f32(arow(sT, i, 2), mlj(2), zero4());
+    if (i == 3) X = mma_f32(arow(sT, 3, 3), mlj(3), X);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * jj + col] = -X[e];
+  }
+  if (NB == 4) lds_barrier();
 
   // R = QKm T, lower-triangular blocks R(r, i) = sum_{k=i}^{r} QKm(r, k) T(k, i), in fp32.
   for (int p = wave; p < NBLK; p += NW) {
