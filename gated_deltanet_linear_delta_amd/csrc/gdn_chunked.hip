@@ -215,14 +215,18 @@ struct PrepLds {
   static constexpr int CP = C < 32 ? 32 : C;     // token rows, padded to a 32 slab
   static constexpr int DKP = DK < 32 ? 32 : DK;  // key columns, padded to a 32 slab
   static constexpr int KP = DKP + E16;           // row stride, elements (16-byte pad)
-  static constexpr int AP = C + 4;               // fp32 row stride of A, QKm, T, R
+  // A, QKm, T and R are lower block triangular: only their NBLK nonzero
+  // 16 x 16 blocks are stored, block (r, i) at index r (r + 1) / 2 + i, rows
+  // BP floats apart (BP = 20 keeps fragment reads and D-layout writes free
+  // of bank conflicts).  All three share the K/Q tile space once the Gram
+  // products are in registers; R later reuses A.
+  static constexpr int NBLK = NB * (NB + 1) / 2;
+  static constexpr int BP = 20;
   static constexpr size_t KQ_BYTES = 2 * size_t(CP) * KP * sizeof(IO);
-  static constexpr size_t M_BYTES = size_t(C) * AP * sizeof(float);
-  // K and Q tiles until the Gram products are in registers; then A (later R) and QKm
-  static constexpr size_t U_BYTES = KQ_BYTES > 2 * M_BYTES ? KQ_BYTES : 2 * M_BYTES;
-  static constexpr size_t A_OFF = 0, QK_OFF = M_BYTES;
-  static constexpr size_t T_OFF = U_BYTES;
-  static constexpr size_t GB_OFF = T_OFF + M_BYTES;   // fp64 prefix sum before each 16-token block
+  static constexpr size_t M_BYTES = size_t(NBLK) * 16 * BP * sizeof(float);
+  static constexpr size_t U_BYTES = KQ_BYTES > 3 * M_BYTES ? KQ_BYTES : 3 * M_BYTES;
+  static constexpr size_t A_OFF = 0, QK_OFF = M_BYTES, T_OFF = 2 * M_BYTES;
+  static constexpr size_t GB_OFF = U_BYTES;           // fp64 prefix sum before each 16-token block
   static constexpr size_t GL_OFF = GB_OFF + 8 * 4;    // fp32 prefix sum within the token's block
   static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);
   static constexpr size_t D_OFF = B_OFF + C * sizeof(float);
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   using Geo = Geom<BF, C>;
   using Lds = PrepLds<IO, DK, C>;
   using E = typename Types<BF>::E;
-  constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, AP = Lds::AP;
+  constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, BP = Lds::BP;
   constexpr int NKS = Lds::DKP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int NW = 8;                     // waves per workgroup
@@ -357,6 +361,11 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   const int j = h / (h_v / h_qk);
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = wave_id();
+  // element (row, c), c <= row rounded to blocks, of a stored lower block-triangular matrix
+  auto lt = [&](float* m, int row, int c) {
+    const int rb = row >> 4, cb = c >> 4;
+    return m + (rb * (rb + 1) / 2 + cb) * 16 * BP + (row & 15) * BP + (c & 15);
+  };
   uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
 
   // K and Q rows of the chunk (rows >= nc and columns >= DK are zero)
@@ -453,8 +462,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
         const float dcy = fast_exp(cl <= row ? dblk + glr[e] - glc : 0.f);
-        sA[row * AP + cl] = cl < row ? btr[e] * dcy * gk[n][e] : 0.f;
-        sQK[row * AP + cl] = cl <= row ? dcy * gq[n][e] : 0.f;
+        *lt(sA, row, cl) = cl < row ? btr[e] * dcy * gk[n][e] : 0.f;
+        *lt(sQK, row, cl) = cl <= row ? dcy * gq[n][e] : 0.f;
       }
     }
   }
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[rr][m] = sA[(16 * b + rr) * AP + 16 * b + 4 * m + s];
+      for (int m = 0; m < 4; ++m) a[rr][m] = *lt(sA, 16 * b + rr, 16 * b + 4 * m + s);
     float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       if (s == (rr & 3)) t[rr >> 2] = val;
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) sT[(16 * b + 4 * m + s) * AP + 16 * b + c] = t[m];
+    for (int m = 0; m < 4; ++m) *lt(sT, 16 * b + 4 * m + s, 16 * b + c) = t[m];
   }
   lds_barrier();
 
@@ -490,18 +499,18 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   auto tcol = [&](int kk, int jj) {  // B operand: block (kk, jj) of T, rows 4 grp .., column col
     f4 bt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bt[e] = sT[(16 * kk + 4 * grp + e) * AP + 16 * jj + col];
+    for (int e = 0; e < 4; ++e) bt[e] = *lt(sT, 16 * kk + 4 * grp + e, 16 * jj + col);
     return bt;
   };
-  auto arow = [&](const float* m, int ii, int kk) {  // A operand: block (ii, kk), row col, columns 4 grp ..
-    return *reinterpret_cast<const f4*>(&m[(16 * ii + col) * AP + 16 * kk + 4 * grp]);
+  auto arow = [&](float* m, int ii, int kk) {  // A operand: block (ii, kk), row col, columns 4 grp ..
+    return *reinterpret_cast<const f4*>(lt(m, 16 * ii + col, 16 * kk + 4 * grp));
   };
   if (NB >= 2 && wave < NB / 2) {
     const int i = 2 * wave + 1;
     const f4 P = mma_f32(arow(sA, i, i - 1), tcol(i - 1, i - 1), zero4());
     const f4 Rr = mma_f32(arow(sT, i, i), P, zero4());
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * (i - 1) + col] = -Rr[e];
+    for (int e = 0; e < 4; ++e) *lt(sT, 16 * i + 4 * grp + e, 16 * (i - 1) + col) = -Rr[e];
   }
   lds_barrier();
   if (NB == 4 && wave < 4) {
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     f4 X = mma_f32(arow(sT, i, 2), mlj(2), zero4());
     if (i == 3) X = mma_f32(arow(sT, 3, 3), mlj(3), X);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * grp + e) * AP + 16 * jj + col] = -X[e];
+    for (int e = 0; e < 4; ++e) *lt(sT, 16 * i + 4 * grp + e, 16 * jj + col) = -X[e];
   }
   if (NB == 4) lds_barrier();
 
@@ -525,14 +534,10 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     const int i = p - r * (r + 1) / 2;
     f4 acc = zero4();
     for (int kk = i; kk <= r; ++kk) {
-      const f4 a = *reinterpret_cast<const f4*>(&sQK[(16 * r + col) * AP + 16 * kk + 4 * grp]);
-      f4 bt;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bt[e] = sT[(16 * kk + 4 * grp + e) * AP + 16 * i + col];
-      acc = mma_f32(a, bt, acc);
+      acc = mma_f32(arow(sQK, r, kk), tcol(kk, i), acc);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sR[(16 * r + 4 * grp + e) * AP + 16 * i + col] = acc[e];
+    for (int e = 0; e < 4; ++e) *lt(sR, 16 * r + 4 * grp + e, 16 * i + col) = acc[e];
   }
   lds_barrier();
 
@@ -545,11 +550,11 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     const int row = 16 * r + col, k0 = 32 * s + 8 * grp;
     f8 tv, rv;
     zero(tv), zero(rv);
-    if (k0 < C) {
-      tv.a = *reinterpret_cast<const f4*>(&sT[row * AP + k0]);
-      tv.b = *reinterpret_cast<const f4*>(&sT[row * AP + k0 + 4]);
-      rv.a = *reinterpret_cast<const f4*>(&sR[row * AP + k0]);
-      rv.b = *reinterpret_cast<const f4*>(&sR[row * AP + k0 + 4]);
+    if (k0 < C && (k0 >> 4) <= r) {  // blocks above the diagonal are zero and not stored
+      tv.a = *reinterpret_cast<const f4*>(lt(sT, row, k0));
+      tv.b = *reinterpret_cast<const f4*>(lt(sT, row, k0 + 4));
+      rv.a = *reinterpret_cast<const f4*>(lt(sR, row, k0));
+      rv.b = *reinterpret_cast<const f4*>(lt(sR, row, k0 + 4));
     }
     const float dr = sDec[row];
 #pragma unroll
