@@ -876,7 +876,8 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
       const IO* sQ = reinterpret_cast<const IO*>(smem + Lds::Q_OFF);
 
-      // (1) Z = Q S^T of block r (S is the chunk's initial state); K of chunk cc+2
+      // (1) Z = Q S^T of block r (S is the chunk's initial state); K, Q, V,
+      // T' and scalars of chunk cc+2
       f4 z = zero4();
       if (rowblk) {
         f4 z1 = zero4();
@@ -892,6 +893,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       }
       const int c2 = min(cc + 2, nchunk - 1), c1 = min(cc + 1, nchunk - 1);  // past the end: harmless refetch
       fetch_k(after, c2);
+      fetch_vt(after, c2);
       lds_barrier();
 
       // (2) O = gamma Z + R Y for block r, stored straight from the D layout;
@@ -917,8 +919,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       fetch_frags(Fn, c1);
       lds_barrier();
 
-      // (3) V, T', scalars of chunk cc+2; stage chunk cc+1 in the other buffers
-      fetch_vt(after, c2);
+      // (3) stage chunk cc+1 in the LDS buffers
       commit(next, buf ^ 1);  // after the last chunk this fills buffers nobody reads
       F = Fn;
       lds_barrier();
