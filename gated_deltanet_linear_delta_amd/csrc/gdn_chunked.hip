@@ -192,6 +192,14 @@ struct Geom {
   static constexpr size_t BYTES = SCAL_OFF + 4 * C * sizeof(float);
   static_assert(BYTES % 256 == 0, "keep per-chunk blocks 256-byte aligned");
 };
+// Q of one (chunk, query/key head) laid out as the sweep's A fragments: for
+// each 16-row block r and 32-column slab s, 64 lanes x 8 values (one 1 KiB
+// plane in bf16, two in fp32), so that the sweep loads them as contiguous
+// 1 KiB rows instead of 16 rows of 64 bytes a power-of-two stride apart.
+__host__ __device__ constexpr size_t qfrag_bytes(int dk, int c, bool bf) {
+  return size_t(c / 16) * size_t((dk < 32 ? 32 : dk) / 32) * (bf ? 1 : 2) * 1024;
+}
+
 // first fragment of row block r: sum over r' < r of (r' / 2 + 1)
 __device__ __forceinline__ constexpr int frag_base(int r) { return r == 0 ? 0 : (r == 1 ? 1 : (r == 2 ? 2 : 4)); }
 // row of the p-th block of a lower-triangular block matrix (blocks (r, i), i <= r, row-major)
@@ -249,8 +257,7 @@ struct SweepLds {
   // the last read of the previous chunk's (the second barrier of a step).
   // The scalars are read until the end of a step and have two (chunk parity).
   static constexpr size_t K_OFF = 0;
-  static constexpr size_t Q_OFF = K_OFF + KBUF;  // Q tile, same layout as K
-  static constexpr size_t V_OFF = Q_OFF + KBUF;
+  static constexpr size_t V_OFF = K_OFF + KBUF;
   static constexpr size_t T_OFF = V_OFF + VBUF;
   static constexpr size_t SC_OFF = T_OFF + TBUF;
   static constexpr size_t S_OFF = SC_OFF + 2 * SCBUF;  // state (B fragments of S^T)
@@ -332,7 +339,8 @@ template <typename IO, int DK, int C>
 __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
                                                          const IO* __restrict__ k, const float* __restrict__ g,
                                                          const float* __restrict__ beta, int num_seqs, int T,
-                                                         const int2* __restrict__ tab, uint8_t* __restrict__ ws) {
+                                                         const int2* __restrict__ tab, uint8_t* __restrict__ ws,
+                                                         uint8_t* __restrict__ qf) {
   constexpr bool BF = sizeof(IO) == 2;
   using Geo = Geom<BF, C>;
   using Lds = PrepLds<IO, DK, C>;
@@ -446,6 +454,21 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       }
       gk[n] = gk[n] + k1;
       gq[n] = gq[n] + q1;
+    }
+  }
+  // the first value head of each query/key group stores Q as fragments
+  if (h % (h_v / h_qk) == 0) {
+    constexpr int NQF = NB * NKS;
+    uint8_t* qb = qf + (size_t(gc) * h_qk + j) * qfrag_bytes(DK, C, BF);
+    for (int p = wave; p < NQF; p += NW) {
+      const int rq = p / NKS, sq = p % NKS;
+      const IO* src = sQ + (16 * rq + col) * KP + 32 * sq + 8 * grp;
+      if constexpr (BF) {
+        *reinterpret_cast<uint4*>(qb + size_t(p) * 1024 + lane * 16) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        *reinterpret_cast<f4*>(qb + size_t(p) * 2048 + lane * 16) = *reinterpret_cast<const f4*>(src);
+        *reinterpret_cast<f4*>(qb + size_t(p) * 2048 + 1024 + lane * 16) = *reinterpret_cast<const f4*>(src + 4);
+      }
     }
   }
   lds_barrier();  // K and Q are dead; their space becomes A and QKm
@@ -587,8 +610,8 @@ template <typename IO, int DK, int C>
 __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
                                                           const IO* __restrict__ q, const IO* __restrict__ k,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
-                                                          const uint8_t* __restrict__ ws, const float* s_in,
-                                                          IO* __restrict__ out, float* s_out) {
+                                                          const uint8_t* __restrict__ ws, const uint8_t* __restrict__ qf,
+                                                          const float* s_in, IO* __restrict__ out, float* s_out) {
   constexpr bool BF = sizeof(IO) == 2;
   using Geo = Geom<BF, C>;
   using Lds = SweepLds<IO, DK, C>;
@@ -785,26 +808,19 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     // loads have a whole chunk to land; the Q and R fragments of the next
     // chunk stay in registers.  Loads are spread over the three windows so
     // that no window waits behind a full memory queue.
-    // Q goes through LDS like K: loading whole rows (4 rows of 256 bytes
-    // per instruction) runs about four times faster than loading the 16-row
-    // fragments directly, whose rows sit a power-of-two stride apart.
     struct Staged {
       uint4 kp[NKP];  // K rows, 16-byte pieces
-      uint4 qp[NKP];  // Q rows, 16-byte pieces
       uint4 vt[NVT];  // V slice, T' fragments and scalars, 16-byte pieces
     };
     struct Frags {
+      E aq[NKS];   // Q rows of block r (A fragments, stored in that order by the prep kernel)
       Sp rf[NTF];  // R fragments of block r
     };
     auto fetch_k = [&](Staged& P, int cc) {
       const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-      const uint32_t rows = uint32_t((nc - 1) * kstride * ESZ) + kq_tail;
-      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, rows);
-      const Rsrc rq = make_rsrc(q + (size_t(t0) * h_qk + j) * DK, rows);
+      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
 #pragma unroll
       for (int it = 0; it < NKP; ++it) P.kp[it] = bload16(rk, koff[it]);
-#pragma unroll
-      for (int it = 0; it < NKP; ++it) P.qp[it] = bload16(rq, koff[it]);
     };
     auto fetch_vt = [&](Staged& P, int cc) {
       // one plain load per piece, its address chosen per lane: V rows past
@@ -828,6 +844,16 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       // every helper wave issues the same loads (a lane whose fragment is not
       // needed reads one shared line instead)
       const int rb = rowblk ? r : 0;
+      const uint8_t* qp = qf + (size_t(gc0 + cc) * h_qk + j) * qfrag_bytes(DK, C, BF) + lane * 16;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        if constexpr (BF) {
+          F.aq[s] = *reinterpret_cast<const uint4*>(qp + size_t(rb * NKS + s) * 1024);
+        } else {
+          F.aq[s].a = *reinterpret_cast<const f4*>(qp + size_t(rb * NKS + s) * 2048);
+          F.aq[s].b = *reinterpret_cast<const f4*>(qp + size_t(rb * NKS + s) * 2048 + 1024);
+        }
+      }
       const uint8_t* rp = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES + Geo::R_OFF +
                           size_t(frag_base(rb)) * 2 * Geo::PLANE;
 #pragma unroll
@@ -838,14 +864,10 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     };
     auto commit = [&](const Staged& P, int buf) {
       IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF);
-      IO* sQ = reinterpret_cast<IO*>(smem + Lds::Q_OFF);
 #pragma unroll
       for (int it = 0; it < NKP; ++it) {
         const int x = ht + 256 * it;
-        if (x < C * PER_ROW) {
-          *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
-          *reinterpret_cast<uint4*>(sQ + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.qp[it];
-        }
+        if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
       }
 #pragma unroll
       for (int it = 0; it < NVT; ++it) {
@@ -874,7 +896,6 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       // next = chunk cc+1 (loaded, not yet committed); after = free, receives chunk cc+2
       const int buf = cc & 1, nc = chunk_nc(cc);
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
-      const IO* sQ = reinterpret_cast<const IO*>(smem + Lds::Q_OFF);
 
       // (1) Z = Q S^T of block r (S is the chunk's initial state); K, Q, V,
       // T' and scalars of chunk cc+2
@@ -883,11 +904,10 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         f4 z1 = zero4();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          E aq, bs;
-          ld8(aq, sQ + (16 * r + col) * KP + 8 * grp + 32 * s);
+          E bs;
           xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
-          if (s & 1) z1 = mma32(aq, bs, z1);
-          else z = mma32(aq, bs, z);
+          if (s & 1) z1 = mma32(F.aq[s], bs, z1);
+          else z = mma32(F.aq[s], bs, z);
         }
         z = z + z1;
       }
@@ -950,10 +970,14 @@ static size_t chunk_bytes(bool bf16, int chunk) {
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t table_bytes(const Dims& d, int chunk) { return round256(chunked_max_chunks(d, chunk) * 8); }
 
+static size_t blocks_bytes(const Dims& d, int chunk) {
+  return chunked_max_chunks(d, chunk) * size_t(d.h_v) * chunk_bytes(d.bf16, chunk);
+}
+
 size_t chunked_workspace_bytes(const Dims& d, int chunk) {
-  const size_t cb = chunk_bytes(d.bf16, chunk);
-  if (cb == 0) return 0;
-  return table_bytes(d, chunk) + chunked_max_chunks(d, chunk) * size_t(d.h_v) * cb;
+  if (chunk_bytes(d.bf16, chunk) == 0) return 0;
+  return table_bytes(d, chunk) + blocks_bytes(d, chunk) +
+         chunked_max_chunks(d, chunk) * size_t(d.h_qk) * qfrag_bytes(d.d_k, chunk, d.bf16);
 }
 
 template <typename IO, int DK, int C>
@@ -963,6 +987,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   uint8_t* base = static_cast<uint8_t*>(workspace);
   int2* tab = reinterpret_cast<int2*>(base);
   uint8_t* ws = base + table_bytes(d, C);
+  uint8_t* qf = ws + blocks_bytes(d, C);
   const size_t max_chunks = chunked_max_chunks(d, C);
   hipError_t e = hipSuccess;
   if (d.num_seqs > 1) {
@@ -982,7 +1007,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
     Prof prof("chunk_prep", st);
     hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(512), lds,
                        st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, d.num_seqs,
-                       d.total_tokens, tab, ws);
+                       d.total_tokens, tab, ws, qf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -998,7 +1023,7 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   Prof prof("chunk_sweep", st);
   hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
                      d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(q),
-                     static_cast<const IO*>(k), static_cast<const IO*>(v), cu, ws, s_in,
+                     static_cast<const IO*>(k), static_cast<const IO*>(v), cu, ws, qf, s_in,
                      static_cast<IO*>(out), s_out);
   return hipGetLastError();
 }
