@@ -840,9 +840,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         P.vt[it] = *reinterpret_cast<const uint4*>(src);
       }
     };
-    auto fetch_frags = [&](Frags& F, int cc) {
-      // every helper wave issues the same loads (a lane whose fragment is not
-      // needed reads one shared line instead)
+    auto fetch_qfrags = [&](Frags& F, int cc) {
       const int rb = rowblk ? r : 0;
       const uint8_t* qp = qf + (size_t(gc0 + cc) * h_qk + j) * qfrag_bytes(DK, C, BF) + lane * 16;
 #pragma unroll
@@ -854,6 +852,11 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
           F.aq[s].b = *reinterpret_cast<const f4*>(qp + size_t(rb * NKS + s) * 2048 + 1024);
         }
       }
+    };
+    auto fetch_rfrags = [&](Frags& F, int cc) {
+      // every helper wave issues the same loads (a lane whose fragment is not
+      // needed reads one shared line instead)
+      const int rb = rowblk ? r : 0;
       const uint8_t* rp = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES + Geo::R_OFF +
                           size_t(frag_base(rb)) * 2 * Geo::PLANE;
 #pragma unroll
@@ -885,7 +888,8 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     if (nchunk > 0) {
       fetch_k(SA, 0);
       fetch_vt(SA, 0);
-      fetch_frags(F, 0);
+      fetch_qfrags(F, 0);
+      fetch_rfrags(F, 0);
       fetch_k(SB, min(1, nchunk - 1));
       fetch_vt(SB, min(1, nchunk - 1));
       commit(SA, 0);
@@ -897,8 +901,8 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       const int buf = cc & 1, nc = chunk_nc(cc);
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
 
-      // (1) Z = Q S^T of block r (S is the chunk's initial state); K, Q, V,
-      // T' and scalars of chunk cc+2
+      // (1) Z = Q S^T of block r (S is the chunk's initial state); K, V, T'
+      // and scalars of chunk cc+2, Q fragments of chunk cc+1
       f4 z = zero4();
       if (rowblk) {
         f4 z1 = zero4();
@@ -914,10 +918,10 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       const int c2 = min(cc + 2, nchunk - 1), c1 = min(cc + 1, nchunk - 1);  // past the end: harmless refetch
       fetch_k(after, c2);
       fetch_vt(after, c2);
+      fetch_qfrags(Fn, c1);
       lds_barrier();
 
-      // (2) O = gamma Z + R Y for block r, stored straight from the D layout;
-      // Q and R fragments of chunk cc+1
+      // (2) O = gamma Z + R Y for block r, stored straight from the D layout
       if (rowblk) {
         f4 oh, ol = zero4();
 #pragma unroll
@@ -936,10 +940,10 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
 #pragma unroll
         for (int e = 0; e < 4; ++e) bstore_el<IO>(ro, ooff[e], o[e]);
       }
-      fetch_frags(Fn, c1);
       lds_barrier();
 
-      // (3) stage chunk cc+1 in the LDS buffers
+      // (3) R fragments of chunk cc+1; stage chunk cc+1 in the LDS buffers
+      fetch_rfrags(Fn, c1);
       commit(next, buf ^ 1);  // after the last chunk this fills buffers nobody reads
       F = Fn;
       lds_barrier();
