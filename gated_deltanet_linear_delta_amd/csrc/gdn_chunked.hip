@@ -12,13 +12,14 @@
 //   A_ri = beta_r exp(G_r - G_i) (k_r . k_i)  (i < r),   T = (I + A)^{-1}
 //   QKm_ri = exp(G_r - G_i) (q_r . k_i)       (i <= r)
 //   Y   = diag(beta) V - diag(beta gamma) (K S0^T)
-//   O   = diag(gamma) (Q S0^T) + R Y,          R  = QKm T
-//   S1^T = gamma_{n-1} S0^T + K^T (T' Y),      T' = diag(dec) T
+//   O   = diag(gamma) (Q S0^T) + R Y,          R = QKm T
+//   S1^T = gamma_{n-1} S0^T + G Y,              G = K^T diag(dec) T
 //
-// (U = T Y is the block's matrix of delta updates; folding T into R and T'
-// leaves two block products between one state and the next.)  Decays are
-// always formed as exp of a non-positive difference of fp64 partial sums, so
-// nothing overflows and nothing but true decay underflows.
+// (T Y is the block's matrix of delta updates; folding T into R and G, which
+// do not depend on the state, leaves two block products between one state
+// and the next: Y from S0, then S1 from Y.)  Decays are always formed as exp
+// of a non-positive difference of fp64 partial sums, so nothing overflows and
+// nothing but true decay underflows.
 //
 // Workspace slots: chunk j of sequence n uses slot (bos_n + n (C - 1)) / C + j
 // (bos_n = its first token).  Consecutive sequences get disjoint slot ranges
@@ -32,21 +33,24 @@
 //   2. chunk_prep_kernel, one workgroup per (chunk, value head), fully
 //      parallel: Gram products on MFMA, gate prefix sums, A, T = (I + A)^{-1}
 //      (16x16 diagonal blocks by forward substitution in registers,
-//      off-diagonal blocks by fp32 MFMA block products), R = QKm T, and the
-//      per-token scalars, written to the workspace as MFMA A fragments.
+//      off-diagonal blocks by fp32 MFMA block products), R = QKm T, G, and the
+//      per-token scalars, written to the workspace as MFMA A fragments; the
+//      first value head of each query/key group also writes Q and K as
+//      fragments.
 //   3. chunk_sweep_kernel, one workgroup per (sequence, value head, 16 rows of
 //      the state): walks the chunks in order with its 16 x d_k slice of the
 //      fp32 state in MFMA accumulators.  State rows are independent given the
-//      block's T, so slices of one head never talk to each other.  Chunk c+1's
-//      inputs are fetched into registers while chunk c is computed, and the
-//      barriers wait only for LDS traffic.
+//      block's G, so slices of one head never talk to each other.  Four
+//      waves run the recurrence (Y, then the state update); four others form
+//      the output and stage inputs ahead.
 //
 // All block products use 16x16x32 fragments (see gdn_common.hpp).  Precision:
-// bf16 inputs (K, Q, V) enter MFMA exactly.  Y and T'Y are split into hi + lo
-// bf16 halves, as is R; the state (in K S^T, Q S^T) and T' enter rounded
-// once to bf16: their error reaches the outputs damped by the block decay
-// and stays well below the output's own bf16 rounding.  Every product
-// accumulates in fp32.  fp32 inputs use fp32 MFMA throughout.
+// bf16 inputs (K, Q, V) enter MFMA exactly.  Y and R are split into hi + lo
+// bf16 halves (as is diag(dec) T when G is formed); G and the state (in
+// K S^T, Q S^T) enter rounded once to bf16: their error reaches the outputs
+// damped by the block decay and stays well below the output's own bf16
+// rounding.  Every product accumulates in
+// fp32.  fp32 inputs use fp32 MFMA throughout.
 #include <type_traits>
 
 #include "gdn_common.hpp"
@@ -74,6 +78,11 @@ __device__ __forceinline__ void mm_ss(const sp8& a, const sp8& b, f4& ch, f4& cl
   cl = mma32(a.lo, b.hi, cl);
 }
 __device__ __forceinline__ void mm_ss(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
+__device__ __forceinline__ void mm_se(const sp8& a, uint4 b, f4& ch, f4& cl) {
+  ch = mma32(a.hi, b, ch);
+  cl = mma32(a.lo, b, cl);
+}
+__device__ __forceinline__ void mm_se(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
 
 template <bool BF>
 struct Types {
@@ -176,29 +185,44 @@ constexpr size_t xb_bytes_split() {
   return (BF ? 2 : 1) * XBuf<BF, K>::PLANE;
 }
 
-// Workspace block of one (chunk, value head).  A fragments of 16 rows x 32
-// columns of the lower-triangular C x C matrices T' and R: fragment (r, s),
-// r = row block, s = 32-wide column slab, exists for s <= r / 2.  A fragment
-// is one (single) or two (split / fp32) planes of 64 lanes x 16 bytes.
-template <bool BF, int C>
+// Fragment counts.  An operand fragment covers 16 rows x 32 columns: 64
+// lanes x 8 values, stored as one 1 KiB plane per 8 bf16 (a bf16 value rounded
+// once) or two planes (hi + lo bf16 halves of a split value, or fp32).
+__host__ __device__ constexpr int dk_pad(int dk) { return dk < 32 ? 32 : dk; }
+__host__ __device__ constexpr int c_pad(int c) { return c < 32 ? 32 : c; }
+// fragments (r, s), s <= r / 2, of a lower-triangular C x C matrix
+__host__ __device__ constexpr int tri_frags(int c) { return c == 16 ? 1 : (c == 32 ? 2 : 6); }
+// Workspace block of one (chunk, value head): G = K^T diag(dec) T as d_k / 16
+// row blocks x 32-token slabs (rounded once), R = QKm T as its
+// lower-triangular fragments (split), then beta, beta gamma and gamma per
+// token.
+__host__ __device__ constexpr size_t g_off(bool, int, int) { return 0; }
+__host__ __device__ constexpr size_t r_off(bool bf, int dk, int c) {
+  return size_t(dk / 16) * (c_pad(c) / 32) * (bf ? 1 : 2) * 1024;
+}
+__host__ __device__ constexpr size_t scal_off(bool bf, int dk, int c) { return r_off(bf, dk, c) + size_t(tri_frags(c)) * 2 * 1024; }
+__host__ __device__ constexpr size_t chunk_block_bytes(bool bf, int dk, int c) {
+  return (scal_off(bf, dk, c) + 3 * size_t(c) * sizeof(float) + 255) / 256 * 256;
+}
+// Block of one (chunk, query/key head): Q, then K, as A fragments (C / 16 row
+// blocks x d_k / 32 slabs), so that the sweep loads them as contiguous 1 KiB
+// rows.
+__host__ __device__ constexpr size_t k_frag_off(int dk, int c, bool bf) {
+  return size_t(c / 16) * (dk_pad(dk) / 32) * (bf ? 1 : 2) * 1024;
+}
+__host__ __device__ constexpr size_t qk_frag_bytes(int dk, int c, bool bf) { return 2 * k_frag_off(dk, c, bf); }
+template <bool BF, int DK, int C>
 struct Geom {
   static constexpr int NB = C / 16;  // 16-token row blocks
-  static constexpr int NF = NB == 1 ? 1 : (NB == 2 ? 2 : 6);
-  static constexpr int TPL = BF ? 1 : 2;  // planes of a T' fragment
+  static constexpr int NF = tri_frags(C);
+  static constexpr int TPL = BF ? 1 : 2;  // planes of a rounded-once fragment
   static constexpr size_t PLANE = 1024;
-  static constexpr size_t T_OFF = 0;
-  static constexpr size_t R_OFF = T_OFF + size_t(NF) * TPL * PLANE;
-  static constexpr size_t SCAL_OFF = R_OFF + size_t(NF) * 2 * PLANE;
-  static constexpr size_t BYTES = SCAL_OFF + 4 * C * sizeof(float);
-  static_assert(BYTES % 256 == 0, "keep per-chunk blocks 256-byte aligned");
+  static constexpr size_t G_OFF = g_off(BF, DK, C);
+  static constexpr size_t R_OFF = r_off(BF, DK, C);
+  static constexpr size_t SCAL_OFF = scal_off(BF, DK, C);
+  static constexpr size_t BYTES = chunk_block_bytes(BF, DK, C);
+  static_assert(SCAL_OFF % 256 == 0 && BYTES % 256 == 0, "keep per-chunk blocks 256-byte aligned");
 };
-// Q of one (chunk, query/key head) laid out as the sweep's A fragments: for
-// each 16-row block r and 32-column slab s, 64 lanes x 8 values (one 1 KiB
-// plane in bf16, two in fp32), so that the sweep loads them as contiguous
-// 1 KiB rows instead of 16 rows of 64 bytes a power-of-two stride apart.
-__host__ __device__ constexpr size_t qfrag_bytes(int dk, int c, bool bf) {
-  return size_t(c / 16) * size_t((dk < 32 ? 32 : dk) / 32) * (bf ? 1 : 2) * 1024;
-}
 
 // first fragment of row block r: sum over r' < r of (r' / 2 + 1)
 __device__ __forceinline__ constexpr int frag_base(int r) { return r == 0 ? 0 : (r == 1 ? 1 : (r == 2 ? 2 : 4)); }
@@ -236,9 +260,11 @@ struct PrepLds {
   static constexpr size_t A_OFF = 0, QK_OFF = M_BYTES, T_OFF = 2 * M_BYTES;
   static constexpr size_t GB_OFF = U_BYTES;           // fp64 prefix sum before each 16-token block
   static constexpr size_t GL_OFF = GB_OFF + 8 * 4;    // fp32 prefix sum within the token's block
-  static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);
-  static constexpr size_t D_OFF = B_OFF + C * sizeof(float);
+  static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);   // beta
+  static constexpr size_t D_OFF = B_OFF + C * sizeof(float);    // dec
   static constexpr size_t BYTES = D_OFF + C * sizeof(float);
+  // at the end the whole region [0, U_BYTES) holds G^T in K's layout
+  static_assert(KQ_BYTES / 2 <= U_BYTES, "G tile fits the union");
 };
 
 template <typename IO, int DK, int C>
@@ -246,24 +272,18 @@ struct SweepLds {
   static constexpr bool BF = sizeof(IO) == 2;
   static constexpr int ESZ = int(sizeof(IO));
   static constexpr int E16 = 16 / ESZ;
-  static constexpr int CP = C < 32 ? 32 : C;     // token rows of the staged K tile
-  static constexpr int DKP = DK < 32 ? 32 : DK;  // its columns
-  static constexpr int KP = frag_row_stride(DKP * ESZ) / ESZ;  // row stride, elements
-  static constexpr size_t KBUF = size_t(CP) * KP * ESZ;
-  static constexpr size_t VBUF = size_t(C) * 16 * ESZ;                       // V slice: C tokens x 16 values
-  static constexpr size_t TBUF = size_t(Geom<BF, C>::NF) * Geom<BF, C>::TPL * Geom<BF, C>::PLANE;  // T' fragments
-  static constexpr size_t SCBUF = 4 * C * sizeof(float);                     // beta, beta gamma, gamma, dec
-  // K, Q, V and T' have one buffer each: a chunk's copies are written after
-  // the last read of the previous chunk's (the second barrier of a step).
-  // The scalars are read until the end of a step and have two (chunk parity).
-  static constexpr size_t K_OFF = 0;
-  static constexpr size_t V_OFF = K_OFF + KBUF;
-  static constexpr size_t T_OFF = V_OFF + VBUF;
-  static constexpr size_t SC_OFF = T_OFF + TBUF;
-  static constexpr size_t S_OFF = SC_OFF + 2 * SCBUF;  // state (B fragments of S^T)
+  static constexpr int CP = c_pad(C);    // token rows of the exchange buffer
+  static constexpr int DKP = dk_pad(DK);  // key columns of the state buffer
+  static constexpr size_t VBUF = size_t(C) * 16 * ESZ;    // V slice: C tokens x 16 values
+  static constexpr size_t SCBUF = 3 * C * sizeof(float);  // beta, beta gamma, gamma
+  // S (B fragments of S^T) and Y have one buffer each.  The V slice and the
+  // scalars are written two chunks ahead: V has two buffers (chunk parity),
+  // the scalars, read until the end of a step, four.
+  static constexpr size_t S_OFF = 0;
   static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
-  static constexpr size_t UD_OFF = Y_OFF + xb_bytes_split<BF, CP>();
-  static constexpr size_t BYTES = UD_OFF + xb_bytes_split<BF, CP>();
+  static constexpr size_t V_OFF = Y_OFF + xb_bytes_split<BF, CP>();
+  static constexpr size_t SC_OFF = V_OFF + 2 * VBUF;
+  static constexpr size_t BYTES = SC_OFF + 4 * SCBUF;
   static_assert(BYTES % 16 == 0, "zeroed in 16-byte pieces");
 };
 
@@ -301,6 +321,18 @@ __device__ __forceinline__ void bstore_el(Rsrc r, uint32_t off, float x) {
   if constexpr (sizeof(IO) == 2) __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), r, off, 0, 0);
   else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
 }
+// Four consecutive values of one row (8 bytes in bf16, 16 in fp32).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename IO>
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, f4 x) {
+  if constexpr (sizeof(IO) == 2) {
+    const uint2 v = bf16x4(x);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
+  }
+}
 __device__ __forceinline__ float io_val(uint16_t x) { return bf2f(x); }
 __device__ __forceinline__ float io_val(float x) { return x; }
 // A split (bf16 hi + lo, two planes `plane` bytes apart) or fp32 operand from global memory.
@@ -312,6 +344,9 @@ __device__ __forceinline__ void ld_split(f8& d, const uint8_t* p, int plane) {
   d.a = *reinterpret_cast<const f4*>(p);
   d.b = *reinterpret_cast<const f4*>(p + plane);
 }
+// A rounded-once (bf16: one plane) or fp32 (two planes) operand from global memory.
+__device__ __forceinline__ void ld_e(uint4& d, const uint8_t* p, int) { d = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void ld_e(f8& d, const uint8_t* p, int plane) { ld_split(d, p, plane); }
 
 }  // namespace
 
@@ -342,21 +377,26 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
                                                          const int2* __restrict__ tab, uint8_t* __restrict__ ws,
                                                          uint8_t* __restrict__ qf) {
   constexpr bool BF = sizeof(IO) == 2;
-  using Geo = Geom<BF, C>;
+  using Geo = Geom<BF, DK, C>;
   using Lds = PrepLds<IO, DK, C>;
   using E = typename Types<BF>::E;
+  using Sp = typename Types<BF>::S;
   constexpr int NB = Geo::NB, E16 = Lds::E16, KP = Lds::KP, BP = Lds::BP;
-  constexpr int NKS = Lds::DKP / 32;
+  constexpr int NKS = Lds::DKP / 32, KB = DK / 16, NTS = Lds::CP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
-  constexpr int NW = 8;                     // waves per workgroup
+  constexpr int NW = 8;                      // waves per workgroup
   constexpr int NGP = (NBLK + NW - 1) / NW;  // Gram blocks per wave
+  constexpr int WPK = NW / KB;               // waves per 16-key block of G
+  constexpr int NRW = (NB + WPK - 1) / WPK;  // token blocks of G per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
-  float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);   // after the Gram products
-  float* sR = sA;                                            // after the inverse
+  float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);  // after the Gram products
+  float* sR = sA;                                           // after the inverse
   float* sQK = reinterpret_cast<float*>(smem + Lds::QK_OFF);
+  float* sTt = sQK;                                         // after R: T'^T
   float* sT = reinterpret_cast<float*>(smem + Lds::T_OFF);
+  IO* sG = reinterpret_cast<IO*>(smem);  // at the end: G^T (tokens x keys) in K's layout
   double* sGb = reinterpret_cast<double*>(smem + Lds::GB_OFF);
   float* sGl = reinterpret_cast<float*>(smem + Lds::GL_OFF);
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
@@ -373,6 +413,43 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   auto lt = [&](float* m, int row, int c) {
     const int rb = row >> 4, cb = c >> 4;
     return m + (rb * (rb + 1) / 2 + cb) * 16 * BP + (row & 15) * BP + (c & 15);
+  };
+  // row `row`, columns k0 .. k0 + 7 of a stored lower-triangular matrix times
+  // per-column factors fc (zero above the diagonal and past C)
+  auto tri_row8 = [&](float* m, const float* fc, int row, int k0) {
+    f8 x;
+    zero(x);
+    if (k0 < C && (k0 >> 4) <= (row >> 4)) {
+      x.a = *reinterpret_cast<const f4*>(lt(m, row, k0));
+      x.b = *reinterpret_cast<const f4*>(lt(m, row, k0 + 4));
+      if (fc) {
+        x.a = x.a * *reinterpret_cast<const f4*>(fc + k0);
+        x.b = x.b * *reinterpret_cast<const f4*>(fc + k0 + 4);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (k0 + e > row) x.a[e] = 0.f;
+      if (k0 + 4 + e > row) x.b[e] = 0.f;
+    }
+    return x;
+  };
+  // fragment p of the lower-triangular fragment set: row block and slab
+  auto frag_rs = [&](int p, int& r, int& s) {
+    r = 0;
+    while (r + 1 < NB && frag_base(r + 1) <= p) ++r;
+    s = p - frag_base(r);
+  };
+  auto store_split = [&](uint8_t* dst, const f8& x) {  // two planes: hi, lo (fp32: a, b)
+    if constexpr (BF) {
+      uint4 hi, lo;
+      split_bf16x8(x, hi, lo);
+      *reinterpret_cast<uint4*>(dst) = hi;
+      *reinterpret_cast<uint4*>(dst + Geo::PLANE) = lo;
+    } else {
+      *reinterpret_cast<f4*>(dst) = x.a;
+      *reinterpret_cast<f4*>(dst + Geo::PLANE) = x.b;
+    }
   };
   uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
 
@@ -418,7 +495,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       sc[lane] = bl;
       sc[C + lane] = bl * gam;
       sc[2 * C + lane] = gam;
-      sc[3 * C + lane] = dec;
     }
   }
   lds_barrier();
@@ -456,22 +532,23 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       gq[n] = gq[n] + q1;
     }
   }
-  // the first value head of each query/key group stores Q as fragments
+  // the first value head of each query/key group stores Q and K as fragments
   if (h % (h_v / h_qk) == 0) {
     constexpr int NQF = NB * NKS;
-    uint8_t* qb = qf + (size_t(gc) * h_qk + j) * qfrag_bytes(DK, C, BF);
-    for (int p = wave; p < NQF; p += NW) {
-      const int rq = p / NKS, sq = p % NKS;
-      const IO* src = sQ + (16 * rq + col) * KP + 32 * sq + 8 * grp;
+    uint8_t* qb = qf + (size_t(gc) * h_qk + j) * qk_frag_bytes(DK, C, BF);
+    for (int p = wave; p < 2 * NQF; p += NW) {
+      const int rq = (p % NQF) / NKS, sq = p % NKS;
+      const IO* src = (p < NQF ? sQ : sK) + (16 * rq + col) * KP + 32 * sq + 8 * grp;
+      uint8_t* dst = qb + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
       if constexpr (BF) {
-        *reinterpret_cast<uint4*>(qb + size_t(p) * 1024 + lane * 16) = *reinterpret_cast<const uint4*>(src);
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
-        *reinterpret_cast<f4*>(qb + size_t(p) * 2048 + lane * 16) = *reinterpret_cast<const f4*>(src);
-        *reinterpret_cast<f4*>(qb + size_t(p) * 2048 + 1024 + lane * 16) = *reinterpret_cast<const f4*>(src + 4);
+        *reinterpret_cast<f4*>(dst) = *reinterpret_cast<const f4*>(src);
+        *reinterpret_cast<f4*>(dst + Geo::PLANE) = *reinterpret_cast<const f4*>(src + 4);
       }
     }
   }
-  lds_barrier();  // K and Q are dead; their space becomes A and QKm
+  lds_barrier();  // K and Q are dead; their space becomes A, QKm and T
 #pragma unroll
   for (int n = 0; n < NGP; ++n) {
     const int pb = wave + NW * n;
@@ -513,6 +590,29 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
+  // K^T operand of this wave's 16-key block of G (rows = keys, k = tokens),
+  // re-read from global memory since the K tile is gone: one element per
+  // load, rows past the chunk read as zero.  Issued here so that the loads
+  // land during the off-diagonal rounds.
+  const int wkb = wave % KB;
+  E ktw[NTS];
+  {
+    const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t(((nc - 1) * h_qk * DK + DK) * sizeof(IO)));
+#pragma unroll
+    for (int s = 0; s < NTS; ++s) {
+      IO e8[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq)
+        e8[qq] = bload_el<IO>(rk, uint32_t(((32 * s + 8 * grp + qq) * h_qk * DK + 16 * wkb + col) * sizeof(IO)));
+      if constexpr (BF) {
+        ktw[s] = uint4{pack2(e8[0], e8[1]), pack2(e8[2], e8[3]), pack2(e8[4], e8[5]), pack2(e8[6], e8[7])};
+      } else {
+        ktw[s].a = f4{e8[0], e8[1], e8[2], e8[3]};
+        ktw[s].b = f4{e8[4], e8[5], e8[6], e8[7]};
+      }
+    }
+  }
+
   // Off-diagonal blocks in two rounds, T being block lower triangular:
   //   T(i, i-1) = -T(i, i) A(i, i-1) T(i-1, i-1)             (i odd)
   // then, with the 32 x 32 halves T1 (blocks 0-1) and T2 (blocks 2-3),
@@ -552,84 +652,115 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
 
   // R = QKm T, lower-triangular blocks R(r, i) = sum_{k=i}^{r} QKm(r, k) T(k, i), in fp32.
   for (int p = wave; p < NBLK; p += NW) {
-    int r = 0;
-    while ((r + 1) * (r + 2) / 2 <= p) ++r;
-    const int i = p - r * (r + 1) / 2;
+    const int r = tri_row(p), i = p - r * (r + 1) / 2;
     f4 acc = zero4();
-    for (int kk = i; kk <= r; ++kk) {
-      acc = mma_f32(arow(sQK, r, kk), tcol(kk, i), acc);
-    }
+    for (int kk = i; kk <= r; ++kk) acc = mma_f32(arow(sQK, r, kk), tcol(kk, i), acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) *lt(sR, 16 * r + 4 * grp + e, 16 * i + col) = acc[e];
   }
   lds_barrier();
 
-  // Fragments (r, s), s <= r / 2, of T' = diag(dec) T and R, lower-triangular
-  // (entries above the diagonal and beyond C are zero).
+  // R as split fragments.  T' = diag(dec) T transposed into QKm's space:
+  // block (jb, ib) of T' is stored in slot (jb, ib) with rows and columns
+  // exchanged, so that a column of T' reads as a row.
   for (int p = wave; p < Geo::NF; p += NW) {
-    int r = 0;
-    while (r + 1 < NB && frag_base(r + 1) <= p) ++r;
-    const int s = p - frag_base(r);
-    const int row = 16 * r + col, k0 = 32 * s + 8 * grp;
-    f8 tv, rv;
-    zero(tv), zero(rv);
-    if (k0 < C && (k0 >> 4) <= r) {  // blocks above the diagonal are zero and not stored
-      tv.a = *reinterpret_cast<const f4*>(lt(sT, row, k0));
-      tv.b = *reinterpret_cast<const f4*>(lt(sT, row, k0 + 4));
-      rv.a = *reinterpret_cast<const f4*>(lt(sR, row, k0));
-      rv.b = *reinterpret_cast<const f4*>(lt(sR, row, k0 + 4));
-    }
-    const float dr = sDec[row];
+    int r, s;
+    frag_rs(p, r, s);
+    store_split(wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16,
+                tri_row8(sR, nullptr, 16 * r + col, 32 * s + 8 * grp));
+  }
+  for (int pb = wave; pb < NBLK; pb += NW) {
+    const int jb = tri_row(pb), ib = pb - jb * (jb + 1) / 2;
+    f4 t;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ka = k0 + e <= row, kb = k0 + 4 + e <= row;
-      tv.a[e] = ka ? dr * tv.a[e] : 0.f;
-      tv.b[e] = kb ? dr * tv.b[e] : 0.f;
-      rv.a[e] = ka ? rv.a[e] : 0.f;
-      rv.b[e] = kb ? rv.b[e] : 0.f;
+      const int jr = 16 * jb + 4 * grp + e;
+      t[e] = sDec[jr] * *lt(sT, jr, 16 * ib + col);
     }
-    uint8_t* tp = wsb + Geo::T_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
-    uint8_t* rp = wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16;
+    *reinterpret_cast<f4*>(sTt + pb * 16 * BP + col * BP + 4 * grp) = t;
+  }
+  lds_barrier();
+
+  // G blocks (key block wkb, token block r) = sum_s K^T(wkb, slab s) T'(slab s, r),
+  // T' split into hi + lo halves: the B fragment of T' holds its column
+  // 16 r + col, rows 32 s + 8 grp .. (slabs reaching the diagonal, s >= r / 2).
+  f4 gacc[NRW];
+#pragma unroll
+  for (int ri = 0; ri < NRW; ++ri) {
+    const int r = wave / KB + WPK * ri;
+    gacc[ri] = zero4();
+    if (r < NB) {
+      f4 cl = zero4();
+#pragma unroll
+      for (int s = 0; s < NTS; ++s) {
+        if (2 * s + 1 >= r) {
+          const int jb = 2 * s + (grp >> 1);  // token block of rows 32 s + 8 grp ..
+          f8 tv;
+          zero(tv);
+          if (jb >= r && jb < NB) {  // blocks above the diagonal and past C are zero
+            const float* src = sTt + (jb * (jb + 1) / 2 + r) * 16 * BP + col * BP + 8 * (grp & 1);
+            tv.a = *reinterpret_cast<const f4*>(src);
+            tv.b = *reinterpret_cast<const f4*>(src + 4);
+          }
+          Sp tb;
+          if constexpr (BF) split_bf16x8(tv, tb.hi, tb.lo);
+          else tb = tv;
+          mm_es(ktw[s], tb, gacc[ri], cl);
+        }
+      }
+      gacc[ri] = gacc[ri] + cl;
+    }
+  }
+  lds_barrier();  // A, R and T are dead; the region becomes the G^T tile
+#pragma unroll
+  for (int ri = 0; ri < NRW; ++ri) {
+    const int r = wave / KB + WPK * ri;
+    if (r < NB) {  // D block: G rows = keys 16 wkb + 4 grp .., column = token 16 r + col
+      IO* dst = sG + (16 * r + col) * KP + 16 * wkb + 4 * grp;
+      if constexpr (BF) *reinterpret_cast<uint2*>(dst) = bf16x4(gacc[ri]);
+      else *reinterpret_cast<f4*>(dst) = gacc[ri];
+    }
+  }
+  lds_barrier();
+  // G as A fragments (b, s): rows = keys 16 b .., k = tokens 32 s + 8 grp ..
+  // (tokens past C zero)
+  for (int p = wave; p < KB * NTS; p += NW) {
+    const int b = p / NTS, s = p % NTS;
+    const bool live = 32 * s + 8 * grp < C;
+    uint8_t* dst = wsb + Geo::G_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
     if constexpr (BF) {
-      uint4 th, tl, rh, rl;
-      split_bf16x8(tv, th, tl);
-      split_bf16x8(rv, rh, rl);
-      *reinterpret_cast<uint4*>(tp) = th;
-      *reinterpret_cast<uint4*>(rp) = rh;
-      *reinterpret_cast<uint4*>(rp + Geo::PLANE) = rl;
+      const IO* src = sG + (32 * s + 8 * grp + col / 4) * KP + 16 * b + 4 * (col % 4);
+      const uint2 lo = lds_tr16(src), hi = lds_tr16(src + 4 * KP);
+      *reinterpret_cast<uint4*>(dst) = live ? uint4{lo.x, lo.y, hi.x, hi.y} : uint4{0u, 0u, 0u, 0u};
     } else {
-      *reinterpret_cast<f4*>(tp) = tv.a;
-      *reinterpret_cast<f4*>(tp + Geo::PLANE) = tv.b;
-      *reinterpret_cast<f4*>(rp) = rv.a;
-      *reinterpret_cast<f4*>(rp + Geo::PLANE) = rv.b;
+      f8 t;
+      ld8col(t, sG + (32 * s + 8 * grp) * KP + 16 * b + col, KP);
+      *reinterpret_cast<f4*>(dst) = live ? t.a : zero4();
+      *reinterpret_cast<f4*>(dst + Geo::PLANE) = live ? t.b : zero4();
     }
   }
 }
 
 template <typename IO, int DK, int C>
 __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
-                                                          const IO* __restrict__ q, const IO* __restrict__ k,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
                                                           const uint8_t* __restrict__ ws, const uint8_t* __restrict__ qf,
                                                           const float* s_in, IO* __restrict__ out, float* s_out) {
   constexpr bool BF = sizeof(IO) == 2;
-  using Geo = Geom<BF, C>;
+  using Geo = Geom<BF, DK, C>;
   using Lds = SweepLds<IO, DK, C>;
   using E = typename Types<BF>::E;
   using Sp = typename Types<BF>::S;
-  constexpr int NB = Geo::NB, KB = DK / 16, CP = Lds::CP, DKP = Lds::DKP, KP = Lds::KP, E16 = Lds::E16;
-  constexpr int ESZ = Lds::ESZ;
+  constexpr int NB = Geo::NB, KB = DK / 16, CP = Lds::CP, DKP = Lds::DKP, E16 = Lds::E16;
+  constexpr int ESZ = Lds::ESZ, TPL = Geo::TPL;
+  constexpr size_t PL = Geo::PLANE;
   constexpr int NKS = DKP / 32, NTS = CP / 32;  // 32-wide slabs along d_k and along the chunk
   constexpr int SB = (KB + 3) / 4;              // state blocks per chain wave
-  constexpr int NTF = (NB + 1) / 2;             // T' / R fragments per row block, at most
-  constexpr int PER_ROW = DK / E16;             // 16-byte pieces per K row
-  constexpr int NKP = (C * PER_ROW + 255) / 256;                                 // K pieces per helper lane
-  constexpr int NVP = int(Lds::VBUF / 16), NTP = int(Lds::TBUF / 16), NSP = int(Lds::SCBUF / 16);
-  constexpr int NVT = (NVP + NTP + NSP + 255) / 256;                             // other pieces per helper lane
+  constexpr int NTF = (NB + 1) / 2;             // R fragments per row block, at most
+  constexpr size_t QKF = qk_frag_bytes(DK, C, BF), KF = k_frag_off(DK, C, BF);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sS = smem + Lds::S_OFF;
   uint8_t* sY = smem + Lds::Y_OFF;
-  uint8_t* sUd = smem + Lds::UD_OFF;
 
   // Workgroups are dealt to the 8 XCDs round-robin; give the 16-row slices of
   // one head consecutive chain numbers on one XCD so they share its L2.
@@ -645,26 +776,34 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   const int wave = wave_id();
   const int r = wave & 3;                    // row block (and state-block group) of this wave
   const bool rowblk = NB >= 4 || r < NB;
+  const int rb = rowblk ? r : 0;             // row block whose fragments this wave loads
 
   int bos, eos;
   seq_range(cu, n, T, bos, eos);
   int nchunk = (eos - bos + C - 1) / C;
   const int gc0 = first_slot(bos, n, C);
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
-  const int kstride = h_qk * DK;  // elements between consecutive tokens of q / k
-  const int vstride = h_v * d_v;  // and of v
+  const int vstride = h_v * d_v;  // elements between consecutive tokens of v
   auto chunk_t0 = [&](int cc) { return bos + cc * C; };
   auto chunk_nc = [&](int cc) { return min(C, eos - chunk_t0(cc)); };
+  auto wsb = [&](int cc) { return ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES; };
+  auto qfb = [&](int cc) { return qf + (size_t(gc0 + cc) * h_qk + j) * QKF; };
+  // A fragments of row block rb from a Q or K set (d_k / 32 slabs)
+  auto fetch_rows = [&](E (&d)[NKS], const uint8_t* set) __attribute__((always_inline)) {
+    const uint8_t* p = set + size_t(rb * NKS) * TPL * PL + lane * 16;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) ld_e(d[s], p + s * TPL * PL, int(PL));
+  };
 
-  // zero LDS once: K rows / columns past C or d_k, and exchange columns past
-  // C or d_k, are read as zeros
+  // zero LDS once: exchange columns past C or d_k are read as zeros
   for (int x = tid; x < int(Lds::BYTES / 16); x += 512) reinterpret_cast<uint4*>(smem)[x] = uint4{0u, 0u, 0u, 0u};
   lds_barrier();
 
   if (wave < 4) {
     // ============================================================ chain waves
-    // The recurrence proper: per chunk X = K S^T, Y, T'Y and the state
-    // update, touching only LDS and the matrix cores.
+    // The recurrence proper: per chunk X = K S^T and Y for token block r,
+    // then S^T <- gamma_last S^T + G Y for the owned state blocks.  K and G
+    // fragments are loaded two chunks ahead into registers.
     f4 st[SB];
 #pragma unroll
     for (int bi = 0; bi < SB; ++bi) {
@@ -675,110 +814,111 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
       }
     }
-    lds_barrier();  // chunk 0 staged, state written
+    auto fetch_g = [&](E (&gf)[SB][NTS], int cc) __attribute__((always_inline)) {
+      const uint8_t* p = wsb(cc) + Geo::G_OFF + lane * 16;
+#pragma unroll
+      for (int bi = 0; bi < SB; ++bi) {
+        const int b = min(r + 4 * bi, KB - 1);  // a wave without this block loads a valid one and ignores it
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) ld_e(gf[bi][s], p + size_t(b * NTS + s) * TPL * PL, int(PL));
+      }
+    };
+    E kA[NKS], kB[NKS], gA[SB][NTS], gB[SB][NTS];
+    if (nchunk > 0) {
+      fetch_rows(kA, qfb(0) + KF);
+      fetch_rows(kB, qfb(min(1, nchunk - 1)) + KF);
+      fetch_g(gA, 0);
+    }
+    lds_barrier();  // state written, chunks 0 and 1 staged
 
-    const int arow = col * KP + 8 * grp;                       // A fragment rows of the K tile
-    const int tcol = 8 * grp * KP + col;                       // K^T fragment, element reads
-    const int trow = (8 * grp + col / 4) * KP + 4 * (col % 4);  // K^T fragment, transpose reads
-    for (int cc = 0; cc < nchunk; ++cc) {
-      const int buf = cc & 1, nc = chunk_nc(cc);
-      const IO* sK = reinterpret_cast<const IO*>(smem + Lds::K_OFF);
-      const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF);
-      const uint8_t* sTp = smem + Lds::T_OFF;
-      const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
+    // kf, gf: fragments of chunk cc; gn: the other G set, loaded here with
+    // chunk cc+1.  Each window issues its LDS reads first and its global
+    // loads next, so that a load waiting for the memory queue overlaps the
+    // LDS latency instead of delaying the barrier.
+    auto step = [&](int cc, E (&kf)[NKS], E (&gf)[SB][NTS], E (&gn)[SB][NTS]) __attribute__((always_inline)) {
+      const int nc = chunk_nc(cc);
+      const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF);
 
       // (1) X = K S^T for token block r; Y = beta V - beta gamma X
+      E bs[NKS];
+      uint2 vt;
+      f4 bt, bg;
+      if (rowblk) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) xb_read_single<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
+        bt = *reinterpret_cast<const f4*>(sSc + 16 * r + 4 * grp);
+        bg = *reinterpret_cast<const f4*>(sSc + C + 16 * r + 4 * grp);
+        if constexpr (BF) {
+          // rows 16 r + 4 grp .. + 3 of column col by one transpose read
+          const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF + (cc & 1) * Lds::VBUF);
+          vt = lds_tr16(sV + (16 * r + 4 * grp + col / 4) * 16 + 4 * (col % 4));
+        }
+      }
+      fetch_g(gn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
+      __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the products
       if (rowblk) {
         f4 x = zero4(), x1 = zero4();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          E ak, bs;
-          ld8(ak, sK + 16 * r * KP + arow + 32 * s);
-          xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
-          if (s & 1) x1 = mma32(ak, bs, x1);
-          else x = mma32(ak, bs, x);
+          if (s & 1) x1 = mma32(kf[s], bs[s], x1);
+          else x = mma32(kf[s], bs[s], x);
         }
         x = x + x1;
         float vv[4];
         if constexpr (BF) {
-          // rows 16 r + 4 grp .. + 3 of column col by one transpose read
-          const uint2 t = lds_tr16(sV + (16 * r + 4 * grp + col / 4) * 16 + 4 * (col % 4));
-          vv[0] = __uint_as_float(t.x << 16), vv[1] = __uint_as_float(t.x & 0xffff0000u);
-          vv[2] = __uint_as_float(t.y << 16), vv[3] = __uint_as_float(t.y & 0xffff0000u);
+          vv[0] = __uint_as_float(vt.x << 16), vv[1] = __uint_as_float(vt.x & 0xffff0000u);
+          vv[2] = __uint_as_float(vt.y << 16), vv[3] = __uint_as_float(vt.y & 0xffff0000u);
         } else {
+          const IO* sV = reinterpret_cast<const IO*>(smem + Lds::V_OFF + (cc & 1) * Lds::VBUF);
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[e] = sV[(16 * r + 4 * grp + e) * 16 + col];
         }
         f4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = 16 * r + 4 * grp + e;
-          const float b = sSc[tok], bg = sSc[C + tok];
-          y[e] = tok < nc ? b * vv[e] - bg * x[e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) y[e] = 16 * r + 4 * grp + e < nc ? bt[e] * vv[e] - bg[e] * x[e] : 0.f;
         xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
       }
       lds_barrier();
 
-      // (2) Ud = T' Y for token block r; K^T fragments for (3)
-      if (rowblk) {
-        const uint8_t* tf = sTp + size_t(frag_base(r)) * Geo::TPL * Geo::PLANE + lane * 16;
-        f4 uh = zero4(), ul = zero4();
+      // (2) S^T <- gamma_last S^T + G Y for the owned state blocks
+      Sp yb[NTS];
 #pragma unroll
-        for (int s = 0; s < NTF; ++s) {
-          if (2 * s <= r) {
-            Sp yb;
-            E tv;
-            xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
-            if constexpr (BF) {
-              tv = *reinterpret_cast<const uint4*>(tf + s * Geo::PLANE);
-            } else {
-              tv.a = *reinterpret_cast<const f4*>(tf + s * 2 * Geo::PLANE);
-              tv.b = *reinterpret_cast<const f4*>(tf + s * 2 * Geo::PLANE + Geo::PLANE);
-            }
-            mm_es(tv, yb, uh, ul);
-          }
-        }
-        xb_write_split<BF, CP>(sUd, col, 16 * r + 4 * grp, uh + ul);
-      }
-      E kt[SB][NTS];
-#pragma unroll
-      for (int bi = 0; bi < SB; ++bi) {
-        const int b = r + 4 * bi;
-        if (b < KB) {
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) {
-            if constexpr (BF) {
-              const uint2 lo = lds_tr16(sK + 32 * s * KP + trow + 16 * b);
-              const uint2 hi = lds_tr16(sK + 32 * s * KP + 4 * KP + trow + 16 * b);
-              kt[bi][s] = uint4{lo.x, lo.y, hi.x, hi.y};
-            } else {
-              ld8col(kt[bi][s], sK + 32 * s * KP + tcol + 16 * b, KP);
-            }
-          }
-        }
-      }
-      lds_barrier();
-
-      // (3) S^T <- gamma_last S^T + K^T Ud for the owned state blocks
+      for (int s = 0; s < NTS; ++s) xb_read_split<BF, CP>(yb[s], sY, col, 32 * s + 8 * grp);
       const float glast = sSc[2 * C + nc - 1];
+      fetch_rows(kf, qfb(min(cc + 2, nchunk - 1)) + KF);
+      __builtin_amdgcn_sched_barrier(0);
+      f4 ah[SB], al[SB];
+#pragma unroll
+      for (int bi = 0; bi < SB; ++bi) ah[bi] = st[bi] * glast, al[bi] = zero4();
+#pragma unroll
+      for (int s = 0; s < NTS; ++s)
+#pragma unroll
+        for (int bi = 0; bi < SB; ++bi)
+          if (r + 4 * bi < KB) mm_es(gf[bi][s], yb[s], ah[bi], al[bi]);
 #pragma unroll
       for (int bi = 0; bi < SB; ++bi) {
         const int b = r + 4 * bi;
         if (b < KB) {
-          f4 ah = st[bi] * glast, al = zero4();
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) {
-            Sp ub;
-            xb_read_split<BF, CP>(ub, sUd, col, 32 * s + 8 * grp);
-            mm_es(kt[bi][s], ub, ah, al);
-          }
-          st[bi] = ah + al;
+          st[bi] = ah[bi] + al[bi];
           xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
         }
       }
       lds_barrier();
+    };
+    // Pairs of steps, the first pair peeled, so that every path into the
+    // loop has issued the same memory operations in the same order (the
+    // memory-counter waits then stay exact); an odd last chunk runs after
+    // the loop.
+    int cc = 0;
+    if (nchunk >= 2) {
+      step(0, kA, gA, gB);
+      step(1, kB, gB, gA);
+      for (cc = 2; cc + 1 < nchunk; cc += 2) {
+        step(cc, kA, gA, gB);
+        step(cc + 1, kB, gB, gA);
+      }
     }
+    if (cc < nchunk) step(cc, kA, gA, gB);
 
 #pragma unroll
     for (int bi = 0; bi < SB; ++bi) {
@@ -787,171 +927,136 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     }
   } else {
     // ============================================================ helper waves
-    // Everything off the recurrence: fetch chunk c+1 while chunk c runs and
-    // stage it in the other LDS buffers, and compute and store the output
-    // O = gamma (Q S^T) + R Y of token block r.
+    // Everything off the recurrence, for token block r: Z = Q S^T, the
+    // output O = gamma Z + R Y, and the staging of V slices and scalars two
+    // chunks ahead.  Both products are formed transposed (the operands swap
+    // roles, same registers), so that each lane holds four consecutive values
+    // of one output row and stores them at once.  Q and R fragments are
+    // loaded two chunks ahead into registers.
     const int ht = tid - 256;  // 0..255
-    // per-lane byte offsets relative to a chunk's first token row
-    uint32_t koff[NKP];
-#pragma unroll
-    for (int it = 0; it < NKP; ++it) {
-      const int x = ht + 256 * it;
-      koff[it] = x < C * PER_ROW ? uint32_t(((x / PER_ROW) * kstride + (x % PER_ROW) * E16) * ESZ) : 0x80000000u;
-    }
-    uint32_t ooff[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ooff[e] = uint32_t(((16 * r + 4 * grp + e) * vstride + col) * ESZ);
-    const uint32_t kq_tail = uint32_t(DK * ESZ), v_tail = uint32_t(16 * ESZ);
+    constexpr int NVP = int(Lds::VBUF / 16);      // 16-byte pieces of a chunk's V slice
+    constexpr int NSP = int(Lds::SCBUF / 16);      // and of its scalars
+    constexpr int NST = (NVP + NSP + 255) / 256;   // pieces per helper lane
+    const uint32_t ooff = uint32_t(((16 * r + col) * vstride + 4 * grp) * ESZ);
+    const uint32_t v_tail = uint32_t(16 * ESZ);
 
-    // Staged inputs (K tile, V slice, T' fragments, scalars) are fetched two
-    // chunks ahead into registers and written to LDS one chunk ahead, so the
-    // loads have a whole chunk to land; the Q and R fragments of the next
-    // chunk stay in registers.  Loads are spread over the three windows so
-    // that no window waits behind a full memory queue.
-    struct Staged {
-      uint4 kp[NKP];  // K rows, 16-byte pieces
-      uint4 vt[NVT];  // V slice, T' fragments and scalars, 16-byte pieces
-    };
-    struct Frags {
-      E aq[NKS];   // Q rows of block r (A fragments, stored in that order by the prep kernel)
-      Sp rf[NTF];  // R fragments of block r
-    };
-    auto fetch_k = [&](Staged& P, int cc) {
-      const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
-      const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t((nc - 1) * kstride * ESZ) + kq_tail);
-#pragma unroll
-      for (int it = 0; it < NKP; ++it) P.kp[it] = bload16(rk, koff[it]);
-    };
-    auto fetch_vt = [&](Staged& P, int cc) {
+    auto fetch_stg = [&](u32x4 (&P)[NST], int cc) __attribute__((always_inline)) {
       // one plain load per piece, its address chosen per lane: V rows past
       // the chunk's end are clamped to its last row (those tokens are masked
       // where V is used)
       const int t0 = chunk_t0(cc), nc = chunk_nc(cc);
       const IO* vb = v + (size_t(t0) * h_v + h) * d_v + dv0;
-      const uint8_t* wsb = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES;
+      const uint8_t* sc = wsb(cc) + Geo::SCAL_OFF;
       constexpr int PPT = 16 / E16;  // pieces per token row of the V slice
 #pragma unroll
-      for (int it = 0; it < NVT; ++it) {
-        const int x = min(ht + 256 * it, NVP + NTP + NSP - 1);
+      for (int it = 0; it < NST; ++it) {
+        const int x = min(ht + 256 * it, NVP + NSP - 1);
         const int tok = min(x / PPT, nc - 1);
-        const uint8_t* src = x < NVP ? reinterpret_cast<const uint8_t*>(vb + tok * vstride + (x % PPT) * E16)
-                           : x < NVP + NTP ? wsb + Geo::T_OFF + size_t(x - NVP) * 16
-                                           : wsb + Geo::SCAL_OFF + size_t(x - NVP - NTP) * 16;
-        P.vt[it] = *reinterpret_cast<const uint4*>(src);
+        const uint8_t* src = x < NVP ? reinterpret_cast<const uint8_t*>(vb + size_t(tok) * vstride + (x % PPT) * E16)
+                                     : sc + size_t(x - NVP) * 16;
+        P[it] = *reinterpret_cast<const u32x4*>(src);
       }
     };
-    auto fetch_qfrags = [&](Frags& F, int cc) {
-      const int rb = rowblk ? r : 0;
-      const uint8_t* qp = qf + (size_t(gc0 + cc) * h_qk + j) * qfrag_bytes(DK, C, BF) + lane * 16;
+    auto commit_stg = [&](const u32x4 (&P)[NST], int cc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        if constexpr (BF) {
-          F.aq[s] = *reinterpret_cast<const uint4*>(qp + size_t(rb * NKS + s) * 1024);
-        } else {
-          F.aq[s].a = *reinterpret_cast<const f4*>(qp + size_t(rb * NKS + s) * 2048);
-          F.aq[s].b = *reinterpret_cast<const f4*>(qp + size_t(rb * NKS + s) * 2048 + 1024);
-        }
-      }
-    };
-    auto fetch_rfrags = [&](Frags& F, int cc) {
-      // every helper wave issues the same loads (a lane whose fragment is not
-      // needed reads one shared line instead)
-      const int rb = rowblk ? r : 0;
-      const uint8_t* rp = ws + (size_t(gc0 + cc) * h_v + h) * Geo::BYTES + Geo::R_OFF +
-                          size_t(frag_base(rb)) * 2 * Geo::PLANE;
-#pragma unroll
-      for (int s = 0; s < NTF; ++s) {
-        const bool need = rowblk && 2 * s <= r;
-        ld_split(F.rf[s], rp + (need ? s * 2 * Geo::PLANE + lane * 16 : 0), need ? Geo::PLANE : 0);
-      }
-    };
-    auto commit = [&](const Staged& P, int buf) {
-      IO* sK = reinterpret_cast<IO*>(smem + Lds::K_OFF);
-#pragma unroll
-      for (int it = 0; it < NKP; ++it) {
+      for (int it = 0; it < NST; ++it) {
         const int x = ht + 256 * it;
-        if (x < C * PER_ROW) *reinterpret_cast<uint4*>(sK + (x / PER_ROW) * KP + (x % PER_ROW) * E16) = P.kp[it];
-      }
-#pragma unroll
-      for (int it = 0; it < NVT; ++it) {
-        const int x = ht + 256 * it;
-        uint8_t* dst = x < NVP ? smem + Lds::V_OFF + size_t(x) * 16
-                     : x < NVP + NTP ? smem + Lds::T_OFF + size_t(x - NVP) * 16
-                                     : smem + Lds::SC_OFF + buf * Lds::SCBUF + size_t(x - NVP - NTP) * 16;
-        if (x < NVP + NTP + NSP) *reinterpret_cast<uint4*>(dst) = P.vt[it];
+        uint8_t* dst = x < NVP ? smem + Lds::V_OFF + (cc & 1) * Lds::VBUF + size_t(x) * 16
+                               : smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF + size_t(x - NVP) * 16;
+        if (x < NVP + NSP) *reinterpret_cast<u32x4*>(dst) = P[it];
       }
     };
 
-    // S_c = staged inputs of chunk c (in registers until committed), F = Q / R fragments
-    Staged SA, SB;
-    Frags F, Fn;
-    if (nchunk > 0) {
-      fetch_k(SA, 0);
-      fetch_vt(SA, 0);
-      fetch_qfrags(F, 0);
-      fetch_rfrags(F, 0);
-      fetch_k(SB, min(1, nchunk - 1));
-      fetch_vt(SB, min(1, nchunk - 1));
-      commit(SA, 0);
-    }
-    lds_barrier();  // chunk 0 staged, state written
-
-    auto step = [&](int cc, Staged& next, Staged& after) {
-      // next = chunk cc+1 (loaded, not yet committed); after = free, receives chunk cc+2
-      const int buf = cc & 1, nc = chunk_nc(cc);
-      const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + buf * Lds::SCBUF);
-
-      // (1) Z = Q S^T of block r (S is the chunk's initial state); K, V, T'
-      // and scalars of chunk cc+2, Q fragments of chunk cc+1
-      f4 z = zero4();
-      if (rowblk) {
-        f4 z1 = zero4();
+    // One loop per fragment count, so that each wave issues only the loads
+    // it needs and every path through a loop issues the same ones.
+    auto run = [&](auto nr_c) __attribute__((always_inline)) {
+      constexpr int NR = decltype(nr_c)::value;  // R fragments of block r (0: no token block)
+      constexpr int NRA = NR > 0 ? NR : 1;
+      auto fetch_r = [&](Sp (&d)[NRA], int cc) __attribute__((always_inline)) {
+        const uint8_t* p = wsb(cc) + Geo::R_OFF + size_t(frag_base(r)) * 2 * PL + lane * 16;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          E bs;
-          xb_read_single<BF, DKP>(bs, sS, col, 32 * s + 8 * grp);
-          if (s & 1) z1 = mma32(F.aq[s], bs, z1);
-          else z = mma32(F.aq[s], bs, z);
+        for (int s = 0; s < NR; ++s) ld_split(d[s], p + s * 2 * PL, int(PL));
+      };
+      E aqA[NKS], aqB[NKS];
+      Sp rA[NRA], rB[NRA];
+      // staged pieces (V slice and scalars) of one chunk, as native vectors so
+      // that the copies stay in registers
+      u32x4 s0[NST], s1[NST];
+      if (nchunk > 0) {
+        const int c1 = min(1, nchunk - 1);
+        fetch_stg(s0, 0);
+        fetch_stg(s1, c1);
+        if constexpr (NR > 0) {
+          fetch_rows(aqA, qfb(0));
+          fetch_rows(aqB, qfb(c1));
+          fetch_r(rA, 0);
         }
-        z = z + z1;
+        commit_stg(s0, 0);
+        commit_stg(s1, 1);
+        fetch_stg(s0, min(2, nchunk - 1));
       }
-      const int c2 = min(cc + 2, nchunk - 1), c1 = min(cc + 1, nchunk - 1);  // past the end: harmless refetch
-      fetch_k(after, c2);
-      fetch_vt(after, c2);
-      fetch_qfrags(Fn, c1);
-      lds_barrier();
+      lds_barrier();  // state written, chunks 0 and 1 staged
 
-      // (2) O = gamma Z + R Y for block r, stored straight from the D layout
-      if (rowblk) {
-        f4 oh, ol = zero4();
+      // aq, rf: fragments of chunk cc; stg: staged chunk cc+2.  rn and sn,
+      // the other sets, are loaded here with R of chunk cc+1 and the staged
+      // pieces of chunk cc+3, in the first window, where these waves wait.
+      auto step = [&](int cc, E (&aq)[NKS], Sp (&rf)[NRA], Sp (&rn)[NRA], u32x4 (&stg)[NST],
+                      u32x4 (&sn)[NST]) __attribute__((always_inline)) {
+        const int nc = chunk_nc(cc);
+        const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF);
+
+        // (1) Z^T = S Q^T for token block r (S is the chunk's initial state)
+        E bs[NKS];
+        if constexpr (NR > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oh[e] = sSc[2 * C + 16 * r + 4 * grp + e] * z[e];
+          for (int s = 0; s < NKS; ++s) xb_read_single<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
+          fetch_r(rn, min(cc + 1, nchunk - 1));
+        }
+        fetch_stg(sn, min(cc + 3, nchunk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        f4 z = zero4();
+        if constexpr (NR > 0) {
+          f4 z1 = zero4();
 #pragma unroll
-        for (int s = 0; s < NTF; ++s) {
-          if (2 * s <= r) {
-            Sp yb;
-            xb_read_split<BF, CP>(yb, sY, col, 32 * s + 8 * grp);
-            mm_ss(F.rf[s], yb, oh, ol);
+          for (int s = 0; s < NKS; ++s) {
+            if (s & 1) z1 = mma32(bs[s], aq[s], z1);
+            else z = mma32(bs[s], aq[s], z);
           }
+          z = z + z1;
+          fetch_rows(aq, qfb(min(cc + 2, nchunk - 1)));
         }
-        const f4 o = oh + ol;
-        const int t0 = chunk_t0(cc);
-        const Rsrc ro = make_rsrc(out + (size_t(t0) * h_v + h) * d_v + dv0, uint32_t((nc - 1) * vstride * ESZ) + v_tail);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bstore_el<IO>(ro, ooff[e], o[e]);
-      }
-      lds_barrier();
+        lds_barrier();
 
-      // (3) R fragments of chunk cc+1; stage chunk cc+1 in the LDS buffers
-      fetch_rfrags(Fn, c1);
-      commit(next, buf ^ 1);  // after the last chunk this fills buffers nobody reads
-      F = Fn;
-      lds_barrier();
+        // (2) O^T = Z^T diag(gamma) + Y^T R^T for token block r: lane holds
+        // values 4 grp .. + 3 of output row 16 r + col; stage chunk cc+2
+        if constexpr (NR > 0) {
+          Sp yb[NRA];
+#pragma unroll
+          for (int s = 0; s < NR; ++s) xb_read_split<BF, CP>(yb[s], sY, col, 32 * s + 8 * grp);
+          f4 oh = z * sSc[2 * C + 16 * r + col], ol = zero4();
+#pragma unroll
+          for (int s = 0; s < NR; ++s) mm_ss(yb[s], rf[s], oh, ol);
+          const Rsrc ro = make_rsrc(out + (size_t(chunk_t0(cc)) * h_v + h) * d_v + dv0,
+                                    uint32_t((nc - 1) * vstride * ESZ) + v_tail);
+          bstore4<IO>(ro, ooff, oh + ol);  // rows past the chunk's end are dropped
+        }
+        commit_stg(stg, cc + 2);  // after the last chunk this fills buffers nobody reads
+        lds_barrier();
+      };
+      int cc = 0;  // pairs of steps, the first pair peeled (as for the chain waves)
+      if (nchunk >= 2) {
+        step(0, aqA, rA, rB, s0, s1);
+        step(1, aqB, rB, rA, s1, s0);
+        for (cc = 2; cc + 1 < nchunk; cc += 2) {
+          step(cc, aqA, rA, rB, s0, s1);
+          step(cc + 1, aqB, rB, rA, s1, s0);
+        }
+      }
+      if (cc < nchunk) step(cc, aqA, rA, rB, s0, s1);
     };
-    for (int cc = 0; cc < nchunk; cc += 2) {
-      step(cc, SB, SA);
-      if (cc + 1 < nchunk) step(cc + 1, SA, SB);
-    }
+    if (!rowblk) run(std::integral_constant<int, 0>());
+    else if (NTF == 1 || r < 2) run(std::integral_constant<int, 1>());
+    else run(std::integral_constant<int, NTF>());
   }
 }
 
@@ -962,26 +1067,22 @@ size_t chunked_max_chunks(const Dims& d, int chunk) {
   return (size_t(d.total_tokens) + size_t(d.num_seqs) * size_t(chunk - 1)) / size_t(chunk);
 }
 
-static size_t chunk_bytes(bool bf16, int chunk) {
-  switch (chunk) {
-    case 16: return bf16 ? Geom<true, 16>::BYTES : Geom<false, 16>::BYTES;
-    case 32: return bf16 ? Geom<true, 32>::BYTES : Geom<false, 32>::BYTES;
-    case 64: return bf16 ? Geom<true, 64>::BYTES : Geom<false, 64>::BYTES;
-  }
-  return 0;
+static size_t chunk_bytes(const Dims& d, int chunk) {
+  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+  return chunk_block_bytes(d.bf16, d.d_k, chunk);
 }
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t table_bytes(const Dims& d, int chunk) { return round256(chunked_max_chunks(d, chunk) * 8); }
 
 static size_t blocks_bytes(const Dims& d, int chunk) {
-  return chunked_max_chunks(d, chunk) * size_t(d.h_v) * chunk_bytes(d.bf16, chunk);
+  return chunked_max_chunks(d, chunk) * size_t(d.h_v) * chunk_bytes(d, chunk);
 }
 
 size_t chunked_workspace_bytes(const Dims& d, int chunk) {
-  if (chunk_bytes(d.bf16, chunk) == 0) return 0;
+  if (chunk_bytes(d, chunk) == 0) return 0;
   return table_bytes(d, chunk) + blocks_bytes(d, chunk) +
-         chunked_max_chunks(d, chunk) * size_t(d.h_qk) * qfrag_bytes(d.d_k, chunk, d.bf16);
+         chunked_max_chunks(d, chunk) * size_t(d.h_qk) * qk_frag_bytes(d.d_k, chunk, d.bf16);
 }
 
 template <typename IO, int DK, int C>
@@ -1026,9 +1127,8 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   }
   Prof prof("chunk_sweep", st);
   hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
-                     d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(q),
-                     static_cast<const IO*>(k), static_cast<const IO*>(v), cu, ws, qf, s_in,
-                     static_cast<IO*>(out), s_out);
+                     d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(v), cu, ws, qf,
+                     s_in, static_cast<IO*>(out), s_out);
   return hipGetLastError();
 }
 

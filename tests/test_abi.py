@@ -48,24 +48,25 @@ def shape(**kw):
 
 def expected_workspace(n, t, h_v, c, bf16=True, h_qk=16, dk=128):
     """The per-slot (first token, length) table, padded to 256 bytes, then
-    per (slot, value head), for (T + N (C - 1)) / C slots: the
-    16-row x 32-column fragments of the lower triangles of T' and R (1, 2 or
-    6 per matrix for C = 16, 32, 64), each one 1 KiB plane per 8 values per
-    lane (T' rounded once to bf16: 1 plane; R split, or fp32: 2 planes), and
-    4 C scalars; then per (slot, query/key head) Q as fragments: C / 16 row
-    blocks x max(d_k, 32) / 32 slabs, one 1 KiB plane each (two in fp32)."""
+    per (slot, value head), for (T + N (C - 1)) / C slots: G = K^T diag(dec) T
+    as d_k / 16 row blocks x max(C, 32) / 32 token slabs (one 1 KiB plane
+    each, two in fp32), the 16-row x 32-column fragments of the lower
+    triangle of R = QKm T (1, 2 or 6 for C = 16, 32, 64; split into two 1 KiB
+    planes each) and 3 C fp32 scalars, padded to 256 bytes; then per (slot,
+    query/key head) Q and K as C / 16 row blocks x max(d_k, 32) / 32 slabs."""
     r256 = lambda x: (x + 255) // 256 * 256
     max_chunks = (t + n * (c - 1)) // c
     nf = {16: 1, 32: 2, 64: 6}[c]
-    per = nf * (1 if bf16 else 2) * 1024 + nf * 2 * 1024 + 4 * c * 4
-    qfrag = (c // 16) * (max(dk, 32) // 32) * (1 if bf16 else 2) * 1024
-    return r256(8 * max_chunks) + max_chunks * h_v * per + max_chunks * h_qk * qfrag
+    tpl = 1 if bf16 else 2
+    per = r256((dk // 16) * (max(c, 32) // 32) * tpl * 1024 + nf * 2 * 1024 + 3 * c * 4)
+    qk = 2 * (c // 16) * (max(dk, 32) // 32) * tpl * 1024
+    return r256(8 * max_chunks) + max_chunks * h_v * per + max_chunks * h_qk * qk
 
 
 def test_workspace_size(lib):
     s = shape()
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64) == expected_workspace(1, 4096, 32, 64)
-    assert expected_workspace(1, 4096, 32, 64) == 512 + 64 * 32 * 19456 + 64 * 16 * 16384
+    assert expected_workspace(1, 4096, 32, 64) == 512 + 64 * 32 * 29440 + 64 * 16 * 32768
     s32 = shape(io_dtype=gdn.GDN_DTYPE_F32)
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s32), 64) == expected_workspace(1, 4096, 32, 64, False)
     assert lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 48) == 0
