@@ -62,14 +62,17 @@ def prefill_flops(t, hv=HV, hqk=HQK, dk=DK, dv=DV, c=CHUNK):
 
 
 def kernel_bytes(name, t, n_seqs, state_in):
-    """Algorithmic HBM bytes of one launch: each input read once, each output
-    written once (bf16 activations, fp32 gate, beta and state)."""
+    """Algorithmic HBM bytes of one launch: each of the kernel's inputs from
+    the caller read once, each output written once (bf16 activations, fp32
+    gate, beta and state).  The prep kernel consumes q, k, g and beta; the
+    sweep consumes v (and the prep's per-chunk operands, which are not
+    algorithmic) and writes o and the state."""
     qk = t * 2 * HQK * DK * 2
     vo = t * HV * DV * 2
     gb = t * 2 * HV * 4
     st = n_seqs * HV * DV * DK * 4
     if name == "chunk_sweep":
-        return qk + 2 * vo + st * (2 if state_in else 1)
+        return 2 * vo + st * (2 if state_in else 1)
     if name == "chunk_prep":
         return qk + gb
     if name == "chunk_table":

@@ -13,9 +13,9 @@
 //   QKm_ri = exp(G_r - G_i) (q_r . k_i)       (i <= r)
 //   Y   = diag(beta) V - diag(beta gamma) (K S0^T)
 //   O   = diag(gamma) (Q S0^T) + R Y,          R = QKm T
-//   S1^T = gamma_{n-1} S0^T + G Y,              G = K^T diag(dec) T
+//   S1^T = gamma_{n-1} S0^T + P Y,              P = K^T diag(dec) T
 //
-// (T Y is the block's matrix of delta updates; folding T into R and G, which
+// (T Y is the block's matrix of delta updates; folding T into R and P, which
 // do not depend on the state, leaves two block products between one state
 // and the next: Y from S0, then S1 from Y.)  Decays are always formed as exp
 // of a non-positive difference of fp64 partial sums, so nothing overflows and
@@ -33,20 +33,20 @@
 //   2. chunk_prep_kernel, one workgroup per (chunk, value head), fully
 //      parallel: Gram products on MFMA, gate prefix sums, A, T = (I + A)^{-1}
 //      (16x16 diagonal blocks by forward substitution in registers,
-//      off-diagonal blocks by fp32 MFMA block products), R = QKm T, G, and the
+//      off-diagonal blocks by fp32 MFMA block products), R = QKm T, P, and the
 //      per-token scalars, written to the workspace as MFMA A fragments; the
 //      first value head of each query/key group also writes Q and K as
 //      fragments.
 //   3. chunk_sweep_kernel, one workgroup per (sequence, value head, 16 rows of
 //      the state): walks the chunks in order with its 16 x d_k slice of the
 //      fp32 state in MFMA accumulators.  State rows are independent given the
-//      block's G, so slices of one head never talk to each other.  Four
+//      block's P, so slices of one head never talk to each other.  Four
 //      waves run the recurrence (Y, then the state update); four others form
 //      the output and stage inputs ahead.
 //
 // All block products use 16x16x32 fragments (see gdn_common.hpp).  Precision:
 // bf16 inputs (K, Q, V) enter MFMA exactly.  Y and R are split into hi + lo
-// bf16 halves (as is diag(dec) T when G is formed); G and the state (in
+// bf16 halves (as is diag(dec) T when P is formed); P and the state (in
 // K S^T, Q S^T) enter rounded once to bf16: their error reaches the outputs
 // damped by the block decay and stays well below the output's own bf16
 // rounding.  Every product accumulates in
@@ -192,11 +192,11 @@ __host__ __device__ constexpr int dk_pad(int dk) { return dk < 32 ? 32 : dk; }
 __host__ __device__ constexpr int c_pad(int c) { return c < 32 ? 32 : c; }
 // fragments (r, s), s <= r / 2, of a lower-triangular C x C matrix
 __host__ __device__ constexpr int tri_frags(int c) { return c == 16 ? 1 : (c == 32 ? 2 : 6); }
-// Workspace block of one (chunk, value head): G = K^T diag(dec) T as d_k / 16
+// Workspace block of one (chunk, value head): P = K^T diag(dec) T as d_k / 16
 // row blocks x 32-token slabs (rounded once), R = QKm T as its
 // lower-triangular fragments (split), then beta, beta gamma and gamma per
 // token.
-__host__ __device__ constexpr size_t g_off(bool, int, int) { return 0; }
+__host__ __device__ constexpr size_t p_off(bool, int, int) { return 0; }
 __host__ __device__ constexpr size_t r_off(bool bf, int dk, int c) {
   return size_t(dk / 16) * (c_pad(c) / 32) * (bf ? 1 : 2) * 1024;
 }
@@ -207,17 +207,17 @@ __host__ __device__ constexpr size_t chunk_block_bytes(bool bf, int dk, int c) {
 // Block of one (chunk, query/key head): Q, then K, as A fragments (C / 16 row
 // blocks x d_k / 32 slabs), so that the sweep loads them as contiguous 1 KiB
 // rows.
-__host__ __device__ constexpr size_t k_frag_off(int dk, int c, bool bf) {
+__host__ __device__ constexpr size_t k_frap_off(int dk, int c, bool bf) {
   return size_t(c / 16) * (dk_pad(dk) / 32) * (bf ? 1 : 2) * 1024;
 }
-__host__ __device__ constexpr size_t qk_frag_bytes(int dk, int c, bool bf) { return 2 * k_frag_off(dk, c, bf); }
+__host__ __device__ constexpr size_t qk_frag_bytes(int dk, int c, bool bf) { return 2 * k_frap_off(dk, c, bf); }
 template <bool BF, int DK, int C>
 struct Geom {
   static constexpr int NB = C / 16;  // 16-token row blocks
   static constexpr int NF = tri_frags(C);
   static constexpr int TPL = BF ? 1 : 2;  // planes of a rounded-once fragment
   static constexpr size_t PLANE = 1024;
-  static constexpr size_t G_OFF = g_off(BF, DK, C);
+  static constexpr size_t P_OFF = p_off(BF, DK, C);
   static constexpr size_t R_OFF = r_off(BF, DK, C);
   static constexpr size_t SCAL_OFF = scal_off(BF, DK, C);
   static constexpr size_t BYTES = chunk_block_bytes(BF, DK, C);
@@ -263,8 +263,8 @@ struct PrepLds {
   static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);   // beta
   static constexpr size_t D_OFF = B_OFF + C * sizeof(float);    // dec
   static constexpr size_t BYTES = D_OFF + C * sizeof(float);
-  // at the end the whole region [0, U_BYTES) holds G^T in K's layout
-  static_assert(KQ_BYTES / 2 <= U_BYTES, "G tile fits the union");
+  // at the end the whole region [0, U_BYTES) holds P^T in K's layout
+  static_assert(KQ_BYTES / 2 <= U_BYTES, "P tile fits the union");
 };
 
 template <typename IO, int DK, int C>
@@ -386,8 +386,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int NW = 8;                      // waves per workgroup
   constexpr int NGP = (NBLK + NW - 1) / NW;  // Gram blocks per wave
-  constexpr int WPK = NW / KB;               // waves per 16-key block of G
-  constexpr int NRW = (NB + WPK - 1) / WPK;  // token blocks of G per wave
+  constexpr int WPK = NW / KB;               // waves per 16-key block of P
+  constexpr int NRW = (NB + WPK - 1) / WPK;  // token blocks of P per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   float* sQK = reinterpret_cast<float*>(smem + Lds::QK_OFF);
   float* sTt = sQK;                                         // after R: T'^T
   float* sT = reinterpret_cast<float*>(smem + Lds::T_OFF);
-  IO* sG = reinterpret_cast<IO*>(smem);  // at the end: G^T (tokens x keys) in K's layout
+  IO* sP = reinterpret_cast<IO*>(smem);  // at the end: P^T (tokens x keys) in K's layout
   double* sGb = reinterpret_cast<double*>(smem + Lds::GB_OFF);
   float* sGl = reinterpret_cast<float*>(smem + Lds::GL_OFF);
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // K^T operand of this wave's 16-key block of G (rows = keys, k = tokens),
+  // K^T operand of this wave's 16-key block of P (rows = keys, k = tokens),
   // re-read from global memory since the K tile is gone: one element per
   // load, rows past the chunk read as zero.  Issued here so that the loads
   // land during the off-diagonal rounds.
@@ -681,14 +681,14 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // G blocks (key block wkb, token block r) = sum_s K^T(wkb, slab s) T'(slab s, r),
+  // P blocks (key block wkb, token block r) = sum_s K^T(wkb, slab s) T'(slab s, r),
   // T' split into hi + lo halves: the B fragment of T' holds its column
   // 16 r + col, rows 32 s + 8 grp .. (slabs reaching the diagonal, s >= r / 2).
-  f4 gacc[NRW];
+  f4 pacc[NRW];
 #pragma unroll
   for (int ri = 0; ri < NRW; ++ri) {
     const int r = wave / KB + WPK * ri;
-    gacc[ri] = zero4();
+    pacc[ri] = zero4();
     if (r < NB) {
       f4 cl = zero4();
 #pragma unroll
@@ -705,36 +705,36 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
           Sp tb;
           if constexpr (BF) split_bf16x8(tv, tb.hi, tb.lo);
           else tb = tv;
-          mm_es(ktw[s], tb, gacc[ri], cl);
+          mm_es(ktw[s], tb, pacc[ri], cl);
         }
       }
-      gacc[ri] = gacc[ri] + cl;
+      pacc[ri] = pacc[ri] + cl;
     }
   }
-  lds_barrier();  // A, R and T are dead; the region becomes the G^T tile
+  lds_barrier();  // A, R and T are dead; the region becomes the P^T tile
 #pragma unroll
   for (int ri = 0; ri < NRW; ++ri) {
     const int r = wave / KB + WPK * ri;
-    if (r < NB) {  // D block: G rows = keys 16 wkb + 4 grp .., column = token 16 r + col
-      IO* dst = sG + (16 * r + col) * KP + 16 * wkb + 4 * grp;
-      if constexpr (BF) *reinterpret_cast<uint2*>(dst) = bf16x4(gacc[ri]);
-      else *reinterpret_cast<f4*>(dst) = gacc[ri];
+    if (r < NB) {  // D block: P rows = keys 16 wkb + 4 grp .., column = token 16 r + col
+      IO* dst = sP + (16 * r + col) * KP + 16 * wkb + 4 * grp;
+      if constexpr (BF) *reinterpret_cast<uint2*>(dst) = bf16x4(pacc[ri]);
+      else *reinterpret_cast<f4*>(dst) = pacc[ri];
     }
   }
   lds_barrier();
-  // G as A fragments (b, s): rows = keys 16 b .., k = tokens 32 s + 8 grp ..
+  // P as A fragments (b, s): rows = keys 16 b .., k = tokens 32 s + 8 grp ..
   // (tokens past C zero)
   for (int p = wave; p < KB * NTS; p += NW) {
     const int b = p / NTS, s = p % NTS;
     const bool live = 32 * s + 8 * grp < C;
-    uint8_t* dst = wsb + Geo::G_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
+    uint8_t* dst = wsb + Geo::P_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
     if constexpr (BF) {
-      const IO* src = sG + (32 * s + 8 * grp + col / 4) * KP + 16 * b + 4 * (col % 4);
+      const IO* src = sP + (32 * s + 8 * grp + col / 4) * KP + 16 * b + 4 * (col % 4);
       const uint2 lo = lds_tr16(src), hi = lds_tr16(src + 4 * KP);
       *reinterpret_cast<uint4*>(dst) = live ? uint4{lo.x, lo.y, hi.x, hi.y} : uint4{0u, 0u, 0u, 0u};
     } else {
       f8 t;
-      ld8col(t, sG + (32 * s + 8 * grp) * KP + 16 * b + col, KP);
+      ld8col(t, sP + (32 * s + 8 * grp) * KP + 16 * b + col, KP);
       *reinterpret_cast<f4*>(dst) = live ? t.a : zero4();
       *reinterpret_cast<f4*>(dst + Geo::PLANE) = live ? t.b : zero4();
     }
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   constexpr int NKS = DKP / 32, NTS = CP / 32;  // 32-wide slabs along d_k and along the chunk
   constexpr int SB = (KB + 3) / 4;              // state blocks per chain wave
   constexpr int NTF = (NB + 1) / 2;             // R fragments per row block, at most
-  constexpr size_t QKF = qk_frag_bytes(DK, C, BF), KF = k_frag_off(DK, C, BF);
+  constexpr size_t QKF = qk_frag_bytes(DK, C, BF), KF = k_frap_off(DK, C, BF);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* sS = smem + Lds::S_OFF;
   uint8_t* sY = smem + Lds::Y_OFF;
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   if (wave < 4) {
     // ============================================================ chain waves
     // The recurrence proper: per chunk X = K S^T and Y for token block r,
-    // then S^T <- gamma_last S^T + G Y for the owned state blocks.  K and G
+    // then S^T <- gamma_last S^T + P Y for the owned state blocks.  K and P
     // fragments are loaded two chunks ahead into registers.
     f4 st[SB];
 #pragma unroll
@@ -814,28 +814,28 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
       }
     }
-    auto fetch_g = [&](E (&gf)[SB][NTS], int cc) __attribute__((always_inline)) {
-      const uint8_t* p = wsb(cc) + Geo::G_OFF + lane * 16;
+    auto fetch_p = [&](E (&pf)[SB][NTS], int cc) __attribute__((always_inline)) {
+      const uint8_t* p = wsb(cc) + Geo::P_OFF + lane * 16;
 #pragma unroll
       for (int bi = 0; bi < SB; ++bi) {
         const int b = min(r + 4 * bi, KB - 1);  // a wave without this block loads a valid one and ignores it
 #pragma unroll
-        for (int s = 0; s < NTS; ++s) ld_e(gf[bi][s], p + size_t(b * NTS + s) * TPL * PL, int(PL));
+        for (int s = 0; s < NTS; ++s) ld_e(pf[bi][s], p + size_t(b * NTS + s) * TPL * PL, int(PL));
       }
     };
-    E kA[NKS], kB[NKS], gA[SB][NTS], gB[SB][NTS];
+    E kA[NKS], kB[NKS], pA[SB][NTS], pB[SB][NTS];
     if (nchunk > 0) {
       fetch_rows(kA, qfb(0) + KF);
       fetch_rows(kB, qfb(min(1, nchunk - 1)) + KF);
-      fetch_g(gA, 0);
+      fetch_p(pA, 0);
     }
     lds_barrier();  // state written, chunks 0 and 1 staged
 
-    // kf, gf: fragments of chunk cc; gn: the other G set, loaded here with
+    // kf, pf: fragments of chunk cc; pn: the other P set, loaded here with
     // chunk cc+1.  Each window issues its LDS reads first and its global
     // loads next, so that a load waiting for the memory queue overlaps the
     // LDS latency instead of delaying the barrier.
-    auto step = [&](int cc, E (&kf)[NKS], E (&gf)[SB][NTS], E (&gn)[SB][NTS]) __attribute__((always_inline)) {
+    auto step = [&](int cc, E (&kf)[NKS], E (&pf)[SB][NTS], E (&pn)[SB][NTS]) __attribute__((always_inline)) {
       const int nc = chunk_nc(cc);
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF);
 
@@ -854,7 +854,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
           vt = lds_tr16(sV + (16 * r + 4 * grp + col / 4) * 16 + 4 * (col % 4));
         }
       }
-      fetch_g(gn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
+      fetch_p(pn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
       __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the products
       if (rowblk) {
         f4 x = zero4(), x1 = zero4();
@@ -880,7 +880,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       }
       lds_barrier();
 
-      // (2) S^T <- gamma_last S^T + G Y for the owned state blocks
+      // (2) S^T <- gamma_last S^T + P Y for the owned state blocks
       Sp yb[NTS];
 #pragma unroll
       for (int s = 0; s < NTS; ++s) xb_read_split<BF, CP>(yb[s], sY, col, 32 * s + 8 * grp);
@@ -894,7 +894,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       for (int s = 0; s < NTS; ++s)
 #pragma unroll
         for (int bi = 0; bi < SB; ++bi)
-          if (r + 4 * bi < KB) mm_es(gf[bi][s], yb[s], ah[bi], al[bi]);
+          if (r + 4 * bi < KB) mm_es(pf[bi][s], yb[s], ah[bi], al[bi]);
 #pragma unroll
       for (int bi = 0; bi < SB; ++bi) {
         const int b = r + 4 * bi;
@@ -911,14 +911,14 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     // the loop.
     int cc = 0;
     if (nchunk >= 2) {
-      step(0, kA, gA, gB);
-      step(1, kB, gB, gA);
+      step(0, kA, pA, pB);
+      step(1, kB, pB, pA);
       for (cc = 2; cc + 1 < nchunk; cc += 2) {
-        step(cc, kA, gA, gB);
-        step(cc + 1, kB, gB, gA);
+        step(cc, kA, pA, pB);
+        step(cc + 1, kB, pB, pA);
       }
     }
-    if (cc < nchunk) step(cc, kA, gA, gB);
+    if (cc < nchunk) step(cc, kA, pA, pB);
 
 #pragma unroll
     for (int bi = 0; bi < SB; ++bi) {

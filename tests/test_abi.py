@@ -48,7 +48,7 @@ def shape(**kw):
 
 def expected_workspace(n, t, h_v, c, bf16=True, h_qk=16, dk=128):
     """The per-slot (first token, length) table, padded to 256 bytes, then
-    per (slot, value head), for (T + N (C - 1)) / C slots: G = K^T diag(dec) T
+    per (slot, value head), for (T + N (C - 1)) / C slots: P = K^T diag(dec) T
     as d_k / 16 row blocks x max(C, 32) / 32 token slabs (one 1 KiB plane
     each, two in fp32), the 16-row x 32-column fragments of the lower
     triangle of R = QKm T (1, 2 or 6 for C = 16, 32, 64; split into two 1 KiB
