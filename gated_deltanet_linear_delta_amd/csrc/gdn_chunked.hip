@@ -256,8 +256,15 @@ struct PrepLds {
   static constexpr int BP = 20;
   static constexpr size_t KQ_BYTES = 2 * size_t(CP) * KP * sizeof(IO);
   static constexpr size_t M_BYTES = size_t(NBLK) * 16 * BP * sizeof(float);
-  static constexpr size_t U_BYTES = KQ_BYTES > 3 * M_BYTES ? KQ_BYTES : 3 * M_BYTES;
+  // After R, T' = diag(dec) T is kept as the split B fragments of P's
+  // products (2 KiB each, as many as R has fragments): in QKm's space when it
+  // fits, else after T.
+  static constexpr size_t TF_BYTES = size_t(tri_frags(C)) * 2048;
+  static constexpr bool TF_IN_QK = TF_BYTES <= M_BYTES;
+  static constexpr size_t U_MIN = 3 * M_BYTES + (TF_IN_QK ? 0 : TF_BYTES);
+  static constexpr size_t U_BYTES = KQ_BYTES > U_MIN ? KQ_BYTES : U_MIN;
   static constexpr size_t A_OFF = 0, QK_OFF = M_BYTES, T_OFF = 2 * M_BYTES;
+  static constexpr size_t TF_OFF = TF_IN_QK ? QK_OFF : 3 * M_BYTES;
   static constexpr size_t GB_OFF = U_BYTES;           // fp64 prefix sum before each 16-token block
   static constexpr size_t GL_OFF = GB_OFF + 8 * 4;    // fp32 prefix sum within the token's block
   static constexpr size_t B_OFF = GL_OFF + C * sizeof(float);   // beta
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);  // after the Gram products
   float* sR = sA;                                           // after the inverse
   float* sQK = reinterpret_cast<float*>(smem + Lds::QK_OFF);
-  float* sTt = sQK;                                         // after R: T'^T
+  uint8_t* sTf = smem + Lds::TF_OFF;                        // after R: T' as split B fragments
   float* sT = reinterpret_cast<float*>(smem + Lds::T_OFF);
   IO* sP = reinterpret_cast<IO*>(smem);  // at the end: P^T (tokens x keys) in K's layout
   double* sGb = reinterpret_cast<double*>(smem + Lds::GB_OFF);
@@ -466,9 +473,10 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     *reinterpret_cast<uint4*>(sK + r * KP + c16) = kv;
     *reinterpret_cast<uint4*>(sQ + r * KP + c16) = qv;
   }
-  // Gate prefix sums in fp64: G_t = sum_{i<=t} g_i.  Kept as the sum before
-  // each 16-token block (fp64) plus the part within the block (fp32, small),
-  // so that every decay exp(G_r - G_i) is formed from a short fp32 argument.
+  // Gate prefix sums in fp64: G_t = sum_{i<=t} g_i.  Kept, in base 2 (times
+  // log2 e), as the sum before each 16-token block (fp64) plus the part within
+  // the block (fp32, small), so that every decay exp(G_r - G_i) is one exp2
+  // of a short fp32 argument.
   if (wave == 0) {
     double gl = 0.0;
     float bl = 0.f;
@@ -487,8 +495,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     if (lane < C) {
       const float gam = lane < nc ? fast_exp(float(gl)) : 0.f;
       const float dec = lane < nc ? fast_exp(float(glast - gl)) : 0.f;
-      if ((lane & 15) == 0) sGb[lane >> 4] = gb;
-      sGl[lane] = float(gl - gb);
+      if ((lane & 15) == 0) sGb[lane >> 4] = gb * 1.4426950408889634;
+      sGl[lane] = float((gl - gb) * 1.4426950408889634);
       sBeta[lane] = bl;
       sDec[lane] = dec;
       float* sc = reinterpret_cast<float*>(wsb + Geo::SCAL_OFF);
@@ -549,21 +557,34 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     }
   }
   lds_barrier();  // K and Q are dead; their space becomes A, QKm and T
+  // Scale the Gram blocks by their decays into A and QKm.  The lane's
+  // elements of block (r, i) are (4 grp + e, col), BP floats apart; only the
+  // diagonal blocks need the causal mask.
 #pragma unroll
   for (int n = 0; n < NGP; ++n) {
     const int pb = wave + NW * n;
     if (pb < NBLK) {
       const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
-      const float dblk = float(sGb[r] - sGb[i]);
+      float* pa = sA + pb * 16 * BP + 4 * grp * BP + col;
+      float* pq = sQK + pb * 16 * BP + 4 * grp * BP + col;
       const f4 glr = *reinterpret_cast<const f4*>(sGl + 16 * r + 4 * grp);
       const f4 btr = *reinterpret_cast<const f4*>(sBeta + 16 * r + 4 * grp);
-      const float glc = sGl[16 * i + col];
+      const float cb = float(sGb[r] - sGb[i]) - sGl[16 * i + col];  // base 2, with glr: <= 0 below the diagonal
+      if (i < r) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * r + 4 * grp + e, cl = 16 * i + col;
-        const float dcy = fast_exp(cl <= row ? dblk + glr[e] - glc : 0.f);
-        *lt(sA, row, cl) = cl < row ? btr[e] * dcy * gk[n][e] : 0.f;
-        *lt(sQK, row, cl) = cl <= row ? dcy * gq[n][e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float dcy = __builtin_amdgcn_exp2f(cb + glr[e]);
+          pa[e * BP] = btr[e] * dcy * gk[n][e];
+          pq[e * BP] = dcy * gq[n][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * grp + e;  // row within the block
+          const float dcy = __builtin_amdgcn_exp2f(col <= rr ? cb + glr[e] : 0.f);
+          pa[e * BP] = col < rr ? btr[e] * dcy * gk[n][e] : 0.f;
+          pq[e * BP] = col <= rr ? dcy * gq[n][e] : 0.f;
+        }
       }
     }
   }
@@ -573,15 +594,20 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   // rows congruent to s mod 4; each row is one quad reduction.
   if (wave < NB) {
     const int b = wave, c = lane >> 2, s = lane & 3;
+    // a[rr][m] = A(rr, 4 m + s) of the block; columns 4 m .. 4 m + 3 >= rr
+    // are zero (A is strictly lower triangular) and are neither read nor used
     float a[16][4];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[rr][m] = *lt(sA, 16 * b + rr, 16 * b + 4 * m + s);
+      for (int m = 0; m < 4; ++m) a[rr][m] = 4 * m < rr ? *lt(sA, 16 * b + rr, 16 * b + 4 * m + s) : 0.f;
     float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float part = a[rr][0] * t[0] + a[rr][1] * t[1] + a[rr][2] * t[2] + a[rr][3] * t[3];
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (4 * m < rr) part += a[rr][m] * t[m];
       const float val = (rr == c ? 1.f : 0.f) - sum_lanes4(part);
       if (s == (rr & 3)) t[rr >> 2] = val;
     }
@@ -598,12 +624,13 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   E ktw[NTS];
   {
     const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t(((nc - 1) * h_qk * DK + DK) * sizeof(IO)));
+    const uint32_t kst = uint32_t(h_qk * DK * sizeof(IO));  // bytes between tokens
 #pragma unroll
     for (int s = 0; s < NTS; ++s) {
+      const uint32_t voff = uint32_t(((32 * s + 8 * grp) * h_qk * DK + 16 * wkb + col) * sizeof(IO));
       IO e8[8];
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq)
-        e8[qq] = bload_el<IO>(rk, uint32_t(((32 * s + 8 * grp + qq) * h_qk * DK + 16 * wkb + col) * sizeof(IO)));
+      for (int qq = 0; qq < 8; ++qq) e8[qq] = bload_el<IO>(rk, voff + uint32_t(qq) * kst);
       if constexpr (BF) {
         ktw[s] = uint4{pack2(e8[0], e8[1]), pack2(e8[2], e8[3]), pack2(e8[4], e8[5]), pack2(e8[6], e8[7])};
       } else {
@@ -660,30 +687,50 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // R as split fragments.  T' = diag(dec) T transposed into QKm's space:
-  // block (jb, ib) of T' is stored in slot (jb, ib) with rows and columns
-  // exchanged, so that a column of T' reads as a row.
+  // R as split fragments.
   for (int p = wave; p < Geo::NF; p += NW) {
     int r, s;
     frag_rs(p, r, s);
     store_split(wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16,
                 tri_row8(sR, nullptr, 16 * r + col, 32 * s + 8 * grp));
   }
-  for (int pb = wave; pb < NBLK; pb += NW) {
-    const int jb = tri_row(pb), ib = pb - jb * (jb + 1) / 2;
-    f4 t;
+  // T' = diag(dec) T as the B operands of P's products, split once here:
+  // fragment (r, s), s >= r / 2, holds column 16 r + col of T' at rows
+  // 32 s + 8 grp .. + 7 (hi plane, then lo plane; fp32: rows + 0..3, then
+  // + 4..7).  Block (jb, ib) of T' fills half jb % 2 of fragment (ib, jb / 2);
+  // the halves above the diagonal (odd ib, jb = ib - 1) and past C (C = 16)
+  // are written as zeros.
+  auto tfrag = [&](int r, int s) { return (r < 2 ? r * NTS : 2 * NTS + (r - 2) * (NTS - 1)) + (s - r / 2); };
+  constexpr int NZB = NB / 2 + (NB == 1 ? 1 : 0);
+  for (int pb = wave; pb < NBLK + NZB; pb += NW) {
+    int jb, ib;
+    f4 t = zero4();
+    if (pb < NBLK) {
+      jb = tri_row(pb), ib = pb - jb * (jb + 1) / 2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int jr = 16 * jb + 4 * grp + e;
-      t[e] = sDec[jr] * *lt(sT, jr, 16 * ib + col);
+      for (int e = 0; e < 4; ++e) {
+        const int jr = 16 * jb + 4 * grp + e;
+        t[e] = sDec[jr] * *lt(sT, jr, 16 * ib + col);
+      }
+    } else {
+      ib = NB == 1 ? 0 : 2 * (pb - NBLK) + 1;
+      jb = NB == 1 ? 1 : ib - 1;
     }
-    *reinterpret_cast<f4*>(sTt + pb * 16 * BP + col * BP + 4 * grp) = t;
+    // lane 16 (2 (jb % 2) + grp / 2) + col of the fragment, its values 4 (grp % 2) ..
+    uint8_t* dst = sTf + tfrag(ib, jb / 2) * 2048 + ((2 * (jb & 1) + (grp >> 1)) * 16 + col) * 16;
+    if constexpr (BF) {
+      uint2 h, l;
+      split_bf16x4(t, h, l);
+      *reinterpret_cast<uint2*>(dst + 8 * (grp & 1)) = h;
+      *reinterpret_cast<uint2*>(dst + 1024 + 8 * (grp & 1)) = l;
+    } else {
+      *reinterpret_cast<f4*>(dst + 1024 * (grp & 1)) = t;
+    }
   }
   lds_barrier();
 
-  // P blocks (key block wkb, token block r) = sum_s K^T(wkb, slab s) T'(slab s, r),
-  // T' split into hi + lo halves: the B fragment of T' holds its column
-  // 16 r + col, rows 32 s + 8 grp .. (slabs reaching the diagonal, s >= r / 2).
+  // P blocks (key block wkb, token block r) = sum_s K^T(wkb, slab s) T'(slab s, r)
+  // over the slabs reaching the diagonal (s >= r / 2).
   f4 pacc[NRW];
 #pragma unroll
   for (int ri = 0; ri < NRW; ++ri) {
@@ -694,17 +741,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
 #pragma unroll
       for (int s = 0; s < NTS; ++s) {
         if (2 * s + 1 >= r) {
-          const int jb = 2 * s + (grp >> 1);  // token block of rows 32 s + 8 grp ..
-          f8 tv;
-          zero(tv);
-          if (jb >= r && jb < NB) {  // blocks above the diagonal and past C are zero
-            const float* src = sTt + (jb * (jb + 1) / 2 + r) * 16 * BP + col * BP + 8 * (grp & 1);
-            tv.a = *reinterpret_cast<const f4*>(src);
-            tv.b = *reinterpret_cast<const f4*>(src + 4);
-          }
           Sp tb;
-          if constexpr (BF) split_bf16x8(tv, tb.hi, tb.lo);
-          else tb = tv;
+          ld_split(tb, sTf + tfrag(r, s) * 2048 + lane * 16, 1024);
           mm_es(ktw[s], tb, pacc[ri], cl);
         }
       }
