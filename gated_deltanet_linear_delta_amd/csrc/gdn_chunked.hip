@@ -239,6 +239,31 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// fp64 lane data movement on the two 32-bit halves: a DPP move (lanes the
+// pattern leaves without a source, or rows outside ROWMASK, read 0) and a
+// read of one lane.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, ROWMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, ROWMASK, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l), __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within rows
+// of 16 lanes, then the last lane of row 0 (of row 2) is added to row 1 (row
+// 3), then the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ double wave_prefix_sum(double x) {
+  x += dpp_f64<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_f64<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_f64<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_f64<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_f64<0x143, 0xc>(x);  // row_bcast:31
+  return x;
+}
+
 
 template <typename IO, int DK, int C>
 struct PrepLds {
@@ -392,7 +417,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NKS = Lds::DKP / 32, KB = DK / 16, NTS = Lds::CP / 32;
   constexpr int NBLK = NB * (NB + 1) / 2;
   constexpr int NW = 8;                      // waves per workgroup
-  constexpr int NGP = (NBLK + NW - 1) / NW;  // Gram blocks per wave
+  constexpr int GW = NW - 1;                 // the gate wave; waves 0 .. GW-1 form the Gram blocks
+  constexpr int NGP = (NBLK + GW - 1) / GW;  // Gram blocks per wave
   constexpr int WPK = NW / KB;               // waves per 16-key block of P
   constexpr int NRW = (NB + WPK - 1) / WPK;  // token blocks of P per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -421,23 +447,16 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     const int rb = row >> 4, cb = c >> 4;
     return m + (rb * (rb + 1) / 2 + cb) * 16 * BP + (row & 15) * BP + (c & 15);
   };
-  // row `row`, columns k0 .. k0 + 7 of a stored lower-triangular matrix times
-  // per-column factors fc (zero above the diagonal and past C)
-  auto tri_row8 = [&](float* m, const float* fc, int row, int k0) {
+  // row `row`, columns k0 .. k0 + 7 of a stored lower block-triangular
+  // matrix whose diagonal blocks are exactly zero above the diagonal (R: the
+  // product of two such blocks); blocks above the diagonal and past C read
+  // as zero
+  auto row8 = [&](float* m, int row, int k0) {
     f8 x;
     zero(x);
     if (k0 < C && (k0 >> 4) <= (row >> 4)) {
       x.a = *reinterpret_cast<const f4*>(lt(m, row, k0));
       x.b = *reinterpret_cast<const f4*>(lt(m, row, k0 + 4));
-      if (fc) {
-        x.a = x.a * *reinterpret_cast<const f4*>(fc + k0);
-        x.b = x.b * *reinterpret_cast<const f4*>(fc + k0 + 4);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (k0 + e > row) x.a[e] = 0.f;
-      if (k0 + 4 + e > row) x.b[e] = 0.f;
     }
     return x;
   };
@@ -460,6 +479,12 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   };
   uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
 
+  // gate and beta of the chunk's tokens, for the gate wave (used after the barrier)
+  float g_ld = 0.f, b_ld = 0.f;
+  if (wave == GW && lane < nc) {
+    g_ld = g[size_t(t0 + lane) * h_v + h];
+    b_ld = beta[size_t(t0 + lane) * h_v + h];
+  }
   // K and Q rows of the chunk (rows >= nc and columns >= DK are zero)
   constexpr int PER_ROW = Lds::DKP / E16;
   for (int x = tid; x < Lds::CP * PER_ROW; x += 64 * NW) {
@@ -473,48 +498,41 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     *reinterpret_cast<uint4*>(sK + r * KP + c16) = kv;
     *reinterpret_cast<uint4*>(sQ + r * KP + c16) = qv;
   }
+  lds_barrier();
+
   // Gate prefix sums in fp64: G_t = sum_{i<=t} g_i.  Kept, in base 2 (times
   // log2 e), as the sum before each 16-token block (fp64) plus the part within
   // the block (fp32, small), so that every decay exp(G_r - G_i) is one exp2
-  // of a short fp32 argument.
-  if (wave == 0) {
-    double gl = 0.0;
-    float bl = 0.f;
-    if (lane < nc) {
-      gl = g[size_t(t0 + lane) * h_v + h];
-      bl = beta[size_t(t0 + lane) * h_v + h];
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(gl, off);
-      if (lane >= off) gl += y;
-    }
-    const double glast = __shfl(gl, nc - 1);
-    const double gbase = __shfl(gl, max((lane & ~15) - 1, 0));  // sum before the token's block
-    const double gb = lane >= 16 ? gbase : 0.0;
+  // of a short fp32 argument.  One wave computes them while the others form
+  // the Gram blocks.
+  if (wave == GW) {
+    const double gl = wave_prefix_sum(double(g_ld));
+    const double glast = readlane_f64(gl, nc - 1);
+    const int blk = lane >> 4;  // sum before the token's 16-token block: the scan at lane 16 blk - 1
+    const double s15 = readlane_f64(gl, 15), s31 = readlane_f64(gl, 31), s47 = readlane_f64(gl, 47);
+    const double gb = blk == 0 ? 0.0 : (blk == 1 ? s15 : (blk == 2 ? s31 : s47));
     if (lane < C) {
       const float gam = lane < nc ? fast_exp(float(gl)) : 0.f;
       const float dec = lane < nc ? fast_exp(float(glast - gl)) : 0.f;
-      if ((lane & 15) == 0) sGb[lane >> 4] = gb * 1.4426950408889634;
+      if ((lane & 15) == 0) sGb[blk] = gb * 1.4426950408889634;
       sGl[lane] = float((gl - gb) * 1.4426950408889634);
-      sBeta[lane] = bl;
+      sBeta[lane] = b_ld;
       sDec[lane] = dec;
       float* sc = reinterpret_cast<float*>(wsb + Geo::SCAL_OFF);
-      sc[lane] = bl;
-      sc[C + lane] = bl * gam;
+      sc[lane] = b_ld;
+      sc[C + lane] = b_ld * gam;
       sc[2 * C + lane] = gam;
     }
   }
-  lds_barrier();
 
-  // Gram blocks (r, i), i <= r, dealt round-robin to the waves: each wave
+  // Gram blocks (r, i), i <= r, dealt round-robin to waves 0 .. GW-1: each wave
   // computes K K^T (-> A) and Q K^T (-> QKm) of the same block, which share
   // the decays.  Products stay in registers until every wave is done with
   // the K and Q tiles.
   f4 gk[NGP], gq[NGP];
 #pragma unroll
   for (int n = 0; n < NGP; ++n) {
-    const int pb = wave + NW * n;
+    const int pb = wave < GW ? wave + GW * n : NBLK;
     gk[n] = zero4(), gq[n] = zero4();
     if (pb < NBLK) {
       const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   // diagonal blocks need the causal mask.
 #pragma unroll
   for (int n = 0; n < NGP; ++n) {
-    const int pb = wave + NW * n;
+    const int pb = wave < GW ? wave + GW * n : NBLK;
     if (pb < NBLK) {
       const int r = tri_row(pb), i = pb - r * (r + 1) / 2;
       float* pa = sA + pb * 16 * BP + 4 * grp * BP + col;
@@ -692,7 +710,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
     int r, s;
     frag_rs(p, r, s);
     store_split(wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16,
-                tri_row8(sR, nullptr, 16 * r + col, 32 * s + 8 * grp));
+                row8(sR, 16 * r + col, 32 * s + 8 * grp));
   }
   // T' = diag(dec) T as the B operands of P's products, split once here:
   // fragment (r, s), s >= r / 2, holds column 16 r + col of T' at rows
