@@ -574,6 +574,21 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
       }
     }
   }
+  // K^T operand of this wave's 16-key block of P (rows = keys, k = tokens),
+  // read by LDS transpose reads while the K tile is still there and kept in
+  // registers until P is formed
+  const int wkb = wave % KB;
+  E ktw[NTS];
+#pragma unroll
+  for (int s = 0; s < NTS; ++s) {
+    if constexpr (BF) {
+      const IO* src = sK + (32 * s + 8 * grp + col / 4) * KP + 16 * wkb + 4 * (col % 4);
+      const uint2 lo = lds_tr16(src), hi = lds_tr16(src + 4 * KP);
+      ktw[s] = uint4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      ld8col(ktw[s], sK + (32 * s + 8 * grp) * KP + 16 * wkb + col, KP);
+    }
+  }
   lds_barrier();  // K and Q are dead; their space becomes A, QKm and T
   // Scale the Gram blocks by their decays into A and QKm.  The lane's
   // elements of block (r, i) are (4 grp + e, col), BP floats apart; only the
@@ -634,29 +649,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
   lds_barrier();
 
-  // K^T operand of this wave's 16-key block of P (rows = keys, k = tokens),
-  // re-read from global memory since the K tile is gone: one element per
-  // load, rows past the chunk read as zero.  Issued here so that the loads
-  // land during the off-diagonal rounds.
-  const int wkb = wave % KB;
-  E ktw[NTS];
-  {
-    const Rsrc rk = make_rsrc(k + (size_t(t0) * h_qk + j) * DK, uint32_t(((nc - 1) * h_qk * DK + DK) * sizeof(IO)));
-    const uint32_t kst = uint32_t(h_qk * DK * sizeof(IO));  // bytes between tokens
-#pragma unroll
-    for (int s = 0; s < NTS; ++s) {
-      const uint32_t voff = uint32_t(((32 * s + 8 * grp) * h_qk * DK + 16 * wkb + col) * sizeof(IO));
-      IO e8[8];
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) e8[qq] = bload_el<IO>(rk, voff + uint32_t(qq) * kst);
-      if constexpr (BF) {
-        ktw[s] = uint4{pack2(e8[0], e8[1]), pack2(e8[2], e8[3]), pack2(e8[4], e8[5]), pack2(e8[6], e8[7])};
-      } else {
-        ktw[s].a = f4{e8[0], e8[1], e8[2], e8[3]};
-        ktw[s].b = f4{e8[4], e8[5], e8[6], e8[7]};
-      }
-    }
-  }
 
   // Off-diagonal blocks in two rounds, T being block lower triangular:
   //   T(i, i-1) = -T(i, i) A(i, i-1) T(i-1, i-1)             (i odd)
