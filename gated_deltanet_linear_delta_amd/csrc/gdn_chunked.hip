@@ -923,7 +923,12 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         }
         f4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = 16 * r + 4 * grp + e < nc ? bt[e] * vv[e] - bg[e] * x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) y[e] = bt[e] * vv[e] - bg[e] * x[e];
+        if (nc < C) {  // tokens past the end of a partial chunk
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * r + 4 * grp + e >= nc) y[e] = 0.f;
+        }
         xb_write_split<BF, CP>(sY, col, 16 * r + 4 * grp, y);
       }
       lds_barrier();
