@@ -5,7 +5,10 @@ cpu_baseline leg of bench.py, never by the library.
 """
 from .gdn_oracle import (  # noqa: F401
     gated_delta_chunk_form,
+    gated_delta_decode_fused,
     gated_delta_decode_step,
     gated_delta_recurrence,
     qk_head_of,
+    sigmoid,
+    softplus,
 )

@@ -36,8 +36,10 @@ gated delta rule, the plainest formula that fits that prose:
 per sequence and per value head, with S a [d_v, d_k] matrix (row index over
 d_v, column index over d_k).  With H_qk query/key heads shared by H_v value
 heads, value head h reads query/key head h // (H_v / H_qk) (contiguous
-groups).  No softplus, sigmoid, q/k normalisation or q scaling is applied
-here: those belong to the caller, and the inputs arrive already prepared.
+groups).  The prefill and decode functions apply no softplus, sigmoid, q/k
+normalisation or q scaling: those belong to the caller, and the inputs
+arrive already prepared.  gated_delta_decode_fused is the one exception: it
+takes raw inputs and applies those steps itself (readings in its docstring).
 
 Every input is widened exactly to fp64 (bf16 and fp32 values are exactly
 representable) and every step runs in fp64.
@@ -46,7 +48,10 @@ Parity status: each public function is pinned by ``tests/test_oracle.py``
 (brute force on the literal matrix form, exact rational arithmetic, the delta
 invariant, closed forms for pure decay / constancy / orthonormal keys, a
 hand-worked fixture in ``tests/golden/``, and agreement of the two forms
-below).  No function here is "parity unpinned".
+below).  The fused decode step is pinned by its own hand-worked fixture
+(three cases covering both norms, the gate and beta activations and both
+epsilons), closed forms of softplus and sigmoid, and its scale invariances.
+No function here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -58,6 +63,9 @@ __all__ = [
     "gated_delta_recurrence",
     "gated_delta_decode_step",
     "gated_delta_chunk_form",
+    "softplus",
+    "sigmoid",
+    "gated_delta_decode_fused",
 ]
 
 
@@ -160,6 +168,53 @@ def gated_delta_decode_step(q, k, v, g, beta, state):
     B = q.shape[0]
     cu = np.arange(B + 1, dtype=np.int64)
     return gated_delta_recurrence(q, k, v, g, beta, cu_seqlens=cu, state_in=state)
+
+
+def softplus(x):
+    """softplus(x) = log(1 + e^x) in fp64, evaluated as logaddexp(0, x)."""
+    return np.logaddexp(0.0, _as_f64(x))
+
+
+def sigmoid(x):
+    """sigmoid(x) = 1 / (1 + e^-x) in fp64, evaluated as exp(-softplus(-x))."""
+    return np.exp(-np.logaddexp(0.0, -_as_f64(x)))
+
+
+def gated_delta_decode_fused(q_raw, k_raw, v, g_raw, beta_raw, state, gate_bias=None, gate_scale=None,
+                             norm_weight=None, qk_eps=1e-6, norm_eps=1e-6):
+    """One decode step with the work on either side of the update folded in
+    (fp64).
+
+    Section "Reduce state and intermediate traffic" (es: "Reducir el tráfico
+    de estados y elementos intermedios") lists, among the chains the decode
+    path fuses so that no intermediate goes through memory, the preparation
+    of queries and keys and the recurrent update together with its
+    normalisation.  The pages name neither the preparation nor the norm; the
+    readings taken here are:
+
+      q = q_raw / sqrt(sum(q_raw^2) + qk_eps)          per (sequence, qk head), over d_k
+      k = k_raw / sqrt(sum(k_raw^2) + qk_eps)
+      g = -gate_scale[h] * softplus(g_raw + gate_bias[h])   (so alpha = exp(g) is in (0, 1])
+      beta = sigmoid(beta_raw)
+      o, S' = one step of the gated delta rule (gated_delta_decode_step)
+      out = o / sqrt(mean(o^2) + norm_eps) * norm_weight    per (sequence, v head), over d_v
+
+    gate_bias, gate_scale: [H_v] or None (zeros, ones); norm_weight: [d_v] or
+    None (ones).  Args otherwise as gated_delta_decode_step, with the raw
+    (pre-activation) q, k, g and beta.  Returns (out [B, H_v, d_v], new state).
+    """
+    q_raw, k_raw, v, g_raw, beta_raw = (_as_f64(a) for a in (q_raw, k_raw, v, g_raw, beta_raw))
+    h_v, d_v = v.shape[1], v.shape[2]
+    bias = np.zeros(h_v) if gate_bias is None else _as_f64(gate_bias)
+    scale = np.ones(h_v) if gate_scale is None else _as_f64(gate_scale)
+    w = np.ones(d_v) if norm_weight is None else _as_f64(norm_weight)
+    q = q_raw / np.sqrt(np.sum(q_raw * q_raw, axis=-1, keepdims=True) + qk_eps)
+    k = k_raw / np.sqrt(np.sum(k_raw * k_raw, axis=-1, keepdims=True) + qk_eps)
+    g = -scale[None, :] * softplus(g_raw + bias[None, :])
+    beta = sigmoid(beta_raw)
+    o, s_new = gated_delta_decode_step(q, k, v, g, beta, state)
+    out = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + norm_eps) * w
+    return out, s_new
 
 
 def gated_delta_chunk_form(q, k, v, g, beta, chunk_size, cu_seqlens=None, state_in=None):

@@ -18,8 +18,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (gated_delta_chunk_form, gated_delta_decode_step,
-                    gated_delta_recurrence, qk_head_of)
+from oracle import (gated_delta_chunk_form, gated_delta_decode_fused, gated_delta_decode_step,
+                    gated_delta_recurrence, qk_head_of, sigmoid, softplus)
 from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -357,4 +357,143 @@ def test_pins_catch_planted_mistakes(kind):
     o_ref, s_ref = literal_matrix_form(*args)
     o, s = fn(*args[:5], state_in=args[5])
     failures += not (rel(o, o_ref) < 1e-12 and rel(s, s_ref) < 1e-12)
+    assert failures >= 1
+
+
+# ---------------------------------------------------------------- fused decode step
+# The decode path fuses the preparation of queries and keys and the recurrent
+# update with its normalisation (section "Reduce state and intermediate
+# traffic"); gated_delta_decode_fused takes the raw inputs.  Pinned by a
+# hand-worked fixture, closed forms of the activations and scale invariances.
+def load_golden_cases(name):
+    """{case: {key: fp64 array}} from 'CASE.key = a, b, ...' lines; a value is
+    a fraction or ln(fraction)."""
+    cases = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rhs = (x.strip() for x in line.split("=", 1))
+            case, key = key.split(".", 1)
+            vals = []
+            for x in rhs.split(","):
+                x = x.strip()
+                vals.append(math.log(Fraction(x[3:-1])) if x.startswith("ln(") else float(Fraction(x)))
+            cases.setdefault(case, {})[key] = np.array(vals)
+    return cases
+
+
+def _run_fused_case(c, fn=gated_delta_decode_fused):
+    return fn(c["q_raw"].reshape(1, 1, 2), c["k_raw"].reshape(1, 1, 2), c["v"].reshape(1, 1, 2),
+              c["g_raw"].reshape(1, 1), c["b_raw"].reshape(1, 1), c["S0"].reshape(1, 1, 2, 2),
+              gate_bias=c["gate_bias"], gate_scale=c["gate_scale"], norm_weight=c["w"],
+              qk_eps=float(c["qk_eps"][0]), norm_eps=float(c["norm_eps"][0]))
+
+
+@pytest.mark.parametrize("case", ["A", "B", "C"])
+def test_golden_decode_fused(case):
+    c = load_golden_cases("hand_worked_decode_fused.txt")[case]
+    out, s1 = _run_fused_case(c)
+    np.testing.assert_allclose(out.reshape(-1), c["out"], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(s1.reshape(-1), c["S1"], rtol=1e-14, atol=1e-14)
+
+
+def test_activation_closed_forms():
+    # softplus(0) = ln 2, softplus(ln(e - 1)) = 1, softplus(x) - softplus(-x) = x
+    assert abs(softplus(0.0) - math.log(2.0)) < 1e-16
+    assert abs(softplus(math.log(math.e - 1.0)) - 1.0) < 1e-15
+    x = np.linspace(-40, 40, 81)
+    np.testing.assert_allclose(softplus(x) - softplus(-x), x, rtol=0, atol=1e-13)
+    assert softplus(800.0) == 800.0 and 0.0 < softplus(-700.0) < 1e-300 and softplus(-800.0) == 0.0
+    # sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1, no overflow at the ends
+    assert sigmoid(0.0) == 0.5
+    assert abs(sigmoid(math.log(3.0)) - 0.75) < 1e-15
+    np.testing.assert_allclose(sigmoid(x) + sigmoid(-x), 1.0, rtol=0, atol=1e-15)
+    assert sigmoid(800.0) == 1.0 and sigmoid(-800.0) == 0.0
+
+
+def _fused_problem(seed, B=3, h_qk=2, h_v=4, d_k=8, d_v=6):
+    rng = np.random.default_rng(seed)
+    return dict(q_raw=rng.normal(size=(B, h_qk, d_k)), k_raw=rng.normal(size=(B, h_qk, d_k)),
+                v=rng.normal(size=(B, h_v, d_v)), g_raw=rng.normal(size=(B, h_v)),
+                beta_raw=rng.normal(size=(B, h_v)), state=rng.normal(size=(B, h_v, d_v, d_k)),
+                gate_bias=rng.normal(size=h_v), gate_scale=rng.uniform(0.5, 2.0, size=h_v),
+                norm_weight=rng.normal(size=d_v))
+
+
+def test_fused_scale_invariances():
+    p = _fused_problem(0)
+    out, s = gated_delta_decode_fused(**p, qk_eps=0.0, norm_eps=0.0)
+    # q and k enter only through their directions
+    p2 = dict(p, q_raw=p["q_raw"] * 3.7, k_raw=p["k_raw"] * 0.21)
+    out2, s2 = gated_delta_decode_fused(**p2, qk_eps=0.0, norm_eps=0.0)
+    assert rel(out2, out) < 1e-13 and rel(s2, s) < 1e-13
+    # (v, state) -> c (v, state) scales the state by c and leaves the normalised output alone
+    p3 = dict(p, v=p["v"] * 5.0, state=p["state"] * 5.0)
+    out3, s3 = gated_delta_decode_fused(**p3, qk_eps=0.0, norm_eps=0.0)
+    assert rel(out3, out) < 1e-13 and rel(s3, 5.0 * s) < 1e-13
+    # the output's RMS over d_v is |norm_weight|'s when norm_eps = 0 and the weight is one
+    out4, _ = gated_delta_decode_fused(**dict(p, norm_weight=None), qk_eps=0.0, norm_eps=0.0)
+    np.testing.assert_allclose(np.mean(out4 ** 2, axis=-1), 1.0, rtol=1e-13)
+
+
+def test_fused_prepared_inputs_match_decode_step():
+    # With unit q, k, g_raw = softplus^-1(-g) and beta_raw = logit(beta), the
+    # fused step's state equals the plain step's, and its output is the plain
+    # output normalised.
+    p = _fused_problem(1)
+    q = p["q_raw"] / np.linalg.norm(p["q_raw"], axis=-1, keepdims=True)
+    k = p["k_raw"] / np.linalg.norm(p["k_raw"], axis=-1, keepdims=True)
+    g = -np.abs(p["g_raw"]) - 0.05
+    beta = 1.0 / (1.0 + np.exp(-p["beta_raw"]))
+    o, s = gated_delta_decode_step(q, k, p["v"], g, beta, p["state"])
+    g_raw = np.log(np.expm1(-g))  # softplus(g_raw) = -g
+    out, s_f = gated_delta_decode_fused(q, k, p["v"], g_raw, p["beta_raw"], p["state"], qk_eps=0.0, norm_eps=0.0)
+    assert rel(s_f, s) < 1e-13
+    assert rel(out, o / np.sqrt(np.mean(o ** 2, axis=-1, keepdims=True))) < 1e-13
+
+
+def _fused_mutant(kind):
+    """A copy of the fused step with one plausible mistake planted in it."""
+    def run(q_raw, k_raw, v, g_raw, beta_raw, state, gate_bias=None, gate_scale=None, norm_weight=None,
+            qk_eps=1e-6, norm_eps=1e-6):
+        h_v, d_v = v.shape[1], v.shape[2]
+        bias = np.zeros(h_v) if gate_bias is None else gate_bias
+        scale = np.ones(h_v) if gate_scale is None else gate_scale
+        w = np.ones(d_v) if norm_weight is None else norm_weight
+        nq = np.sum(q_raw * q_raw, axis=-1, keepdims=True) + qk_eps
+        nk = np.sum(k_raw * k_raw, axis=-1, keepdims=True) + qk_eps
+        q = q_raw / (nq if kind == "qk_no_sqrt" else np.sqrt(nq))
+        k = k_raw / np.sqrt(nk)
+        sp = np.logaddexp(0.0, g_raw + (0.0 if kind == "no_bias" else bias))
+        g = (scale * sp) if kind == "gate_sign" else -scale * sp
+        beta = np.logaddexp(0.0, beta_raw) if kind == "beta_softplus" else 1.0 / (1.0 + np.exp(-beta_raw))
+        o, s = gated_delta_decode_step(q, k, v, g, beta, state)
+        if kind == "norm_eps_outside":
+            out = o / (np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + norm_eps) * w
+        elif kind == "norm_over_heads":
+            out = o / np.sqrt(np.mean(o * o, axis=-2, keepdims=True) + norm_eps) * w
+        elif kind == "weight_before_norm":
+            ow = o * w
+            out = ow / np.sqrt(np.mean(ow * ow, axis=-1, keepdims=True) + norm_eps)
+        else:
+            out = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + norm_eps) * w
+        return out, s
+    return run
+
+
+@pytest.mark.parametrize("kind", ["qk_no_sqrt", "no_bias", "gate_sign", "beta_softplus", "norm_eps_outside",
+                                  "norm_over_heads", "weight_before_norm"])
+def test_fused_pins_catch_planted_mistakes(kind):
+    fn = _fused_mutant(kind)
+    cases = load_golden_cases("hand_worked_decode_fused.txt")
+    failures = 0
+    for c in cases.values():
+        out, s1 = _run_fused_case(c, fn)
+        failures += not (np.allclose(out.reshape(-1), c["out"]) and np.allclose(s1.reshape(-1), c["S1"]))
+    # the invariance pin with several heads
+    p = _fused_problem(0)
+    out, _ = fn(**dict(p, norm_weight=None), qk_eps=0.0, norm_eps=0.0)
+    failures += not np.allclose(np.mean(out ** 2, axis=-1), 1.0, rtol=1e-12)
     assert failures >= 1
