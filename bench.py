@@ -13,6 +13,10 @@ same JSON line also carries:
               eight state sets (512 MiB, twice the 256 MB Infinity Cache) so
               each step streams its state from HBM; timed by replaying a HIP
               graph of captured steps, and per kernel with HIP events;
+  decode_fused  gdn_decode_step_fused (q/k L2 norms, gate and beta
+              activations and the per-head RMS output norm in the decode
+              kernel) at the same two batches, beside the same step
+              unfused (torch prologue and epilogue around gdn_decode_step);
   scan        gdn_prefill_scan over the same 4096-token prompt (the
               direct-scan alternative, kept for the crossover);
   roofline    for the longest kernel of the chunked call: algorithmic bytes
@@ -214,6 +218,25 @@ def main():
         return
 
     # ------------------------------------------------------------ decode
+    def replay_us(step, steps_per_graph):
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(steps_per_graph):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(2, 2000 // steps_per_graph)
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t1) * 1e6 / (reps * steps_per_graph)
+
     def decode_leg(B, n_sets, steps_per_graph, seed):
         dec = make_decode(n_sets, B, HQK, HV, DK, DV, "bf16", 2.0 if B > 1 else 0.0, 0.02, seed=seed)
         dq, dk_, dv_ = io(dec.q), io(dec.k), io(dec.v)
@@ -237,23 +260,7 @@ def main():
         gdn.profile_enable(False)
         kern = mean_by_name(gdn.profile_collect())["decode"][0]
         # launch-free step time: replay a captured graph of steps
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(graph, stream=s):
-                for i in range(steps_per_graph):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        reps = max(2, 2000 // steps_per_graph)
-        t1 = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        us = (time.perf_counter() - t1) * 1e6 / (reps * steps_per_graph)
+        us = replay_us(step, steps_per_graph)
         nbytes = decode_bytes(B)
         return {
             "batch": B,
@@ -269,11 +276,74 @@ def main():
             "hbm_frac_event_timed": round(nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
 
+    def fused_leg(B, n_sets, steps_per_graph, seed):
+        """gdn_decode_step_fused from raw q/k/g/beta, and for comparison the same
+        step unfused: torch prologue (L2 norms, softplus, sigmoid), the plain
+        gdn_decode_step, torch RMS norm epilogue, each intermediate in memory."""
+        from gated_deltanet_linear_delta_amd.workloads import make_decode_raw
+        rng = np.random.default_rng(seed)
+        sets = [make_decode_raw(B, HQK, HV, DK, DV, "bf16", 0.02, rng=rng) for _ in range(n_sets)]
+        t = lambda x: torch.from_numpy(x).to(dev)
+        dq = [io(r.q_raw) for r in sets]
+        dk_ = [io(r.k_raw) for r in sets]
+        dv_ = [io(r.v) for r in sets]
+        dg = [t(r.g_raw) for r in sets]
+        db = [t(r.beta_raw) for r in sets]
+        states = [t(r.state).clone() for r in sets]
+        bias, scale, w = t(sets[0].gate_bias), t(sets[0].gate_scale), t(sets[0].norm_weight)
+        dout = torch.empty((B, HV, DV), dtype=torch.bfloat16, device=dev)
+        eps = 1e-6
+
+        def fused(i):
+            s = i % n_sets
+            gdn.decode_step_fused(dq[s], dk_[s], dv_[s], dg[s], db[s], states[s], gate_bias=bias, gate_scale=scale,
+                                  norm_weight=w, qk_eps=eps, norm_eps=eps, out=dout, state_out=states[s])
+
+        def unfused(i):
+            s = i % n_sets
+            qf, kf = dq[s].float(), dk_[s].float()
+            qn = (qf * torch.rsqrt((qf * qf).sum(-1, keepdim=True) + eps)).to(torch.bfloat16)
+            kn = (kf * torch.rsqrt((kf * kf).sum(-1, keepdim=True) + eps)).to(torch.bfloat16)
+            g = -scale * torch.nn.functional.softplus(dg[s] + bias)
+            beta = torch.sigmoid(db[s])
+            o, _ = gdn.decode_step(qn, kn, dv_[s], g, beta, states[s], state_out=states[s])
+            of = o.float()
+            dout.copy_(of * torch.rsqrt((of * of).mean(-1, keepdim=True) + eps) * w)
+
+        for i in range(2 * n_sets):
+            fused(i)
+            unfused(i)
+        torch.cuda.synchronize()
+        gdn.profile_enable(True)
+        for i in range(steps_per_graph):
+            fused(i)
+        torch.cuda.synchronize()
+        gdn.profile_enable(False)
+        kern = mean_by_name(gdn.profile_collect())["decode_fused"][0]
+        us = replay_us(fused, steps_per_graph)
+        us_unfused = replay_us(unfused, steps_per_graph)
+        nbytes = decode_bytes(B) + 2 * HV * 4 + DV * 4
+        return {
+            "batch": B,
+            "state_sets": n_sets,
+            "us_per_step_graph": round(us, 3),
+            "kernel_us": round(kern * 1e3, 3),
+            "tokens_per_s": round(B / (us * 1e-6), 1),
+            "bytes_per_step": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "unfused_us_per_step_graph": round(us_unfused, 3),
+            "fusion_speedup": round(us_unfused / us, 2),
+        }
+
     log("decode legs")
     dec_b1 = decode_leg(1, 1, 200, 1001)
     dec_b32 = decode_leg(32, 8, 64, 1004)
     log(f"decode B=1: {dec_b1}")
     log(f"decode B=32 cold: {dec_b32}")
+    fused_b1 = fused_leg(1, 1, 200, 2001)
+    fused_b32 = fused_leg(32, 8, 64, 2004)
+    log(f"fused decode B=1: {fused_b1}")
+    log(f"fused decode B=32 cold: {fused_b32}")
 
     # ------------------------------------------------------------ direct scan
     scan = None
@@ -342,6 +412,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
         "decode": {"b1_warm": dec_b1, "b32_cold": dec_b32},
+        "decode_fused": {"b1_warm": fused_b1, "b32_cold": fused_b32},
         "scan": scan,
         "cpu_baseline": cpu,
     }

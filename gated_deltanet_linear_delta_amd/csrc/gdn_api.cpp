@@ -227,4 +227,32 @@ gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d
                   what);
 }
 
+gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                                   gdn_dtype_t io_dtype, const void* q_raw, const void* k_raw, const void* v,
+                                   const float* g_raw, const float* beta_raw,
+                                   const gdn_decode_fused_params_t* params, const float* state_in, void* out,
+                                   float* state_out, void* stream) {
+  const char* what = "gdn_decode_step_fused";
+  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, io_dtype, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"q_raw", q_raw}, {"k_raw", k_raw}, {"v", v}, {"g_raw", g_raw}, {"beta_raw", beta_raw},
+                         {"state_in", state_in}, {"out", out}, {"state_out", state_out}});
+  if (st != GDN_OK) return st;
+  if (out == q_raw || out == k_raw || out == v || out == state_in || out == state_out)
+    return fail(GDN_ERR_INVALID, "%s: out aliases another tensor", what);
+  gdn_decode_fused_params_t p{nullptr, nullptr, nullptr, 1e-6f, 1e-6f};
+  if (params) p = *params;
+  for (const void* a : {static_cast<const void*>(p.gate_bias), static_cast<const void*>(p.gate_scale),
+                        static_cast<const void*>(p.norm_weight)})
+    if (a && (reinterpret_cast<uintptr_t>(a) & 3u) != 0)
+      return fail(GDN_ERR_INVALID, "%s: gate_bias, gate_scale and norm_weight must be 4-byte aligned", what);
+  if (!(p.qk_eps >= 0.f && p.qk_eps <= 3.0e38f) || !(p.norm_eps >= 0.f && p.norm_eps <= 3.0e38f))
+    return fail(GDN_ERR_INVALID, "%s: qk_eps and norm_eps must be finite and >= 0", what);
+  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, io_dtype == GDN_DTYPE_BF16};
+  return launched(gdn::launch_decode_fused(d, q_raw, k_raw, v, g_raw, beta_raw, p.gate_bias, p.gate_scale,
+                                           p.norm_weight, p.qk_eps, p.norm_eps, state_in, out, state_out,
+                                           static_cast<hipStream_t>(stream)),
+                  what);
+}
+
 }  // extern "C"

@@ -14,6 +14,8 @@
 // d_k / 8 lanes share a row, each holding 8 floats as two float4 at column
 // offsets 4*l and d_k/2 + 4*l, so every load instruction covers contiguous
 // 16*LPR-byte runs.  A workgroup holds 16 rows (16 * LPR threads).
+#include <type_traits>
+
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
 
@@ -99,6 +101,178 @@ __global__ __launch_bounds__(16 * (DK / 8)) void decode_kernel(
     __builtin_nontemporal_store(f4{s[4], s[5], s[6], s[7]}, reinterpret_cast<f4*>(so + c1));
     if (l == 0) io_traits<IO>::store(out + size_t(row0 + r), fmaf(alpha, rq, u * kq));
   }
+}
+
+// ---------------------------------------------------------------- fused step
+// The same step with the work on either side of it folded in (section
+// "Reduce state and intermediate traffic": the decode path fuses the
+// preparation of queries and keys, and the recurrent update with its
+// normalisation, so that no intermediate goes through memory):
+//   q = q_raw / sqrt(|q_raw|^2 + qk_eps),  k likewise        (fp32, not rounded)
+//   alpha = exp(-scale_h softplus(g_raw + bias_h)),  beta = sigmoid(beta_raw)
+//   o = S' q as above,  out = o / sqrt(mean_dv(o^2) + norm_eps) * w
+// The norm spans all d_v rows of a head, so a workgroup owns one (sequence,
+// head): d_v / RPL lane groups of LPR lanes, RPL rows each (rows rg,
+// rg + d_v / RPL, ...), at least one full wave.  The unnormalised o
+// goes through LDS; every wave then sums the squares in the same order, so
+// all of them derive the same scale without a second barrier.
+struct FusedArgs {
+  const float* gate_bias;   // [h_v] or null
+  const float* gate_scale;  // [h_v] or null
+  const float* norm_w;      // [d_v] or null
+  float qk_eps, norm_eps;
+};
+
+__device__ __forceinline__ float wave_sum64(float x) {
+  x = sum_lanes16(x);
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <typename IO, int DK, int RPL>
+__global__ __launch_bounds__(1024) void decode_fused_kernel(
+    int h_qk, int h_v, int d_v, const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ g_raw, const float* __restrict__ b_raw, FusedArgs fa, const float* s_in,
+    IO* __restrict__ out, float* s_out) {
+  constexpr int LPR = DK / 8;
+  __shared__ float so[128];
+  const int bh = blockIdx.x;  // b * h_v + h
+  const int h = bh % h_v;
+  const int b = bh / h_v;
+  const int j = h / (h_v / h_qk);
+  const int l = threadIdx.x % LPR;
+  const int rg = threadIdx.x / LPR;
+  const int ngrp = d_v / RPL;
+  const bool act = rg < ngrp;  // lane groups past the rows (blocks padded to a wave) only join the sum
+  const int c0 = 4 * l, c1 = DK / 2 + 4 * l;
+
+  f4 sa[RPL], sb[RPL];
+  int row[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    row[r] = min(rg, ngrp - 1) + r * ngrp;
+    const float* sr = s_in + (size_t(bh) * d_v + row[r]) * DK;
+    sa[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c0));
+    sb[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c1));
+  }
+  const IO* kp = k + (size_t(b) * h_qk + j) * DK;
+  const IO* qp = q + (size_t(b) * h_qk + j) * DK;
+  float kv[8], qv[8];
+  load4(kp + c0, kv);
+  load4(kp + c1, kv + 4);
+  load4(qp + c0, qv);
+  load4(qp + c1, qv + 4);
+  const float x = g_raw[bh] + (fa.gate_bias ? fa.gate_bias[h] : 0.f);
+  const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus; log1p(e^x) = x to fp32 precision past 20
+  const float alpha = expf(-(fa.gate_scale ? fa.gate_scale[h] : 1.f) * sp);
+  const float bt = 1.f / (1.f + expf(-b_raw[bh]));
+  float vi[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) vi[r] = io_traits<IO>::load(v + size_t(bh) * d_v + row[r]);
+
+  float kk0 = 0.f, kk1 = 0.f, qq0 = 0.f, qq1 = 0.f, kq0 = 0.f, kq1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kk0 = fmaf(kv[e], kv[e], kk0);
+    kk1 = fmaf(kv[e + 4], kv[e + 4], kk1);
+    qq0 = fmaf(qv[e], qv[e], qq0);
+    qq1 = fmaf(qv[e + 4], qv[e + 4], qq1);
+    kq0 = fmaf(kv[e], qv[e], kq0);
+    kq1 = fmaf(kv[e + 4], qv[e + 4], kq1);
+  }
+  const float rk = 1.f / sqrtf(sum_lanes<LPR>(kk0 + kk1) + fa.qk_eps);
+  const float rq = 1.f / sqrtf(sum_lanes<LPR>(qq0 + qq1) + fa.qk_eps);
+  const float kq = sum_lanes<LPR>(kq0 + kq1) * rk * rq;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kv[e] *= rk, qv[e] *= rq;
+
+  float o[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    float s[8] = {sa[r][0], sa[r][1], sa[r][2], sa[r][3], sb[r][0], sb[r][1], sb[r][2], sb[r][3]};
+    float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p0 = fmaf(s[e], kv[e], p0);
+      p1 = fmaf(s[e + 4], kv[e + 4], p1);
+      r0 = fmaf(s[e], qv[e], r0);
+      r1 = fmaf(s[e + 4], qv[e + 4], r1);
+    }
+    const float p = sum_lanes<LPR>(p0 + p1);
+    const float sq = sum_lanes<LPR>(r0 + r1);
+    const float u = bt * (vi[r] - alpha * p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], u * kv[e]);
+    if (act) {
+      float* so_row = s_out + (size_t(bh) * d_v + row[r]) * DK;
+      __builtin_nontemporal_store(f4{s[0], s[1], s[2], s[3]}, reinterpret_cast<f4*>(so_row + c0));
+      __builtin_nontemporal_store(f4{s[4], s[5], s[6], s[7]}, reinterpret_cast<f4*>(so_row + c1));
+    }
+    o[r] = fmaf(alpha, sq, u * kq);
+    if (act && l == 0) so[row[r]] = o[r];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  float ss = 0.f;
+  for (int i = lane; i < d_v; i += 64) ss = fmaf(so[i], so[i], ss);
+  const float scale = 1.f / sqrtf(wave_sum64(ss) / float(d_v) + fa.norm_eps);
+  if (act && l == 0) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      io_traits<IO>::store(out + size_t(bh) * d_v + row[r], o[r] * scale * (fa.norm_w ? fa.norm_w[row[r]] : 1.f));
+  }
+}
+
+template <typename IO, int DK>
+static hipError_t launch_decode_fused_t(const Dims& d, const void* q, const void* k, const void* v,
+                                        const float* g_raw, const float* b_raw, const FusedArgs& fa,
+                                        const float* s_in, void* out, float* s_out, hipStream_t st) {
+  const int blocks = d.num_seqs * d.h_v;
+  if (blocks == 0) return hipSuccess;
+  constexpr int LPR = DK / 8;
+  const int lanes = d.d_v * LPR;  // <= 16 d_k
+  Prof prof("decode_fused", st);
+  // At most MAXL lanes per workgroup (RPL = 1, 2, 4 or 8 rows per lane
+  // group), so that each lane keeps 2 RPL state loads in flight.
+  constexpr int MAXL = 512;
+  const int rpl = lanes <= MAXL ? 1 : lanes / MAXL;
+  auto go = [&](auto rc) {
+    constexpr int RPL = decltype(rc)::value;
+    hipLaunchKernelGGL((decode_fused_kernel<IO, DK, RPL>), dim3(blocks), dim3(lanes / RPL < 64 ? 64 : lanes / RPL),
+                       0, st, d.h_qk, d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
+                       static_cast<const IO*>(v), g_raw, b_raw, fa, s_in, static_cast<IO*>(out), s_out);
+    return hipGetLastError();
+  };
+  constexpr int RMAX = 16 * DK / MAXL;  // rows per lane group at d_v = 128
+  if constexpr (RMAX >= 8) if (rpl == 8) return go(std::integral_constant<int, 8>());
+  if constexpr (RMAX >= 4) if (rpl == 4) return go(std::integral_constant<int, 4>());
+  if constexpr (RMAX >= 2) if (rpl == 2) return go(std::integral_constant<int, 2>());
+  return go(std::integral_constant<int, 1>());
+}
+
+hipError_t launch_decode_fused(const Dims& d, const void* q, const void* k, const void* v, const float* g_raw,
+                               const float* b_raw, const float* gate_bias, const float* gate_scale,
+                               const float* norm_weight, float qk_eps, float norm_eps, const float* s_in,
+                               void* out, float* s_out, hipStream_t st) {
+  const FusedArgs fa{gate_bias, gate_scale, norm_weight, qk_eps, norm_eps};
+#define GDN_DECF(IO, DK) return launch_decode_fused_t<IO, DK>(d, q, k, v, g_raw, b_raw, fa, s_in, out, s_out, st)
+  if (d.bf16) {
+    switch (d.d_k) {
+      case 16: GDN_DECF(uint16_t, 16);
+      case 32: GDN_DECF(uint16_t, 32);
+      case 64: GDN_DECF(uint16_t, 64);
+      case 128: GDN_DECF(uint16_t, 128);
+    }
+  } else {
+    switch (d.d_k) {
+      case 16: GDN_DECF(float, 16);
+      case 32: GDN_DECF(float, 32);
+      case 64: GDN_DECF(float, 64);
+      case 128: GDN_DECF(float, 128);
+    }
+  }
+#undef GDN_DECF
+  return hipErrorInvalidValue;
 }
 
 // Large batches use 4 rows per lane group (more bytes in flight per wave);

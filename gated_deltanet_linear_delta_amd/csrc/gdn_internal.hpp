@@ -33,6 +33,14 @@ struct Dims {
 hipError_t launch_decode(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* s_in, void* out, float* s_out, hipStream_t st);
 
+// Decode with the q/k L2 norms, the gate and beta activations and the
+// per-head RMS output norm folded in; gate_bias, gate_scale and norm_weight
+// may be null.
+hipError_t launch_decode_fused(const Dims& d, const void* q, const void* k, const void* v, const float* g_raw,
+                               const float* b_raw, const float* gate_bias, const float* gate_scale,
+                               const float* norm_weight, float qk_eps, float norm_eps, const float* s_in,
+                               void* out, float* s_out, hipStream_t st);
+
 // Prefill by direct token scan.
 hipError_t launch_scan(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const int32_t* cu, const float* s_in, void* out, float* s_out,

@@ -20,13 +20,19 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace", "gdn_decode_step",
-           "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string", "gdn_last_error")
+           "gdn_decode_step_fused", "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string",
+           "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("h_qk", ctypes.c_int32),
                 ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int)]
+
+
+class GdnFusedParams(ctypes.Structure):
+    _fields_ = [("gate_bias", ctypes.c_void_p), ("gate_scale", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("qk_eps", ctypes.c_float), ("norm_eps", ctypes.c_float)]
 
 
 class GdnError(RuntimeError):
@@ -57,6 +63,9 @@ def load_library(path: str | None = None):
     lib.gdn_prefill_chunked_workspace.restype = ctypes.c_size_t
     lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f, f, vp, f, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f,
+                                          ctypes.POINTER(GdnFusedParams), f, vp, f, vp]
+    lib.gdn_decode_step_fused.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
@@ -208,6 +217,42 @@ def decode_step(q, k, v, g, beta, state_in, out=None, state_out=None, stream=Non
         _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
     _check(lib.gdn_decode_step(B, h_qk, h_v, d_k, d_v, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
+    return out, state_out
+
+
+def decode_step_fused(q_raw, k_raw, v, g_raw, beta_raw, state_in, gate_bias=None, gate_scale=None,
+                      norm_weight=None, qk_eps=1e-6, norm_eps=1e-6, out=None, state_out=None, stream=None):
+    """Decode step with the q/k L2 norms, the gate and beta activations and
+    the per-head RMS output norm in the same kernel (gdn_decode_step_fused).
+    q_raw, k_raw [B, h_qk, d_k]; v [B, h_v, d_v]; g_raw, beta_raw [B, h_v];
+    state_in [B, h_v, d_v, d_k]; gate_bias, gate_scale [h_v] and norm_weight
+    [d_v] fp32 or None.  Returns (out, state_out)."""
+    lib = load_library()
+    io = _io_dtype(q_raw)
+    B, h_qk, d_k = q_raw.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    _need(q_raw, "q_raw", q_raw.dtype, (B, h_qk, d_k))
+    _need(k_raw, "k_raw", q_raw.dtype, (B, h_qk, d_k))
+    _need(v, "v", q_raw.dtype, (B, h_v, d_v))
+    _need(g_raw, "g_raw", torch.float32, (B, h_v))
+    _need(beta_raw, "beta_raw", torch.float32, (B, h_v))
+    _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
+    for t, name, n in ((gate_bias, "gate_bias", h_v), (gate_scale, "gate_scale", h_v),
+                       (norm_weight, "norm_weight", d_v)):
+        if t is not None:
+            _need(t, name, torch.float32, (n,))
+    if out is None:
+        out = torch.empty((B, h_v, d_v), dtype=q_raw.dtype, device=q_raw.device)
+    else:
+        _need(out, "out", q_raw.dtype, (B, h_v, d_v))
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    else:
+        _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
+    params = GdnFusedParams(_ptr(gate_bias), _ptr(gate_scale), _ptr(norm_weight), float(qk_eps), float(norm_eps))
+    _check(lib.gdn_decode_step_fused(B, h_qk, h_v, d_k, d_v, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_raw),
+                                     _ptr(beta_raw), ctypes.byref(params), _ptr(state_in), _ptr(out),
+                                     _ptr(state_out), _stream(stream)))
     return out, state_out
 
 

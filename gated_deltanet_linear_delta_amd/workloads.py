@@ -25,7 +25,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Inputs", "DecodeInputs", "round_to_bf16", "make_prefill", "make_decode", "config"]
+__all__ = ["Inputs", "DecodeInputs", "RawDecodeInputs", "round_to_bf16", "make_prefill", "make_decode",
+           "make_decode_raw", "config"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -150,6 +151,48 @@ def make_decode(steps, batch, h_qk, h_v, d_k, d_v, io_dtype="bf16", gate_shift=0
     g, beta = _draw_gate(rng, (steps, batch, h_v), gate_shift)
     return DecodeInputs(q, k, v, g, beta, np.ascontiguousarray(state, dtype=np.float32), io_dtype,
                         dict(steps=steps, batch=batch, gate_shift=gate_shift, seed=seed))
+
+
+@dataclass
+class RawDecodeInputs:
+    """One decode step for B sequences with raw (unprepared) activations, for
+    the fused step: q_raw, k_raw [B, h_qk, d_k]; v [B, h_v, d_v]; g_raw,
+    beta_raw [B, h_v]; state [B, h_v, d_v, d_k]; per-head gate_bias and
+    gate_scale [h_v]; norm_weight [d_v]."""
+
+    q_raw: np.ndarray
+    k_raw: np.ndarray
+    v: np.ndarray
+    g_raw: np.ndarray
+    beta_raw: np.ndarray
+    state: np.ndarray
+    gate_bias: np.ndarray
+    gate_scale: np.ndarray
+    norm_weight: np.ndarray
+    io_dtype: str
+    meta: dict = field(default_factory=dict)
+
+
+def make_decode_raw(batch, h_qk, h_v, d_k, d_v, io_dtype="bf16", state_std=0.02, seed=0,
+                    rng=None) -> RawDecodeInputs:
+    """Draw one fused decode step.  Draw order: state (normal, standard
+    deviation ``state_std``), q_raw, k_raw, v (standard normal, rounded to the
+    io dtype, q and k NOT normalised), g_raw, beta_raw (standard normal),
+    gate_bias (normal, mean 2, sd 0.5), gate_scale (uniform [0.5, 1.5]),
+    norm_weight (normal, mean 1, sd 0.2).  All float32."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    f = np.float32
+    state = (rng.standard_normal((batch, h_v, d_v, d_k), dtype=f) * f(state_std)).astype(f)
+    q = _io(rng.standard_normal((batch, h_qk, d_k), dtype=f), io_dtype)
+    k = _io(rng.standard_normal((batch, h_qk, d_k), dtype=f), io_dtype)
+    v = _io(rng.standard_normal((batch, h_v, d_v), dtype=f), io_dtype)
+    g_raw = rng.standard_normal((batch, h_v), dtype=f)
+    beta_raw = rng.standard_normal((batch, h_v), dtype=f)
+    gate_bias = (2.0 + 0.5 * rng.standard_normal(h_v)).astype(f)
+    gate_scale = rng.uniform(0.5, 1.5, size=h_v).astype(f)
+    norm_weight = (1.0 + 0.2 * rng.standard_normal(d_v)).astype(f)
+    return RawDecodeInputs(q, k, v, g_raw, beta_raw, state, gate_bias, gate_scale, norm_weight, io_dtype,
+                           dict(batch=batch, seed=seed, state_std=state_std))
 
 
 def ragged_lengths(rng, n, lo=256, hi=8192):

@@ -15,9 +15,10 @@
  *     o_t = S_t q_t
  *
  * with S a d_v x d_k fp32 matrix.  Value head h reads query/key head
- * h / (h_v / h_qk) (contiguous groups).  The library applies no softplus,
- * sigmoid, normalisation or scaling to q, k, v, g or beta: callers pass g as
- * the log of the decay (finite, normally <= 0) and beta as the write strength.
+ * h / (h_v / h_qk) (contiguous groups).  Apart from gdn_decode_step_fused
+ * (below), the library applies no softplus, sigmoid, normalisation or scaling
+ * to q, k, v, g or beta: callers pass g as the log of the decay (finite,
+ * normally <= 0) and beta as the write strength.
  *
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers allocated and owned by the
@@ -131,6 +132,46 @@ gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d
                              const void* q, const void* k, const void* v,
                              const float* g, const float* beta,
                              const float* state_in, void* out, float* state_out, void* stream);
+
+/*
+ * Optional parts of the fused decode step.  The three pointers are DEVICE
+ * pointers (fp32, 4-byte aligned) or NULL; NULL selects the default noted.
+ */
+typedef struct {
+  const float* gate_bias;   /* [h_v], added to g_raw before softplus; NULL = zeros */
+  const float* gate_scale;  /* [h_v], multiplies the softplus;          NULL = ones  */
+  const float* norm_weight; /* [d_v], multiplies the normalised output; NULL = ones  */
+  float qk_eps;             /* finite, >= 0 */
+  float norm_eps;           /* finite, >= 0 */
+} gdn_decode_fused_params_t;
+
+/*
+ * One decode step with the work on either side of the recurrent update folded
+ * into the same kernel (section "Reduce state and intermediate traffic": the
+ * decode path fuses the preparation of queries and keys, and the recurrent
+ * update with its normalisation, so that no intermediate value goes through
+ * memory).  The pages name neither the preparation nor the norm; this call
+ * computes, per sequence b, value head h (query/key head j = h / (h_v / h_qk)):
+ *
+ *     q = q_raw / sqrt(sum(q_raw^2) + qk_eps)        over d_k, fp32, not rounded
+ *     k = k_raw / sqrt(sum(k_raw^2) + qk_eps)
+ *     g = -gate_scale[h] * softplus(g_raw + gate_bias[h]),   beta = sigmoid(beta_raw)
+ *     the gdn_decode_step update of state with q, k, v, g, beta, giving o
+ *     out = o / sqrt(mean(o^2) + norm_eps) * norm_weight     over d_v
+ *
+ * Tensors and layouts as gdn_decode_step: q_raw, k_raw [batch, h_qk, d_k] and
+ * v, out [batch, h_v, d_v] in io_dtype; g_raw, beta_raw [batch, h_v] fp32;
+ * state_in, state_out [batch, h_v, d_v, d_k] fp32 (state_out may equal
+ * state_in).  `params` is a HOST pointer read during the call, or NULL for
+ * {NULL, NULL, NULL, 1e-6, 1e-6}.  With qk_eps = 0 an all-zero q_raw or k_raw
+ * gives NaN, as does an all-zero output with norm_eps = 0.
+ */
+gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                                   gdn_dtype_t io_dtype,
+                                   const void* q_raw, const void* k_raw, const void* v,
+                                   const float* g_raw, const float* beta_raw,
+                                   const gdn_decode_fused_params_t* params,
+                                   const float* state_in, void* out, float* state_out, void* stream);
 
 /*
  * Kernel timing for benchmarks and profiling.  While enabled (process-wide),

@@ -132,3 +132,26 @@ def test_decode_rejects(lib):
     bad = list(p)
     bad[6] = p[5]  # out aliases state_in
     assert lib.gdn_decode_step(*ok, *bad, None) == 1
+
+
+def test_decode_fused_rejects(lib):
+    p = [FAKE + 256 * i for i in range(5)]  # q_raw, k_raw, v, g_raw, beta_raw
+    st_in, out, st_out = FAKE + 2048, FAKE + 2304, FAKE + 2560
+    ok = [1, 16, 32, 128, 128, gdn.GDN_DTYPE_BF16]
+    P = gdn.GdnFusedParams
+
+    def call(dims=ok, ptrs=p, params=None, s_in=st_in, o=out, s_out=st_out):
+        pr = ctypes.byref(params) if params is not None else None
+        return lib.gdn_decode_step_fused(*dims, *ptrs, pr, s_in, o, s_out, None)
+
+    assert call(dims=[0, 16, 32, 128, 128, 1]) == 1
+    assert call(dims=[1, 16, 24, 128, 128, 1]) == 1
+    assert call(dims=[1, 16, 32, 128, 96, 1]) == 2
+    assert call(ptrs=[p[0], None] + p[2:]) == 1          # k_raw missing
+    assert call(s_in=None) == 1                           # state_in is required
+    assert call(o=st_in) == 1                             # out aliases state_in
+    assert call(params=P(None, None, None, -1.0, 1e-6)) == 1
+    assert call(params=P(None, None, None, 1e-6, float("nan"))) == 1
+    assert call(params=P(None, None, None, 1e-6, float("inf"))) == 1
+    assert call(params=P(FAKE + 3072 + 2, None, None, 1e-6, 1e-6)) == 1  # misaligned gate_bias
+    assert "aligned" in lib.gdn_last_error().decode()
