@@ -19,6 +19,12 @@ same JSON line also carries:
               unfused (torch prologue and epilogue around gdn_decode_step);
   scan        gdn_prefill_scan over the same 4096-token prompt (the
               direct-scan alternative, kept for the crossover);
+  state_residency_ablation  the first 2048 tokens through the resident scan
+              and through gdn_prefill_scan_blockwise (state to memory and
+              back every 32 or 16 tokens), with the state bytes moved;
+  segmented_prefill  a 131072-token prompt (drawn on the device) chunked in
+              one call and through gdn_prefill_segmented in 8192- and
+              4096-token segments: time, workspace, and output equality;
   roofline    for the longest kernel of the chunked call: algorithmic bytes
               per launch over its mean duration, from HIP events that the
               library records on the launch stream while profiling is on;
@@ -138,6 +144,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 131072-token segmented-prefill leg")
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -366,6 +373,89 @@ def main():
                 "chunked_speedup": round(scan_wall / ms_step, 2)}
         log(f"direct scan: {scan}")
 
+    # ------------------------------------------------------------ state on chip vs blockwise
+    # The pages' ablation: a 2K-token prompt, the register-resident scan against
+    # a blockwise scan that moves the state through memory every block.
+    ablation = None
+    if not args.no_scan:
+        T2 = 2048
+        q2, k2, v2 = q[:T2], k[:T2], v[:T2]
+        g2, b2 = g[:T2].contiguous(), beta[:T2].contiguous()
+        cu2 = torch.tensor([0, T2], dtype=torch.int32, device=dev)
+        o2, s2 = torch.empty((T2, HV, DV), dtype=torch.bfloat16, device=dev), torch.empty_like(st)
+
+        def time_call(fn, n=5):
+            fn()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t3) * 1e3 / n
+
+        state_bytes = HV * DV * DK * 4
+        ablation = {"prompt_tokens": T2,
+                    "resident_ms": round(time_call(lambda: gdn.prefill_scan(q2, k2, v2, g2, b2, cu2, None, out=o2,
+                                                                             state_out=s2)), 4)}
+        for blk in (32, 16):
+            ms = time_call(lambda: gdn.prefill_scan_blockwise(q2, k2, v2, g2, b2, cu2, None, out=o2, state_out=s2,
+                                                              state_block=blk))
+            trips = (T2 - 1) // blk
+            ablation[f"blockwise_{blk}"] = {"ms": round(ms, 4), "state_round_trips": trips,
+                                            "state_mib_moved": round(trips * 2 * state_bytes / 2**20, 1),
+                                            "slowdown": round(ms / ablation["resident_ms"], 3)}
+        log(f"state residency ablation: {ablation}")
+
+    # ------------------------------------------------------------ bounded prompt segments
+    # One 131072-token prompt (the long workload's shape; inputs drawn on the
+    # device with the same distributions), chunked in one call with a
+    # whole-prompt workspace, and in segments with a per-segment workspace.
+    segmented = None
+    if not args.no_long:
+        TL = 131072
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1003)
+
+        def unit_bf16(shape):
+            x = torch.randn(shape, generator=gen, device=dev)
+            return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+        qL, kL = unit_bf16((TL, HQK, DK)), unit_bf16((TL, HQK, DK))
+        vL = torch.randn((TL, HV, DV), generator=gen, device=dev).to(torch.bfloat16)
+        bL = torch.sigmoid(torch.randn((TL, HV), generator=gen, device=dev))
+        gL = -torch.nn.functional.softplus(torch.randn((TL, HV), generator=gen, device=dev) + 2.0)
+        cuL = torch.tensor([0, TL], dtype=torch.int32, device=dev)
+        oL = torch.empty((TL, HV, DV), dtype=torch.bfloat16, device=dev)
+        sL = torch.empty_like(st)
+        full_ws = gdn.chunked_workspace_bytes(1, TL, HQK, HV, DK, DV, gdn.GDN_DTYPE_BF16, CHUNK)
+        wsL = gdn.alloc_workspace(full_ws, dev)
+
+        def timed(fn, n=5):
+            fn()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t3) * 1e3 / n
+
+        segmented = {"prompt_tokens": TL, "whole_prompt": {
+            "ms": round(timed(lambda: gdn.prefill_chunked(qL, kL, vL, gL, bL, cuL, None, out=oL, state_out=sL,
+                                                          chunk_size=CHUNK, workspace=wsL)), 3),
+            "workspace_mib": round(full_ws / 2**20, 1)}}
+        o_ref = oL.clone()
+        for L in (8192, 4096):
+            need = gdn.segmented_workspace_bytes(1, TL, HQK, HV, DK, DV, gdn.GDN_DTYPE_BF16, CHUNK, L)
+            ms = timed(lambda: gdn.prefill_segmented(qL, kL, vL, gL, bL, cuL, None, out=oL, state_out=sL,
+                                                     chunk_size=CHUNK, segment_tokens=L, workspace=wsL))
+            torch.cuda.synchronize()
+            segmented[f"segments_{L}"] = {"ms": round(ms, 3), "workspace_mib": round(need / 2**20, 1),
+                                          "output_equal": bool(torch.equal(oL, o_ref))}
+        segmented["tokens_per_s_whole"] = round(TL / (segmented["whole_prompt"]["ms"] * 1e-3), 1)
+        del qL, kL, vL, bL, gL, oL, wsL, o_ref
+        torch.cuda.empty_cache()
+        log(f"segmented long prompt: {segmented}")
+
     # ------------------------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -413,6 +503,8 @@ def main():
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
         "decode": {"b1_warm": dec_b1, "b32_cold": dec_b32},
         "decode_fused": {"b1_warm": fused_b1, "b32_cold": fused_b32},
+        "state_residency_ablation": ablation,
+        "segmented_prefill": segmented,
         "scan": scan,
         "cpu_baseline": cpu,
     }

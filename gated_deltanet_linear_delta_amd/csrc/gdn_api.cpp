@@ -79,11 +79,18 @@ gdn_status_t check_prefill(const gdn_shape_t* s, const void* q, const void* k, c
   if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
   gdn_status_t st = check_dims(s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, s->io_dtype, what);
   if (st != GDN_OK) return st;
-  st = check_ptrs(what, {{"q", q}, {"k", k}, {"v", v}, {"g", g}, {"beta", beta}, {"cu_seqlens", cu},
-                         {"out", out}, {"state_out", state_out}});
+  // with no tokens the per-token tensors are never read or written and may be NULL
+  if (s->total_tokens > 0) {
+    st = check_ptrs(what, {{"q", q}, {"k", k}, {"v", v}, {"g", g}, {"beta", beta}, {"out", out}});
+    if (st != GDN_OK) return st;
+  } else {
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(beta), out})
+      if (p && !aligned16(p)) return fail(GDN_ERR_INVALID, "%s: a token tensor is not 16-byte aligned", what);
+  }
+  st = check_ptrs(what, {{"cu_seqlens", cu}, {"state_out", state_out}});
   if (st != GDN_OK) return st;
   if (state_in && !aligned16(state_in)) return fail(GDN_ERR_INVALID, "%s: state_in is not 16-byte aligned", what);
-  if (out == q || out == k || out == v || out == state_in || out == state_out)
+  if (out && (out == q || out == k || out == v || out == state_in || out == state_out))
     return fail(GDN_ERR_INVALID, "%s: out aliases another tensor", what);
   return GDN_OK;
 }
@@ -178,6 +185,19 @@ gdn_status_t gdn_prefill_scan(const gdn_shape_t* shape, const void* q, const voi
                   "gdn_prefill_scan");
 }
 
+gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                        const float* g, const float* beta, const int32_t* cu_seqlens,
+                                        const float* state_in, void* out, float* state_out, int32_t state_block,
+                                        void* stream) {
+  const char* what = "gdn_prefill_scan_blockwise";
+  gdn_status_t st = check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, what);
+  if (st != GDN_OK) return st;
+  if (state_block < 1) return fail(GDN_ERR_INVALID, "%s: state_block must be >= 1 (got %d)", what, state_block);
+  return launched(gdn::launch_scan(dims_of(shape), q, k, v, g, beta, cu_seqlens, state_in, out, state_out,
+                                   static_cast<hipStream_t>(stream), state_block),
+                  what);
+}
+
 size_t gdn_prefill_chunked_workspace(const gdn_shape_t* shape, int32_t chunk_size) {
   if (!shape || (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)) return 0;
   if (check_dims(shape->num_seqs, shape->total_tokens, shape->h_qk, shape->h_v, shape->d_k, shape->d_v,
@@ -206,6 +226,47 @@ gdn_status_t gdn_prefill_chunked(const gdn_shape_t* shape, const void* q, const 
     return fail(GDN_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", what, workspace_bytes, need);
   return launched(gdn::launch_chunked(d, chunk_size, q, k, v, g, beta, cu_seqlens, state_in, out, state_out,
                                       workspace, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+size_t gdn_prefill_segmented_workspace(const gdn_shape_t* shape, int32_t chunk_size, int32_t segment_tokens) {
+  if (!shape || (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)) return 0;
+  if (segment_tokens < 1 || (chunk_size > 0 && segment_tokens % chunk_size != 0)) return 0;
+  if (check_dims(shape->num_seqs, shape->total_tokens, shape->h_qk, shape->h_v, shape->d_k, shape->d_v,
+                 shape->io_dtype, "gdn_prefill_segmented_workspace") != GDN_OK)
+    return 0;
+  return gdn::segmented_workspace_bytes(dims_of(shape), chunk_size, segment_tokens);
+}
+
+gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* state_in, void* out, float* state_out, int32_t chunk_size,
+                                   int32_t segment_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "gdn_prefill_segmented";
+  gdn_status_t st = check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, what);
+  if (st != GDN_OK) return st;
+  if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: chunk_size %d; supported are 0 (direct scan), 16, 32, 64", what,
+                chunk_size);
+  if (segment_tokens < 1) return fail(GDN_ERR_INVALID, "%s: segment_tokens must be >= 1", what);
+  if (chunk_size > 0 && segment_tokens % chunk_size != 0)
+    return fail(GDN_ERR_INVALID, "%s: segment_tokens (%d) must be a multiple of chunk_size (%d)", what,
+                segment_tokens, chunk_size);
+  const gdn::Dims d = dims_of(shape);
+  if (chunk_size > 0) {
+    gdn::Dims dw = d;
+    dw.total_tokens = d.total_tokens < segment_tokens ? d.total_tokens : segment_tokens;
+    if (gdn::chunked_max_chunks(dw, chunk_size) > size_t(1u << 31) - 1)
+      return fail(GDN_ERR_UNSUPPORTED, "%s: too many chunks per segment", what);
+  }
+  const size_t need = gdn::segmented_workspace_bytes(d, chunk_size, segment_tokens);
+  if (!workspace) return fail(GDN_ERR_INVALID, "%s: workspace is NULL", what);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GDN_ERR_INVALID, "%s: workspace is not 256-byte aligned", what);
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", what, workspace_bytes, need);
+  return launched(gdn::launch_segmented(d, chunk_size, segment_tokens, q, k, v, g, beta, cu_seqlens, state_in, out,
+                                        state_out, workspace, static_cast<hipStream_t>(stream)),
                   what);
 }
 

@@ -831,6 +831,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   int nchunk = (eos - bos + C - 1) / C;
   const int gc0 = first_slot(bos, n, C);
   nchunk = max(0, min(nchunk, max_chunks - gc0));  // malformed offsets cannot run past the workspace
+  if (nchunk == 0 && s_in == s_out) return;  // no tokens and the state already in place
   const int vstride = h_v * d_v;  // elements between consecutive tokens of v
   auto chunk_t0 = [&](int cc) { return bos + cc * C; };
   auto chunk_nc = [&](int cc) { return min(C, eos - chunk_t0(cc)); };

@@ -41,10 +41,11 @@ hipError_t launch_decode_fused(const Dims& d, const void* q, const void* k, cons
                                const float* norm_weight, float qk_eps, float norm_eps, const float* s_in,
                                void* out, float* s_out, hipStream_t st);
 
-// Prefill by direct token scan.
+// Prefill by direct token scan.  sblock > 0 builds the blockwise ablation:
+// the state goes to s_out and back every sblock tokens.
 hipError_t launch_scan(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const int32_t* cu, const float* s_in, void* out, float* s_out,
-                       hipStream_t st);
+                       hipStream_t st, int sblock = 0);
 
 // Chunked prefill: workspace layout and the three launches.
 size_t chunked_max_chunks(const Dims& d, int chunk);
@@ -52,5 +53,13 @@ size_t chunked_workspace_bytes(const Dims& d, int chunk);
 hipError_t launch_chunked(const Dims& d, int chunk, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, const int32_t* cu, const float* s_in, void* out,
                           float* s_out, void* workspace, hipStream_t st);
+
+// Prefill in windows of L packed tokens with the state carried through
+// s_out; chunk 0 selects the direct scan.  The workspace holds the window's
+// offsets and, for the chunked path, one window's chunked workspace.
+size_t segmented_workspace_bytes(const Dims& d, int chunk, int L);
+hipError_t launch_segmented(const Dims& d, int chunk, int L, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const int32_t* cu, const float* s_in, void* out,
+                            float* s_out, void* workspace, hipStream_t st);
 
 }  // namespace gdn

@@ -16,6 +16,13 @@
 // Token data (k, q, alpha, beta, k.q and the workgroup's 16 v values) is
 // staged in LDS in tiles of TT tokens; outputs are staged and written per
 // tile.
+//
+// The same section measures the alternative, a blockwise scan that keeps the
+// state in memory and moves it there and back every block, with the
+// cooperating threads meeting at barriers.  BLOCKWISE = true builds that
+// ablation: every `sblock` tokens each lane stores its state to s_out, the
+// workgroup meets at a barrier, and the lane reads the state back, so the
+// arithmetic and its rounding are those of the resident scan.
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
 
@@ -39,11 +46,11 @@ __device__ __forceinline__ void lds_load4(const IO* p, float* x) {
 }
 }  // namespace
 
-template <typename IO, int DK>
+template <typename IO, int DK, bool BLOCKWISE>
 __global__ __launch_bounds__(16 * (DK / 8)) void scan_kernel(
     int T, int h_qk, int h_v, int d_v, const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
-    const int32_t* __restrict__ cu, const float* s_in, IO* __restrict__ out, float* s_out) {
+    const int32_t* __restrict__ cu, const float* s_in, IO* __restrict__ out, float* s_out, int sblock) {
   constexpr int LPR = DK / 8;
   constexpr int NT = 16 * LPR;            // threads
   constexpr int E16 = 16 / sizeof(IO);    // io elements per 16 bytes
@@ -66,6 +73,10 @@ __global__ __launch_bounds__(16 * (DK / 8)) void scan_kernel(
   const int c0 = 4 * l, c1 = DK / 2 + 4 * l;
   const size_t srow = (size_t(nh) * d_v + i) * DK;
 
+  int bos, eos;
+  seq_range(cu, n, T, bos, eos);
+  if (bos == eos && s_in == s_out) return;  // no tokens and the state already in place
+
   float s[8];
   if (s_in) {
     f4 a = *reinterpret_cast<const f4*>(s_in + srow + c0);
@@ -77,8 +88,7 @@ __global__ __launch_bounds__(16 * (DK / 8)) void scan_kernel(
     for (int e = 0; e < 8; ++e) s[e] = 0.f;
   }
 
-  int bos, eos;
-  seq_range(cu, n, T, bos, eos);
+  int left = sblock;  // tokens before the next round trip through memory (blockwise only)
   for (int t0 = bos; t0 < eos; t0 += TT) {
     const int nt = min(TT, eos - t0);
     // ---- stage the tile
@@ -113,6 +123,19 @@ __global__ __launch_bounds__(16 * (DK / 8)) void scan_kernel(
     __syncthreads();
     // ---- walk the tile
     for (int r = 0; r < nt; ++r) {
+      if constexpr (BLOCKWISE) {
+        if (left == 0) {  // the same count in every lane: the barrier is uniform
+          *reinterpret_cast<f4*>(s_out + srow + c0) = f4{s[0], s[1], s[2], s[3]};
+          *reinterpret_cast<f4*>(s_out + srow + c1) = f4{s[4], s[5], s[6], s[7]};
+          __syncthreads();
+          const f4 a = *reinterpret_cast<const f4*>(s_out + srow + c0);
+          const f4 b = *reinterpret_cast<const f4*>(s_out + srow + c1);
+          s[0] = a[0]; s[1] = a[1]; s[2] = a[2]; s[3] = a[3];
+          s[4] = b[0]; s[5] = b[1]; s[6] = b[2]; s[7] = b[3];
+          left = sblock;
+        }
+        --left;
+      }
       float kv[8], qv[8];
       lds_load4(&sk[r][c0], kv);
       lds_load4(&sk[r][c1], kv + 4);
@@ -150,20 +173,27 @@ __global__ __launch_bounds__(16 * (DK / 8)) void scan_kernel(
 template <typename IO, int DK>
 static hipError_t launch_scan_t(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const int32_t* cu, const float* s_in, void* out,
-                                float* s_out, hipStream_t st) {
+                                float* s_out, int sblock, hipStream_t st) {
   const int blocks = d.num_seqs * d.h_v * (d.d_v / 16);
   if (blocks == 0) return hipSuccess;
-  Prof prof("scan", st);
-  hipLaunchKernelGGL((scan_kernel<IO, DK>), dim3(blocks), dim3(16 * (DK / 8)), 0, st, d.total_tokens, d.h_qk,
-                     d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
-                     static_cast<const IO*>(v), g, beta, cu, s_in, static_cast<IO*>(out), s_out);
+  if (sblock > 0) {
+    Prof prof("scan_blockwise", st);
+    hipLaunchKernelGGL((scan_kernel<IO, DK, true>), dim3(blocks), dim3(16 * (DK / 8)), 0, st, d.total_tokens,
+                       d.h_qk, d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
+                       static_cast<const IO*>(v), g, beta, cu, s_in, static_cast<IO*>(out), s_out, sblock);
+  } else {
+    Prof prof("scan", st);
+    hipLaunchKernelGGL((scan_kernel<IO, DK, false>), dim3(blocks), dim3(16 * (DK / 8)), 0, st, d.total_tokens,
+                       d.h_qk, d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
+                       static_cast<const IO*>(v), g, beta, cu, s_in, static_cast<IO*>(out), s_out, 0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const Dims& d, const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const int32_t* cu, const float* s_in, void* out, float* s_out,
-                       hipStream_t st) {
-#define GDN_SCAN(IO, DK) return launch_scan_t<IO, DK>(d, q, k, v, g, beta, cu, s_in, out, s_out, st)
+                       hipStream_t st, int sblock) {
+#define GDN_SCAN(IO, DK) return launch_scan_t<IO, DK>(d, q, k, v, g, beta, cu, s_in, out, s_out, sblock, st)
   if (d.bf16) {
     switch (d.d_k) {
       case 16: GDN_SCAN(uint16_t, 16);

@@ -19,9 +19,9 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 
 GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
-EXPORTS = ("gdn_prefill_scan", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace", "gdn_decode_step",
-           "gdn_decode_step_fused", "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string",
-           "gdn_last_error")
+EXPORTS = ("gdn_prefill_scan", "gdn_prefill_scan_blockwise", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace",
+           "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_decode_step", "gdn_decode_step_fused",
+           "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -59,6 +59,12 @@ def load_library(path: str | None = None):
     lib.gdn_prefill_scan.restype = ctypes.c_int
     lib.gdn_prefill_chunked.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, vp, ctypes.c_size_t, vp]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_scan_blockwise.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, vp]
+    lib.gdn_prefill_scan_blockwise.restype = ctypes.c_int
+    lib.gdn_prefill_segmented.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.gdn_prefill_segmented.restype = ctypes.c_int
+    lib.gdn_prefill_segmented_workspace.argtypes = [shp, i32, i32]
+    lib.gdn_prefill_segmented_workspace.restype = ctypes.c_size_t
     lib.gdn_prefill_chunked_workspace.argtypes = [shp, i32]
     lib.gdn_prefill_chunked_workspace.restype = ctypes.c_size_t
     lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f, f, vp, f, vp]
@@ -156,6 +162,20 @@ def prefill_scan(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_ou
     return out, state_out
 
 
+def prefill_scan_blockwise(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, state_block=32,
+                           stream=None):
+    """The blockwise-scan ablation (gdn_prefill_scan_blockwise): the direct
+    scan with its state moved to state_out and back every ``state_block``
+    tokens.  Returns (out, state_out)."""
+    lib = load_library()
+    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+    out, state_out = _outputs(shape, q, out, state_out)
+    _check(lib.gdn_prefill_scan_blockwise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                          int(state_block), _stream(stream)))
+    return out, state_out
+
+
 def chunked_workspace_bytes(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype=GDN_DTYPE_BF16, chunk_size=64):
     lib = load_library()
     shape = GdnShape(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype)
@@ -189,6 +209,34 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state
     _check(lib.gdn_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
                                    ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)), _stream(stream)))
+    return out, state_out
+
+
+def segmented_workspace_bytes(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype=GDN_DTYPE_BF16, chunk_size=64,
+                              segment_tokens=8192):
+    lib = load_library()
+    shape = GdnShape(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype)
+    return int(lib.gdn_prefill_segmented_workspace(ctypes.byref(shape), int(chunk_size), int(segment_tokens)))
+
+
+def prefill_segmented(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, chunk_size=64,
+                      segment_tokens=8192, workspace=None, stream=None):
+    """Prefill in windows of ``segment_tokens`` packed tokens with the state
+    carried between them (gdn_prefill_segmented); chunk_size 0 runs the
+    direct scan in each window.  Returns (out, state_out)."""
+    lib = load_library()
+    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+    out, state_out = _outputs(shape, q, out, state_out)
+    need = int(lib.gdn_prefill_segmented_workspace(ctypes.byref(shape), int(chunk_size), int(segment_tokens)))
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    wp, wn = _aligned_ptr(workspace)
+    _check(lib.gdn_prefill_segmented(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
+                                     int(segment_tokens), ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)),
+                                     _stream(stream)))
     return out, state_out
 
 

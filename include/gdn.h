@@ -33,7 +33,8 @@
  *                                          sequences allowed)
  *        state_in,
  *        state_out   [num_seqs, h_v, d_v, d_k]  fp32 (d_k fastest)
- *    Pointers must be 16-byte aligned.
+ *    Pointers must be 16-byte aligned.  When total_tokens is 0, q, k, v, g,
+ *    beta and out are not accessed and may be NULL.
  *  - state_in may be NULL (zero initial state).  state_out may be the same
  *    pointer as state_in (in place); no other output may alias any input.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -96,6 +97,25 @@ gdn_status_t gdn_prefill_scan(const gdn_shape_t* shape,
                               void* out, float* state_out, void* stream);
 
 /*
+ * The ablation of section "Keeping the recurrent state on chip": with
+ * register residency switched off the pages fall back to a blockwise scan,
+ * which moves the state through memory every block and stops the cooperating
+ * threads at barriers.  This is gdn_prefill_scan with the state's home in
+ * state_out: every state_block tokens of a sequence each lane stores its part
+ * of the state there, the workgroup meets at a barrier, and the lane reads it
+ * back.  The arithmetic is the resident scan's, so out and state_out equal
+ * gdn_prefill_scan's bit for bit; only the time differs.  Each round trip
+ * moves 2 * h_v * d_v * d_k * 4 bytes per sequence.  state_block >= 1.
+ */
+gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape,
+                                        const void* q, const void* k, const void* v,
+                                        const float* g, const float* beta,
+                                        const int32_t* cu_seqlens, const float* state_in,
+                                        void* out, float* state_out, int32_t state_block,
+                                        void* stream);
+
+/*
+ * Bytes of device workspace gdn_prefill_chunked needs for this shape and/*
  * Bytes of device workspace gdn_prefill_chunked needs for this shape and
  * chunk size (0 if the shape or chunk size is invalid).  The bound depends
  * only on num_seqs, total_tokens, h_v and chunk_size.
@@ -121,6 +141,39 @@ gdn_status_t gdn_prefill_chunked(const gdn_shape_t* shape,
                                  void* stream);
 
 /*
+ * Bytes of device workspace gdn_prefill_segmented needs (0 if an argument is
+ * invalid): the window's offsets, (num_seqs + 1) int32 rounded up to 256
+ * bytes, plus, for chunk_size > 0, gdn_prefill_chunked_workspace of a batch of
+ * min(total_tokens, segment_tokens) tokens.  It grows with segment_tokens,
+ * not with the prompt.
+ */
+size_t gdn_prefill_segmented_workspace(const gdn_shape_t* shape, int32_t chunk_size, int32_t segment_tokens);
+
+/*
+ * Prefill of a long packed batch in bounded segments (section "Bounding
+ * scratch memory by chunking the prompt": the prompt runs as a sequence of
+ * bounded segments, the recurrent state carries the context from one to the
+ * next, and the output does not change while peak scratch memory is set by
+ * the segment).  The packed tokens are cut into windows of segment_tokens;
+ * each sequence's tokens inside a window run through the chunked path
+ * (chunk_size 16, 32 or 64; segment_tokens a multiple of it) or the direct
+ * scan (chunk_size 0).  The state starts from state_in and passes from window
+ * to window through state_out, in place.  Same tensors as gdn_prefill_chunked.
+ * Results equal one gdn_prefill_chunked call up to rounding; for a single
+ * sequence (and for the scan in every case) they are bit for bit the same,
+ * because the windows then cut at chunk boundaries.  The workspace must be
+ * 256-byte aligned and at least gdn_prefill_segmented_workspace() bytes.
+ */
+gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape,
+                                   const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const int32_t* cu_seqlens, const float* state_in,
+                                   void* out, float* state_out,
+                                   int32_t chunk_size, int32_t segment_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent step for each of `batch` sequences (section "Decode: minimize/*
  * One recurrent step for each of `batch` sequences (section "Decode: minimize
  * bytes moved per token": one step per new token, bound by the bytes moved).
  * Tensors: q, k [batch, h_qk, d_k]; v, out [batch, h_v, d_v] (io_dtype);

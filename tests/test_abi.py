@@ -155,3 +155,61 @@ def test_decode_fused_rejects(lib):
     assert call(params=P(None, None, None, 1e-6, float("inf"))) == 1
     assert call(params=P(FAKE + 3072 + 2, None, None, 1e-6, 1e-6)) == 1  # misaligned gate_bias
     assert "aligned" in lib.gdn_last_error().decode()
+
+
+def test_segmented_workspace_size(lib):
+    s = shape(total_tokens=131072)
+    r256 = lambda x: (x + 255) // 256 * 256
+    # offsets for N + 1 sequences, then one window's chunked workspace
+    for L in (4096, 8192):
+        assert lib.gdn_prefill_segmented_workspace(ctypes.byref(s), 64, L) == r256(8) + expected_workspace(1, L, 32, 64)
+    assert lib.gdn_prefill_segmented_workspace(ctypes.byref(s), 0, 1000) == 256      # direct scan: offsets only
+    # a window never exceeds the prompt
+    assert lib.gdn_prefill_segmented_workspace(ctypes.byref(shape(total_tokens=100)), 64, 8192) == \
+        256 + expected_workspace(1, 100, 32, 64)
+    s2 = shape(num_seqs=32, total_tokens=73000)
+    assert lib.gdn_prefill_segmented_workspace(ctypes.byref(s2), 32, 8192) == r256(33 * 4) + \
+        expected_workspace(32, 8192, 32, 32)
+    # bounded: the segmented workspace at T = 131072 is a small fraction of the whole-prompt one
+    assert lib.gdn_prefill_segmented_workspace(ctypes.byref(s), 64, 8192) * 15 < \
+        lib.gdn_prefill_chunked_workspace(ctypes.byref(s), 64)
+    for c, L in ((64, 100), (48, 4096), (64, 0), (0, 0), (16, -16)):
+        assert lib.gdn_prefill_segmented_workspace(ctypes.byref(s), c, L) == 0
+    assert lib.gdn_prefill_segmented_workspace(None, 64, 4096) == 0
+
+
+def test_segmented_and_blockwise_reject(lib):
+    s = shape()
+    args = prefill_args(s)
+    need = lib.gdn_prefill_segmented_workspace(ctypes.byref(s), 64, 1024)
+    ws = FAKE + 4096
+    assert lib.gdn_prefill_segmented(*args, 48, 1024, ws, need, None) == 2
+    assert lib.gdn_prefill_segmented(*args, 64, 1000, ws, need, None) == 1     # not a multiple of the chunk
+    assert lib.gdn_prefill_segmented(*args, 64, 0, ws, need, None) == 1
+    assert lib.gdn_prefill_segmented(*args, 64, 1024, None, need, None) == 1
+    assert lib.gdn_prefill_segmented(*args, 64, 1024, ws + 16, need, None) == 1
+    assert lib.gdn_prefill_segmented(*args, 64, 1024, ws, need - 1, None) == 1
+    assert "needs" in lib.gdn_last_error().decode()
+    bad = prefill_args(shape(d_k=48))
+    assert lib.gdn_prefill_segmented(*bad, 64, 1024, ws, 1 << 40, None) == 2
+    assert lib.gdn_prefill_scan_blockwise(*args, 0, None) == 1
+    assert lib.gdn_prefill_scan_blockwise(*prefill_args(s, out=FAKE), 16, None) == 1  # out aliases q
+    assert lib.gdn_prefill_scan_blockwise(*bad, 16, None) == 2
+
+
+def test_empty_prompt_token_tensors_may_be_null(lib):
+    # T = 0: q, k, v, g, beta and out are never touched, so NULL passes validation;
+    # cu_seqlens and state_out are still required.  Only validation runs here: the
+    # calls below fail on a later check (workspace) or on purpose, before any launch.
+    s = shape(total_tokens=0)
+    nul = [ctypes.byref(s), None, None, None, None, None, FAKE, None, None, FAKE + 256]
+    assert lib.gdn_prefill_chunked(*nul, 64, None, 0, None) == 1
+    assert "workspace" in lib.gdn_last_error().decode()
+    nul_cu = list(nul)
+    nul_cu[6] = None
+    assert lib.gdn_prefill_chunked(*nul_cu, 64, FAKE + 4096, 1 << 40, None) == 1
+    assert "cu_seqlens" in lib.gdn_last_error().decode()
+    mis = list(nul)
+    mis[1] = FAKE + 8
+    assert lib.gdn_prefill_chunked(*mis, 64, FAKE + 4096, 1 << 40, None) == 1
+    assert "aligned" in lib.gdn_last_error().decode()
