@@ -115,7 +115,6 @@ gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape,
                                         void* stream);
 
 /*
- * Bytes of device workspace gdn_prefill_chunked needs for this shape and/*
  * Bytes of device workspace gdn_prefill_chunked needs for this shape and
  * chunk size (0 if the shape or chunk size is invalid).  The bound depends
  * only on num_seqs, total_tokens, h_v and chunk_size.
@@ -173,7 +172,6 @@ gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One recurrent step for each of `batch` sequences (section "Decode: minimize/*
  * One recurrent step for each of `batch` sequences (section "Decode: minimize
  * bytes moved per token": one step per new token, bound by the bytes moved).
  * Tensors: q, k [batch, h_qk, d_k]; v, out [batch, h_v, d_v] (io_dtype);
