@@ -22,6 +22,9 @@ same JSON line also carries:
   state_residency_ablation  the first 2048 tokens through the resident scan
               and through gdn_prefill_scan_blockwise (state to memory and
               back every 32 or 16 tokens), with the state bytes moved;
+  ragged_prefill  32 sequences with the ragged workload's lengths (about
+              73k tokens, drawn on the device) through the chunked path and
+              the scan: tokens/s, MFMA and HBM fractions;
   segmented_prefill  a 131072-token prompt (drawn on the device) chunked in
               one call and through gdn_prefill_segmented in 8192- and
               4096-token segments: time, workspace, and output equality;
@@ -144,7 +147,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
-    ap.add_argument("--no-long", action="store_true", help="skip the 131072-token segmented-prefill leg")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 131072-token segmented-prefill and the ragged-batch legs")
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -406,6 +410,61 @@ def main():
                                             "slowdown": round(ms / ablation["resident_ms"], 3)}
         log(f"state residency ablation: {ablation}")
 
+    # ------------------------------------------------------------ ragged batch
+    # 32 sequences with the ragged workload's lengths (log-uniform in [256,
+    # 8192], the same seeded draw), inputs drawn on the device with its
+    # distributions and a per-sequence N(0, 0.02) initial state: the regime
+    # where many sequences fill the chip.
+    ragged = None
+    if not args.no_long:
+        from gated_deltanet_linear_delta_amd.workloads import ragged_lengths
+        lengths = ragged_lengths(np.random.default_rng(1004), 32)
+        cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        TR, NR = int(cu_np[-1]), len(lengths)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1004)
+        unit = lambda x: (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        qR = unit(torch.randn((TR, HQK, DK), generator=gen, device=dev))
+        kR = unit(torch.randn((TR, HQK, DK), generator=gen, device=dev))
+        vR = torch.randn((TR, HV, DV), generator=gen, device=dev).to(torch.bfloat16)
+        bR = torch.sigmoid(torch.randn((TR, HV), generator=gen, device=dev))
+        gR = -torch.nn.functional.softplus(torch.randn((TR, HV), generator=gen, device=dev) + 2.0)
+        s0R = 0.02 * torch.randn((NR, HV, DV, DK), generator=gen, device=dev)
+        cuR = torch.from_numpy(cu_np).to(dev)
+        oR, sR = torch.empty((TR, HV, DV), dtype=torch.bfloat16, device=dev), torch.empty_like(s0R)
+        wsR = gdn.alloc_workspace(gdn.chunked_workspace_bytes(NR, TR, HQK, HV, DK, DV, gdn.GDN_DTYPE_BF16, CHUNK), dev)
+        chunked_call = lambda: gdn.prefill_chunked(qR, kR, vR, gR, bR, cuR, s0R, out=oR, state_out=sR,
+                                                   chunk_size=CHUNK, workspace=wsR)
+        for _ in range(3):
+            chunked_call()
+        torch.cuda.synchronize()
+        gdn.profile_enable(True)
+        n_r = 10
+        t3 = time.perf_counter()
+        for _ in range(n_r):
+            chunked_call()
+        torch.cuda.synchronize()
+        ms_r = (time.perf_counter() - t3) * 1e3 / n_r
+        gdn.profile_enable(False)
+        kr = {n_: round(m_ * 1e3, 2) for n_, (m_, _) in mean_by_name(gdn.profile_collect()).items()}
+        nbytes = TR * (2 * HQK * DK * 2 + 2 * HV * DV * 2 + 2 * HV * 4) + NR * HV * DV * DK * 4 * 2
+        ragged = {"sequences": NR, "tokens": TR, "chunked_ms": round(ms_r, 4),
+                  "tokens_per_s": round(TR / (ms_r * 1e-3), 1), "kernels_us": kr,
+                  "mfma_util": round(prefill_flops(TR) / (ms_r * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "algorithmic_bytes": nbytes,
+                  "hbm_frac": round(nbytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if not args.no_scan:
+            gdn.prefill_scan(qR, kR, vR, gR, bR, cuR, s0R, out=oR, state_out=sR)
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for _ in range(3):
+                gdn.prefill_scan(qR, kR, vR, gR, bR, cuR, s0R, out=oR, state_out=sR)
+            torch.cuda.synchronize()
+            ragged["scan_ms"] = round((time.perf_counter() - t3) * 1e3 / 3, 4)
+        del qR, kR, vR, bR, gR, s0R, oR, sR, wsR
+        torch.cuda.empty_cache()
+        log(f"ragged batch: {ragged}")
+
     # ------------------------------------------------------------ bounded prompt segments
     # One 131072-token prompt (the long workload's shape; inputs drawn on the
     # device with the same distributions), chunked in one call with a
@@ -505,6 +564,7 @@ def main():
         "decode_fused": {"b1_warm": fused_b1, "b32_cold": fused_b32},
         "state_residency_ablation": ablation,
         "segmented_prefill": segmented,
+        "ragged_prefill": ragged,
         "scan": scan,
         "cpu_baseline": cpu,
     }

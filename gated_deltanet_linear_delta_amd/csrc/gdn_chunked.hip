@@ -810,13 +810,18 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   uint8_t* sS = smem + Lds::S_OFF;
   uint8_t* sY = smem + Lds::Y_OFF;
 
-  // Workgroups are dealt to the 8 XCDs round-robin; give the 16-row slices of
-  // one head consecutive chain numbers on one XCD so they share its L2.
+  // Workgroups are dealt to the 8 XCDs round-robin (workgroup i to XCD i % 8).
+  // A unit is the h_v / h_qk value heads that share one query/key head, each
+  // in d_v / 16 row slices; units are dealt to the XCDs round-robin, so the
+  // chains of a unit share one L2 (the same Q and K, and each head's P and R),
+  // and every sequence's heads spread over all XCDs, which keeps a ragged
+  // batch's XCDs evenly loaded.
   const int ntile = d_v / 16;
-  const int nchain = N * h_v * ntile;
-  const int per = (nchain + 7) / 8;
-  const int L = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
-  if (L >= nchain) return;
+  const int U = (h_v / h_qk) * ntile;  // chains per unit
+  const int i_x = int(blockIdx.x >> 3);
+  const int unit = int(blockIdx.x & 7) + 8 * (i_x / U);
+  if (unit >= N * h_qk) return;
+  const int L = unit * U + i_x % U;
   const int tl = L % ntile, nh = L / ntile, h = nh % h_v, n = nh / h_v;
   const int j = h / (h_v / h_qk);
   const int dv0 = 16 * tl;
@@ -1170,9 +1175,10 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nchain = d.num_seqs * d.h_v * (d.d_v / 16);
-  if (nchain == 0) return hipSuccess;
-  const int per = (nchain + 7) / 8;
+  // eight XCDs, each dealt ceil(units / 8) units of U chains (see the kernel)
+  const int units = d.num_seqs * d.h_qk, U = (d.h_v / d.h_qk) * (d.d_v / 16);
+  if (units == 0) return hipSuccess;
+  const int per = (units + 7) / 8 * U;
   constexpr size_t lds = SweepLds<IO, DK, C>::BYTES;
   if (lds > 65536) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_sweep_kernel<IO, DK, C>),
