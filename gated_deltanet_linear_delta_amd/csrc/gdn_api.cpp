@@ -192,7 +192,8 @@ gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape, const void* q,
   const char* what = "gdn_prefill_scan_blockwise";
   gdn_status_t st = check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, what);
   if (st != GDN_OK) return st;
-  if (state_block < 1) return fail(GDN_ERR_INVALID, "%s: state_block must be >= 1 (got %d)", what, state_block);
+  if (state_block < 1 || state_block % 4 != 0)
+    return fail(GDN_ERR_INVALID, "%s: state_block must be a positive multiple of 4 (got %d)", what, state_block);
   return launched(gdn::launch_scan(dims_of(shape), q, k, v, g, beta, cu_seqlens, state_in, out, state_out,
                                    static_cast<hipStream_t>(stream), state_block),
                   what);

@@ -105,7 +105,8 @@ gdn_status_t gdn_prefill_scan(const gdn_shape_t* shape,
  * of the state there, the workgroup meets at a barrier, and the lane reads it
  * back.  The arithmetic is the resident scan's, so out and state_out equal
  * gdn_prefill_scan's bit for bit; only the time differs.  Each round trip
- * moves 2 * h_v * d_v * d_k * 4 bytes per sequence.  state_block >= 1.
+ * moves 2 * h_v * d_v * d_k * 4 bytes per sequence.  state_block must be a
+ * positive multiple of 4 (the scan walks tokens in blocks of 4).
  */
 gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape,
                                         const void* q, const void* k, const void* v,
@@ -158,9 +159,10 @@ size_t gdn_prefill_segmented_workspace(const gdn_shape_t* shape, int32_t chunk_s
  * (chunk_size 16, 32 or 64; segment_tokens a multiple of it) or the direct
  * scan (chunk_size 0).  The state starts from state_in and passes from window
  * to window through state_out, in place.  Same tensors as gdn_prefill_chunked.
- * Results equal one gdn_prefill_chunked call up to rounding; for a single
- * sequence (and for the scan in every case) they are bit for bit the same,
- * because the windows then cut at chunk boundaries.  The workspace must be
+ * Results equal one gdn_prefill_chunked (or gdn_prefill_scan) call up to
+ * rounding.  For a single sequence they are bit for bit the same when the
+ * windows cut at the boundaries of the blocks the path walks: always for the
+ * chunked path, and for the scan when segment_tokens is a multiple of 4.  The workspace must be
  * 256-byte aligned and at least gdn_prefill_segmented_workspace() bytes.
  */
 gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape,

@@ -193,6 +193,7 @@ def test_segmented_and_blockwise_reject(lib):
     bad = prefill_args(shape(d_k=48))
     assert lib.gdn_prefill_segmented(*bad, 64, 1024, ws, 1 << 40, None) == 2
     assert lib.gdn_prefill_scan_blockwise(*args, 0, None) == 1
+    assert lib.gdn_prefill_scan_blockwise(*args, 6, None) == 1      # not a multiple of 4
     assert lib.gdn_prefill_scan_blockwise(*prefill_args(s, out=FAKE), 16, None) == 1  # out aliases q
     assert lib.gdn_prefill_scan_blockwise(*bad, 16, None) == 2
 
