@@ -51,6 +51,9 @@ hand-worked fixture in ``tests/golden/``, and agreement of the two forms
 below).  The fused decode step is pinned by its own hand-worked fixture
 (three cases covering both norms, the gate and beta activations and both
 epsilons), closed forms of softplus and sigmoid, and its scale invariances.
+The grouped GEMM on 4-bit weights is pinned by a hand-worked fixture (which
+fixes the nibble order and the bf16 rounding of a rebuilt weight), a
+brute-force triple loop, closed forms and the definition of bf16 rounding.
 No function here is "parity unpinned".
 """
 
@@ -66,6 +69,9 @@ __all__ = [
     "softplus",
     "sigmoid",
     "gated_delta_decode_fused",
+    "round_bf16",
+    "dequantize_q4",
+    "grouped_gemm_q4",
 ]
 
 
@@ -266,3 +272,79 @@ def gated_delta_chunk_form(q, k, v, g, beta, chunk_size, cu_seqlens=None, state_
                 S = np.exp(G[-1]) * S + (np.exp(G[-1] - G)[:, None] * U).T @ Kc
             s_out[n, h] = S
     return o, s_out
+
+
+# ---------------------------------------------------------------- expert GEMM on 4-bit weights
+# Section "Dequantize the weights during the matrix multiplication" (es:
+# "Descuantificar los pesos durante la multiplicación de matrices"): each
+# expert weight is a 4-bit integer code, every group of 64 weights shares a
+# bf16 scale and a bf16 bias that reconstruct its values, the matrix unit
+# consumes bf16 operands, so the weights are rebuilt in bf16 before the
+# multiplication; accumulation is fp32 and the output bf16.  Section "Keep
+# expert routing on the GPU" says the activation rows routed to each expert
+# are stored together; a grouped GEMM multiplies each expert's rows by that
+# expert's matrix.  Readings taken: a weight is scale * code + bias with code
+# in 0..15 (affine); groups run along the contraction index k; codes are
+# packed two to a byte along k, the even k in the low nibble; the rebuilt
+# weight is rounded once to bf16 (nearest, ties to even).
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 value (ties to even), returned as fp64.
+    Values must be finite and exactly representable in fp32 (rounding
+    happens from the fp32 value, which the checks here hold exactly)."""
+    f = np.asarray(x, dtype=np.float64)
+    f32 = f.astype(np.float32)
+    if not np.array_equal(f32.astype(np.float64), f):
+        raise ValueError("round_bf16: value not exactly representable in fp32")
+    u = f32.view(np.uint32).astype(np.uint64)
+    keep = u >> np.uint64(16)
+    rest = u & np.uint64(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))
+    r = ((keep + up.astype(np.uint64)) << np.uint64(16)).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def dequantize_q4(codes, scales, biases, group=64):
+    """Rebuild bf16 weights from 4-bit group-affine codes.
+
+    codes: uint8 [..., N, K / 2], two codes per byte, k = 2 i in the low
+    nibble of byte i and k = 2 i + 1 in the high nibble; scales, biases:
+    [..., N, K / group] (bf16 values).  Returns [..., N, K] fp64 holding the
+    bf16-rounded weights scale * code + bias.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo = (codes & 0x0F).astype(np.float64)
+    hi = (codes >> 4).astype(np.float64)
+    q = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], 2 * codes.shape[-1])
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+    b = np.repeat(np.asarray(biases, dtype=np.float64), group, axis=-1)
+    if s.shape != q.shape:
+        raise ValueError("scales and biases must hold one value per group of codes")
+    return round_bf16(s * q + b)  # the product and sum are exact in fp64
+
+
+def grouped_gemm_q4(x, codes, scales, biases, expert_offsets, group=64):
+    """Grouped GEMM over experts with 4-bit group-affine weights (fp64).
+
+    x: [M, K] activation rows, grouped by expert: rows
+    expert_offsets[e] .. expert_offsets[e + 1] - 1 go to expert e (empty
+    groups allowed); codes [E, N, K / 2], scales and biases [E, N, K / group].
+    Returns y [M, N] with y[r] = W_e x[r] for the expert e owning row r, W_e
+    the rebuilt bf16 weights of dequantize_q4, in fp64.
+    """
+    x = _as_f64(x)
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    w = dequantize_q4(codes, scales, biases, group)  # [E, N, K]
+    E, N, K = w.shape
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M, K]")
+    if off.shape != (E + 1,) or off[0] != 0 or off[-1] != x.shape[0] or np.any(np.diff(off) < 0):
+        raise ValueError("expert_offsets must be non-decreasing, start at 0 and end at M")
+    y = np.zeros((x.shape[0], N), dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            y[a:b] = x[a:b] @ w[e].T
+    return y
+

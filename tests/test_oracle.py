@@ -18,8 +18,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (gated_delta_chunk_form, gated_delta_decode_fused, gated_delta_decode_step,
-                    gated_delta_recurrence, qk_head_of, sigmoid, softplus)
+from oracle import (dequantize_q4, gated_delta_chunk_form, gated_delta_decode_fused, gated_delta_decode_step,
+                    gated_delta_recurrence, grouped_gemm_q4, qk_head_of, round_bf16, sigmoid, softplus)
 from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -497,3 +497,151 @@ def test_fused_pins_catch_planted_mistakes(kind):
     out, _ = fn(**dict(p, norm_weight=None), qk_eps=0.0, norm_eps=0.0)
     failures += not np.allclose(np.mean(out ** 2, axis=-1), 1.0, rtol=1e-12)
     assert failures >= 1
+
+
+# ---------------------------------------------------------------- grouped GEMM on 4-bit weights
+# Section "Dequantize the weights during the matrix multiplication": 4-bit
+# codes, a bf16 scale and bias per group of 64 weights, weights rebuilt in bf16
+# before the multiplication.  Pinned by a hand-worked fixture (which also fixes
+# the bf16 rounding and the nibble order), an independent brute-force loop,
+# closed forms and planted mistakes.
+def _expand(tok):
+    """'v*n', '[a;b]*n' or a plain token -> list of strings."""
+    tok = tok.strip()
+    if "*" in tok:
+        body, n = tok.rsplit("*", 1)
+        items = body[1:-1].split(";") if body.startswith("[") else [body]
+        return [t.strip() for t in items] * int(n)
+    return [tok]
+
+
+def load_q4_fixture():
+    vals = {}
+    with open(os.path.join(GOLDEN, "hand_worked_q4_gemm.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rhs = (x.strip() for x in line.split("=", 1))
+            toks = [t for part in rhs.split(",") for t in _expand(part)]
+            if key.startswith("codes"):
+                vals[key] = np.array([int(t, 16) for t in toks], dtype=np.uint8)
+            else:
+                vals[key] = np.array([float(Fraction(t)) for t in toks])
+    codes = np.stack([np.stack([vals["codes_e0_n0"], vals["codes_e0_n1"]]),
+                      np.stack([vals["codes_e1_n0"], vals["codes_e1_n1"]])])  # [2, 2, 64]
+    x = np.stack([vals["x_row0"], vals["x_row1"], vals["x_row2"]])
+    return dict(x=x, codes=codes, scales=vals["scales"].reshape(2, 2, 2), biases=vals["biases"].reshape(2, 2, 2),
+                offsets=vals["offsets"].astype(np.int64), y=vals["y"].reshape(3, 2))
+
+
+def test_golden_q4_gemm():
+    f = load_q4_fixture()
+    assert f["codes"].shape == (2, 2, 64) and f["x"].shape == (3, 128)
+    y = grouped_gemm_q4(f["x"], f["codes"], f["scales"], f["biases"], f["offsets"])
+    np.testing.assert_array_equal(y, f["y"])  # every value and partial sum is exact in fp64
+
+
+def test_round_bf16_definition():
+    # bf16 keeps 8 significant bits: values on the grid stay, midpoints go to the even neighbour
+    assert round_bf16(1.0) == 1.0 and round_bf16(-3.03125) == -3.03125
+    assert round_bf16(1 + 2.0 ** -8) == 1.0                       # tie: 1.0 is even
+    assert round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6          # tie: up to the even neighbour
+    assert round_bf16(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7  # past the tie: up
+    assert round_bf16(387 / 128) == 3.03125
+    x = np.random.default_rng(3).normal(size=2000).astype(np.float32).astype(np.float64)
+    r = round_bf16(x)
+    # on the bf16 grid (low 16 bits zero) and within half a unit in the last place
+    assert np.all((r.astype(np.float32).view(np.uint32) & 0xFFFF) == 0)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(x))) - 7)
+    assert np.all(np.abs(r - x) <= ulp / 2)
+
+
+def _q4_problem(seed, E=4, N=8, K=128, rows=(3, 0, 5, 1)):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    scales = round_bf16(rng.uniform(0.001, 0.1, size=(E, N, K // 64)).astype(np.float32).astype(np.float64))
+    biases = round_bf16(rng.uniform(-0.5, 0.5, size=(E, N, K // 64)).astype(np.float32).astype(np.float64))
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    x = rng.normal(size=(int(off[-1]), K))
+    return x, codes, scales, biases, off
+
+
+def _brute_q4(x, codes, scales, biases, off):
+    """Triple loop over rows, columns and k, with the nibble taken by divmod."""
+    E, N, half = codes.shape
+    y = np.zeros((x.shape[0], N))
+    for e in range(E):
+        for r in range(int(off[e]), int(off[e + 1])):
+            for n in range(N):
+                acc = 0.0
+                for i in range(half):
+                    hi, lo = divmod(int(codes[e, n, i]), 16)
+                    for k, c in ((2 * i, lo), (2 * i + 1, hi)):
+                        w = float(round_bf16(scales[e, n, k // 64] * c + biases[e, n, k // 64]))
+                        acc += x[r, k] * w
+                y[r, n] = acc
+    return y
+
+
+def test_q4_gemm_brute_force_and_empty_experts():
+    x, codes, scales, biases, off = _q4_problem(5)
+    y = grouped_gemm_q4(x, codes, scales, biases, off)
+    np.testing.assert_allclose(y, _brute_q4(x, codes, scales, biases, off), rtol=1e-12, atol=1e-12)
+    assert y.shape == (9, 8)
+
+
+def test_q4_closed_forms():
+    E, N, K = 2, 3, 128
+    codes = np.full((E, N, K // 2), 0x77, dtype=np.uint8)  # every code 7
+    scales = np.full((E, N, 2), 0.25)
+    biases = np.full((E, N, 2), -1.0)
+    x = np.random.default_rng(1).normal(size=(5, K))
+    off = np.array([0, 2, 5])
+    # constant weight 7/4 - 1 = 3/4: y = 3/4 * row sum
+    np.testing.assert_allclose(grouped_gemm_q4(x, codes, scales, biases, off),
+                               0.75 * np.repeat(x.sum(axis=1, keepdims=True), N, axis=1), rtol=1e-13)
+    # one-hot rows read one rebuilt weight: x = e_k gives y[n] = w[e, n, k]
+    c2 = np.random.default_rng(2).integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    w = dequantize_q4(c2, scales, biases)
+    eye = np.eye(K)[[0, 1, 64, 127]]
+    y = grouped_gemm_q4(eye, c2, scales, biases, np.array([0, 4, 4]))
+    np.testing.assert_array_equal(y, w[0][:, [0, 1, 64, 127]].T)
+    # a zero scale leaves the bias
+    np.testing.assert_array_equal(dequantize_q4(c2, np.zeros((E, N, 2)), biases), np.full((E, N, K), -1.0))
+
+
+def _q4_mutant(kind):
+    def run(x, codes, scales, biases, off, group=64):
+        codes = np.asarray(codes)
+        lo, hi = (codes & 0x0F).astype(float), (codes >> 4).astype(float)
+        if kind == "nibble_swap":
+            lo, hi = hi, lo
+        q = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], -1)
+        g = 32 if kind == "group_32" else group
+        s = np.repeat(scales, g, axis=-1)[..., :q.shape[-1]]
+        b = np.repeat(biases, g, axis=-1)[..., :q.shape[-1]]
+        if s.shape[-1] < q.shape[-1]:
+            s = np.concatenate([s, s[..., -1:].repeat(q.shape[-1] - s.shape[-1], -1)], -1)
+            b = np.concatenate([b, b[..., -1:].repeat(q.shape[-1] - b.shape[-1], -1)], -1)
+        if kind == "scale_bias_swap":
+            s, b = b, s
+        w = s * q + b
+        if kind != "no_rounding":
+            w = round_bf16(w)
+        off2 = np.array(off)
+        if kind == "offsets_shift":
+            off2 = np.concatenate([[0], off2[1:-1] + 1, [off2[-1]]])
+        y = np.zeros((x.shape[0], w.shape[1]))
+        for e in range(w.shape[0]):
+            a, c = int(off2[e]), int(off2[e + 1])
+            y[a:c] = x[a:c] @ w[e].T
+        return y
+    return run
+
+
+@pytest.mark.parametrize("kind", ["nibble_swap", "group_32", "scale_bias_swap", "no_rounding", "offsets_shift"])
+def test_q4_pins_catch_planted_mistakes(kind):
+    f = load_q4_fixture()
+    y = _q4_mutant(kind)(f["x"], f["codes"], f["scales"], f["biases"], f["offsets"])
+    assert not np.allclose(y, f["y"])
