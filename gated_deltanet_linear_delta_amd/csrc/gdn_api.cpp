@@ -317,4 +317,65 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
                   what);
 }
 
+static gdn_status_t check_moe(const gdn_moe_shape_t* s, const char* what) {
+  if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
+  if (s->num_experts < 1) return fail(GDN_ERR_INVALID, "%s: num_experts must be >= 1", what);
+  if (s->rows < 0) return fail(GDN_ERR_INVALID, "%s: rows must be >= 0", what);
+  if (s->k < 64 || s->k % 64 != 0) return fail(GDN_ERR_UNSUPPORTED, "%s: k (%d) must be a positive multiple of 64", what, s->k);
+  if (s->n < 128 || s->n % 128 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: n (%d) must be a positive multiple of 128", what, s->n);
+  if ((long long)s->num_experts * (s->n / 128) > (1ll << 31) - 1)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: num_experts * n / 128 exceeds int32", what);
+  if ((long long)s->rows * s->k > (1ll << 40) || (long long)s->rows * s->n > (1ll << 40))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: rows too large", what);
+  return GDN_OK;
+}
+
+gdn_status_t gdn_moe_gemm_q4(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                             const uint8_t* codes, const void* scales, const void* biases, void* y, void* stream) {
+  const char* what = "gdn_moe_gemm_q4";
+  gdn_status_t st = check_moe(shape, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"expert_offsets", expert_offsets}, {"codes", codes}, {"scales", scales},
+                         {"biases", biases}});
+  if (st != GDN_OK) return st;
+  if (shape->rows > 0) {
+    st = check_ptrs(what, {{"x", x}, {"y", y}});
+    if (st != GDN_OK) return st;
+    if (y == x) return fail(GDN_ERR_INVALID, "%s: y aliases x", what);
+  }
+  return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets, codes,
+                                       scales, biases, y, true, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_dequant_q4(const gdn_moe_shape_t* shape, const uint8_t* codes, const void* scales,
+                            const void* biases, void* weights, void* stream) {
+  const char* what = "gdn_dequant_q4";
+  gdn_status_t st = check_moe(shape, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"codes", codes}, {"scales", scales}, {"biases", biases}, {"weights", weights}});
+  if (st != GDN_OK) return st;
+  return launched(gdn::launch_dequant_q4(shape->num_experts, shape->n, shape->k, codes, scales, biases, weights,
+                                         static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_moe_gemm_bf16(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                               const void* weights, void* y, void* stream) {
+  const char* what = "gdn_moe_gemm_bf16";
+  gdn_status_t st = check_moe(shape, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"expert_offsets", expert_offsets}, {"weights", weights}});
+  if (st != GDN_OK) return st;
+  if (shape->rows > 0) {
+    st = check_ptrs(what, {{"x", x}, {"y", y}});
+    if (st != GDN_OK) return st;
+    if (y == x) return fail(GDN_ERR_INVALID, "%s: y aliases x", what);
+  }
+  return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets,
+                                       weights, nullptr, nullptr, y, false, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
 }  // extern "C"

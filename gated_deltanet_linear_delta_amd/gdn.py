@@ -21,7 +21,8 @@ GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_scan_blockwise", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace",
            "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_decode_step", "gdn_decode_step_fused",
-           "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string", "gdn_last_error")
+           "gdn_moe_gemm_q4", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_profile_enable", "gdn_profile_collect",
+           "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -33,6 +34,11 @@ class GdnShape(ctypes.Structure):
 class GdnFusedParams(ctypes.Structure):
     _fields_ = [("gate_bias", ctypes.c_void_p), ("gate_scale", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
                 ("qk_eps", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+class GdnMoeShape(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("n", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -72,6 +78,13 @@ def load_library(path: str | None = None):
     lib.gdn_decode_step_fused.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, f, f,
                                           ctypes.POINTER(GdnFusedParams), f, vp, f, vp]
     lib.gdn_decode_step_fused.restype = ctypes.c_int
+    mshp = ctypes.POINTER(GdnMoeShape)
+    lib.gdn_moe_gemm_q4.argtypes = [mshp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_moe_gemm_q4.restype = ctypes.c_int
+    lib.gdn_dequant_q4.argtypes = [mshp, vp, vp, vp, vp, vp]
+    lib.gdn_dequant_q4.restype = ctypes.c_int
+    lib.gdn_moe_gemm_bf16.argtypes = [mshp, vp, vp, vp, vp, vp]
+    lib.gdn_moe_gemm_bf16.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
@@ -302,6 +315,67 @@ def decode_step_fused(q_raw, k_raw, v, g_raw, beta_raw, state_in, gate_bias=None
                                      _ptr(beta_raw), ctypes.byref(params), _ptr(state_in), _ptr(out),
                                      _ptr(state_out), _stream(stream)))
     return out, state_out
+
+
+def _moe_shape(x, expert_offsets, codes_or_weights, packed):
+    E, N = codes_or_weights.shape[0], codes_or_weights.shape[1]
+    K = codes_or_weights.shape[2] * (2 if packed else 1)
+    M = x.shape[0]
+    _need(x, "x", torch.bfloat16, (M, K))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    return GdnMoeShape(E, M, K, N)
+
+
+def moe_gemm_q4(x, expert_offsets, codes, scales, biases, y=None, stream=None):
+    """Grouped expert GEMM on 4-bit group-affine weights (gdn_moe_gemm_q4).
+    x [M, K] bf16 grouped by expert; expert_offsets [E + 1] int32; codes
+    [E, N, K / 2] uint8; scales, biases [E, N, K / 64] bf16.  Returns y [M, N]
+    bf16."""
+    lib = load_library()
+    shape = _moe_shape(x, expert_offsets, codes, True)
+    E, N, K = shape.num_experts, shape.n, shape.k
+    _need(codes, "codes", torch.uint8, (E, N, K // 2))
+    _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
+    _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
+    if y is None:
+        y = torch.empty((shape.rows, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(y, "y", torch.bfloat16, (shape.rows, N))
+    _check(lib.gdn_moe_gemm_q4(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(codes), _ptr(scales),
+                               _ptr(biases), _ptr(y), _stream(stream)))
+    return y
+
+
+def dequant_q4(codes, scales, biases, weights=None, stream=None):
+    """The whole bf16 weight matrix [E, N, K] rebuilt from 4-bit codes
+    (gdn_dequant_q4, the ablation's separate pass)."""
+    lib = load_library()
+    E, N, K = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+    _need(codes, "codes", torch.uint8, (E, N, K // 2))
+    _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
+    _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
+    if weights is None:
+        weights = torch.empty((E, N, K), dtype=torch.bfloat16, device=codes.device)
+    else:
+        _need(weights, "weights", torch.bfloat16, (E, N, K))
+    shape = GdnMoeShape(E, 0, K, N)
+    _check(lib.gdn_dequant_q4(ctypes.byref(shape), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(weights),
+                              _stream(stream)))
+    return weights
+
+
+def moe_gemm_bf16(x, expert_offsets, weights, y=None, stream=None):
+    """The same grouped GEMM on bf16 weights [E, N, K] (gdn_moe_gemm_bf16)."""
+    lib = load_library()
+    shape = _moe_shape(x, expert_offsets, weights, False)
+    _need(weights, "weights", torch.bfloat16, (shape.num_experts, shape.n, shape.k))
+    if y is None:
+        y = torch.empty((shape.rows, shape.n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(y, "y", torch.bfloat16, (shape.rows, shape.n))
+    _check(lib.gdn_moe_gemm_bf16(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(weights), _ptr(y),
+                                 _stream(stream)))
+    return y
 
 
 def profile_enable(enabled: bool = True):

@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Inputs", "DecodeInputs", "RawDecodeInputs", "round_to_bf16", "make_prefill", "make_decode",
-           "make_decode_raw", "config"]
+           "make_decode_raw", "MoeInputs", "make_moe", "config"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -193,6 +193,59 @@ def make_decode_raw(batch, h_qk, h_v, d_k, d_v, io_dtype="bf16", state_std=0.02,
     norm_weight = (1.0 + 0.2 * rng.standard_normal(d_v)).astype(f)
     return RawDecodeInputs(q, k, v, g_raw, beta_raw, state, gate_bias, gate_scale, norm_weight, io_dtype,
                            dict(batch=batch, seed=seed, state_std=state_std))
+
+
+@dataclass
+class MoeInputs:
+    """A grouped expert GEMM on 4-bit group-affine weights.  x [M, K] (rows
+    grouped by expert; bf16 values in float32); expert_offsets [E + 1] int32;
+    codes [E, N, K / 2] uint8 (even k in the low nibble); scales, biases
+    [E, N, K / 64] (bf16 values in float32); token_of_row [M]: the token each
+    row was routed from."""
+
+    x: np.ndarray
+    expert_offsets: np.ndarray
+    codes: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray
+    token_of_row: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+
+def make_moe(tokens, num_experts=256, top_k=8, k=2048, n=1024, weight_std=0.02, skew=0.3, seed=0,
+             rng=None) -> MoeInputs:
+    """Route ``tokens`` tokens to ``top_k`` of ``num_experts`` experts and draw
+    4-bit expert weights.
+
+    Draw order: per-expert popularity (normal, standard deviation ``skew``),
+    per-(token, expert) routing
+    noise (normal; each token takes the top_k largest popularity + noise, so
+    experts receive uneven row counts), token activations (standard normal,
+    rounded to bf16), codes (uniform nibbles), then per group the range of a
+    quantized N(0, weight_std) weight group (6 weight_std times U[0.8, 1.2])
+    giving scale = bf16(range / 15) and bias = bf16(-range / 2 + a shift
+    uniform in +-scale).  Rows are the routed tokens' activations, grouped by
+    expert and in token order within an expert.
+    """
+    rng = np.random.default_rng(seed) if rng is None else rng
+    pop = skew * rng.standard_normal(num_experts)
+    noise = rng.standard_normal((tokens, num_experts))
+    choice = np.argsort(-(pop[None, :] + noise), axis=1, kind="stable")[:, :top_k]  # [tokens, top_k]
+    xt = round_to_bf16(rng.standard_normal((tokens, k), dtype=np.float32))
+    expert_of = choice.reshape(-1)
+    token_of = np.repeat(np.arange(tokens), top_k)
+    order = np.lexsort((token_of, expert_of))  # by expert, then token
+    counts = np.bincount(expert_of, minlength=num_experts)
+    offsets = np.zeros(num_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    token_of_row = token_of[order]
+    codes = rng.integers(0, 256, size=(num_experts, n, k // 2), dtype=np.uint8)
+    rngs = (6.0 * weight_std * rng.uniform(0.8, 1.2, size=(num_experts, n, k // 64))).astype(np.float32)
+    scales = round_to_bf16(rngs / np.float32(15.0))
+    shift = rng.uniform(-1.0, 1.0, size=rngs.shape).astype(np.float32) * scales
+    biases = round_to_bf16(-rngs / np.float32(2.0) + shift)
+    return MoeInputs(xt[token_of_row], offsets, codes, scales, biases, token_of_row,
+                     dict(tokens=tokens, num_experts=num_experts, top_k=top_k, k=k, n=n, skew=skew, seed=seed))
 
 
 def ragged_lengths(rng, n, lo=256, hi=8192):

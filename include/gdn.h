@@ -227,6 +227,50 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
                                    const float* state_in, void* out, float* state_out, void* stream);
 
 /*
+ * Expert GEMM on 4-bit group-affine weights (section "Dequantize the weights
+ * during the matrix multiplication": each weight is a 4-bit code, each group
+ * of 64 weights shares a bf16 scale and bias that rebuild it, the matrix unit
+ * consumes bf16, accumulation is fp32 and the output bf16; section "Keep
+ * expert routing on the GPU": the activation rows routed to an expert are
+ * stored together).  Shapes:
+ *     x        [rows, k]        bf16, rows grouped by expert
+ *     expert_offsets [num_experts + 1] int32, device; expert e owns rows
+ *              expert_offsets[e] .. expert_offsets[e + 1] - 1 (empty allowed,
+ *              non-decreasing, from 0 to rows; clamped on the device)
+ *     codes    [num_experts, n, k / 2] uint8: byte i of row (e, c) holds
+ *              the codes of k = 2 i (low nibble) and k = 2 i + 1 (high)
+ *     scales, biases [num_experts, n, k / 64] bf16: one per group of 64 k
+ *     y        [rows, n]        bf16
+ * Weight (e, c, k) = bf16(scale * code + bias), the product and sum formed by
+ * one fp32 fma and rounded once (nearest even); y[r, c] = sum_k x[r, k] *
+ * weight(e, c, k) for the expert e of row r, fp32 accumulation.  k is a
+ * positive multiple of 64, n of 128.  With rows = 0, x and y may be NULL.
+ */
+typedef struct {
+  int32_t num_experts;  /* E >= 1 */
+  int32_t rows;         /* total routed activation rows, >= 0 */
+  int32_t k;            /* contraction size, a multiple of 64 */
+  int32_t n;            /* output columns, a multiple of 128 */
+} gdn_moe_shape_t;
+
+/* The fused form: each weight tile is rebuilt in registers as it is used; the
+ * bf16 matrix never exists in memory. */
+gdn_status_t gdn_moe_gemm_q4(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                             const uint8_t* codes, const void* scales, const void* biases, void* y,
+                             void* stream);
+
+/* The pages' ablation, first half: rebuild the whole bf16 matrix
+ * weights [num_experts, n, k] in memory (the same rounding as the fused form). */
+gdn_status_t gdn_dequant_q4(const gdn_moe_shape_t* shape, const uint8_t* codes, const void* scales,
+                            const void* biases, void* weights, void* stream);
+
+/* The ablation, second half: the same grouped GEMM reading bf16 weights
+ * [num_experts, n, k].  With weights from gdn_dequant_q4 it returns exactly
+ * gdn_moe_gemm_q4's y. */
+gdn_status_t gdn_moe_gemm_bf16(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                               const void* weights, void* y, void* stream);
+
+/*
  * Kernel timing for benchmarks and profiling.  While enabled (process-wide),
  * every kernel the library enqueues is bracketed by two hipEvents recorded on
  * the stream it is launched on.  Off by default; when off, no events are

@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_match_header(lib):
@@ -214,3 +214,22 @@ def test_empty_prompt_token_tensors_may_be_null(lib):
     mis[1] = FAKE + 8
     assert lib.gdn_prefill_chunked(*mis, 64, FAKE + 4096, 1 << 40, None) == 1
     assert "aligned" in lib.gdn_last_error().decode()
+
+
+def test_moe_rejects(lib):
+    S = gdn.GdnMoeShape
+    p = [FAKE + 256 * i for i in range(6)]  # x, offsets, codes, scales, biases, y
+    ok = S(8, 100, 256, 256)
+    assert lib.gdn_moe_gemm_q4(None, *p, None) == 1
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(0, 100, 256, 256)), *p, None) == 1
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, -1, 256, 256)), *p, None) == 1
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, 100, 96, 256)), *p, None) == 2     # k not a multiple of 64
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, 100, 256, 192)), *p, None) == 2    # n not a multiple of 128
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), None, *p[1:], None) == 1            # x missing with rows > 0
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), p[0], None, *p[2:], None) == 1      # offsets missing
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), *p[:5], p[0], None) == 1           # y aliases x
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), p[0] + 8, *p[1:], None) == 1       # misaligned x
+    assert "aligned" in lib.gdn_last_error().decode()
+    assert lib.gdn_dequant_q4(ctypes.byref(ok), p[2], p[3], p[4], None, None) == 1   # weights missing
+    assert lib.gdn_moe_gemm_bf16(ctypes.byref(S(8, 100, 100, 256)), p[0], p[1], p[2], p[5], None) == 2
+    assert lib.gdn_moe_gemm_bf16(ctypes.byref(ok), p[0], p[1], None, p[5], None) == 1
