@@ -25,6 +25,10 @@ same JSON line also carries:
   ragged_prefill  32 sequences with the ragged workload's lengths (about
               73k tokens, drawn on the device) through the chunked path and
               the scan: tokens/s, MFMA and HBM fractions;
+  moe_gemm_q4  the expert GEMM on 4-bit group-affine weights (256 experts,
+              top 8, K = 2048, N = 1024) at 512- and 2048-token prompts:
+              rebuilt in the GEMM against the two-pass ablation, with the
+              HBM and MFMA fractions of the fused kernel;
   segmented_prefill  a 131072-token prompt (drawn on the device) chunked in
               one call and through gdn_prefill_segmented in 8192- and
               4096-token segments: time, workspace, and output equality;
@@ -147,6 +151,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--no-moe", action="store_true", help="skip the 4-bit expert GEMM leg")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 131072-token segmented-prefill and the ragged-batch legs")
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
@@ -465,6 +470,54 @@ def main():
         torch.cuda.empty_cache()
         log(f"ragged batch: {ragged}")
 
+    # ------------------------------------------------------------ expert GEMM on 4-bit weights
+    # The pages' other ablation: 4-bit group-affine expert weights rebuilt
+    # inside the grouped GEMM against rebuilding the whole bf16 matrix in
+    # memory first.  256 experts, top 8, one projection K = 2048 -> N = 1024,
+    # at prompts of 512 and 2048 tokens.
+    moe = None
+    if not args.no_moe:
+        from gated_deltanet_linear_delta_amd.workloads import make_moe
+        moe = {}
+        for tok in (512, 2048):
+            mi = make_moe(tok, num_experts=256, top_k=8, k=2048, n=1024, seed=5000 + tok)
+            bfd = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
+            xm, offm = bfd(mi.x), torch.from_numpy(mi.expert_offsets.astype(np.int32)).to(dev)
+            cm, sm, bm = torch.from_numpy(mi.codes).to(dev), bfd(mi.scales), bfd(mi.biases)
+            ym = torch.empty((xm.shape[0], 1024), dtype=torch.bfloat16, device=dev)
+            wm = torch.empty((256, 1024, 2048), dtype=torch.bfloat16, device=dev)
+            fused = lambda: gdn.moe_gemm_q4(xm, offm, cm, sm, bm, y=ym)
+            two_pass = lambda: (gdn.dequant_q4(cm, sm, bm, weights=wm), gdn.moe_gemm_bf16(xm, offm, wm, y=ym))
+            for fn in (fused, two_pass, fused):
+                for _ in range(3):
+                    fn()
+            torch.cuda.synchronize()
+            res = {}
+            for name, fn in (("fused", fused), ("two_pass", two_pass)):
+                gdn.profile_enable(True)
+                t3 = time.perf_counter()
+                for _ in range(20):
+                    fn()
+                torch.cuda.synchronize()
+                res[name + "_us"] = round((time.perf_counter() - t3) * 1e6 / 20, 2)
+                gdn.profile_enable(False)
+                res[name + "_kernels_us"] = {n_: round(m_ * 1e3, 2) for n_, (m_, _) in
+                                             mean_by_name(gdn.profile_collect()).items()}
+            M = int(xm.shape[0])
+            nbytes = cm.numel() + 2 * 2 * sm.numel() + 2 * xm.numel() + 2 * ym.numel() + 4 * offm.numel()
+            kern = res["fused_kernels_us"]["moe_gemm_q4"]
+            res.update({"routed_rows": M, "rows_per_expert_max": int(np.diff(mi.expert_offsets).max()),
+                        "algorithmic_bytes": nbytes,
+                        "hbm_gbs": round(nbytes / (kern * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tflops": round(2.0 * M * 2048 * 1024 / (kern * 1e-6) / 1e12, 1),
+                        "mfma_util": round(2.0 * M * 2048 * 1024 / (kern * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "fusion_speedup": round(res["two_pass_us"] / res["fused_us"], 2)})
+            moe[f"tokens_{tok}"] = res
+            del xm, cm, sm, bm, ym, wm
+        torch.cuda.empty_cache()
+        log(f"expert GEMM on 4-bit weights: {moe}")
+
     # ------------------------------------------------------------ bounded prompt segments
     # One 131072-token prompt (the long workload's shape; inputs drawn on the
     # device with the same distributions), chunked in one call with a
@@ -565,6 +618,7 @@ def main():
         "state_residency_ablation": ablation,
         "segmented_prefill": segmented,
         "ragged_prefill": ragged,
+        "moe_gemm_q4": moe,
         "scan": scan,
         "cpu_baseline": cpu,
     }

@@ -320,14 +320,16 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
 static gdn_status_t check_moe(const gdn_moe_shape_t* s, const char* what) {
   if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
   if (s->num_experts < 1) return fail(GDN_ERR_INVALID, "%s: num_experts must be >= 1", what);
+  if (s->num_experts > 4096) return fail(GDN_ERR_UNSUPPORTED, "%s: at most 4096 experts", what);
   if (s->rows < 0) return fail(GDN_ERR_INVALID, "%s: rows must be >= 0", what);
-  if (s->k < 64 || s->k % 64 != 0) return fail(GDN_ERR_UNSUPPORTED, "%s: k (%d) must be a positive multiple of 64", what, s->k);
+  if (s->k < 128 || s->k % 128 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: k (%d) must be a positive multiple of 128", what, s->k);
   if (s->n < 128 || s->n % 128 != 0)
     return fail(GDN_ERR_UNSUPPORTED, "%s: n (%d) must be a positive multiple of 128", what, s->n);
   if ((long long)s->num_experts * (s->n / 128) > (1ll << 31) - 1)
     return fail(GDN_ERR_UNSUPPORTED, "%s: num_experts * n / 128 exceeds int32", what);
-  if ((long long)s->rows * s->k > (1ll << 40) || (long long)s->rows * s->n > (1ll << 40))
-    return fail(GDN_ERR_UNSUPPORTED, "%s: rows too large", what);
+  if ((long long)s->rows * s->k > (1ll << 31) - 1 || (long long)s->rows * s->n > (1ll << 40))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: rows * k must stay below 2^31", what);
   return GDN_OK;
 }
 

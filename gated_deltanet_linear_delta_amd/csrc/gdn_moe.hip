@@ -16,16 +16,23 @@
 // scale and bias of group k / 64; the product and the sum are formed by one
 // fp32 fma and rounded once to bf16 (nearest even).
 //
-// Tiling (gfx950, wave64, v_mfma_f32_16x16x32_bf16): a workgroup of four waves
-// owns one expert and a block of BN = 128 output columns, and walks all of
-// that expert's rows in passes of up to RT row tiles of 16.  Wave w owns 32
-// columns (two 16-column tiles): per 32-wide slab of k it rebuilds its two B
-// fragments once (one dword of eight codes per lane: two mask operations,
-// eight byte conversions, eight fma and four bf16 packs) and multiplies them
-// by the pass's A fragments (16 bytes of one activation row per lane), so
-// each weight is rebuilt once per pass and up to RT row tiles reuse it.  The
-// next slab's codes and activations are loaded while the current one
-// computes.
+// Tiling (gfx950, wave64, v_mfma_f32_16x16x32_bf16).  The rows of each expert
+// are cut into blocks of BM = 64 (the last one short); block b of expert e is
+// slot first_slot(e) + b with first_slot(e) = (offset_e + e (BM - 1)) / BM, so
+// the grid needs no table: a workgroup stages the expert offsets in LDS and
+// finds its expert by binary search.  A workgroup of four waves owns one row
+// block and BN = 128 output columns; wave w owns 32 of them (two 16-column
+// tiles) for all four row tiles.  The contraction runs in super-slabs of 128
+// k, each four MFMA slabs of 32; within a super-slab lane group grp takes
+// k = 32 grp + 8 j + (0..7) in slab j, the same for the activations and the
+// weights (a sum over k does not care about the order), so one 16-byte load
+// per lane and column brings the codes of all four slabs, all in one group of
+// 64 (one scale and bias per lane and column).  The codes are loaded two
+// super-slabs ahead, the activations one slab ahead; each weight is rebuilt
+// once per row block (two mask operations, eight byte conversions, eight fma
+// and four bf16 packs per eight weights).
+#include <type_traits>
+
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
 
@@ -33,10 +40,16 @@ namespace gdn {
 
 namespace {
 constexpr int BN = 128;  // output columns per workgroup
-constexpr int RT = 8;    // row tiles (of 16) per pass
+constexpr int BM = 64;   // rows per block (four row tiles of 16)
+constexpr int RT = BM / 16;
 constexpr int GROUP = 64;
+constexpr int KS = 128;        // k per super-slab
+constexpr int MAX_EXPERTS = 4096;  // expert offsets staged in LDS (16 KiB at most)
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// staged pieces as native vectors, so that arrays of them stay in registers
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // byte j of x as a float (the compiler emits v_cvt_f32_ubyte<j>)
 template <int J>
@@ -66,115 +79,176 @@ __global__ __launch_bounds__(256) void dequant_q4_kernel(size_t n_dwords, int k,
   w[i] = rebuild8(codes[i], bf16_bits_to_f32(scales[gi]), bf16_bits_to_f32(biases[gi]));
 }
 
+__device__ __forceinline__ int first_slot(int off, int e) { return (off + e * (BM - 1)) / BM; }
+
+// LDS: the expert offsets, then two buffers of the row block's activations for
+// one super-slab, [BM rows][KS k] bf16 with rows AS bytes apart (32 mod 128,
+// so the 16-lane fragment reads of 16 rows are free of bank conflicts).
+constexpr int AS = KS * 2 + 32;
+constexpr int ABUF = BM * AS;
+__host__ __device__ constexpr size_t moe_lds_bytes(int n_exp) { return (size_t(n_exp + 1) * 4 + 15) / 16 * 16 + 2 * ABUF; }
+
 template <bool Q4>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(int n_exp, int m, int n, int k, const uint16_t* __restrict__ x,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const uint8_t* __restrict__ wsrc,
-                                                       const uint16_t* __restrict__ scales,
-                                                       const uint16_t* __restrict__ biases, uint16_t* __restrict__ y) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemm_kernel(
+    int n_exp, int m, int n, int k, const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ wsrc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int* soff = reinterpret_cast<int*>(smem);
+  uint8_t* sa = smem + (size_t(n_exp + 1) * 4 + 15) / 16 * 16;
   const int ncb = n / BN;
-  const int e = blockIdx.x / ncb, cb = blockIdx.x % ncb;
-  int r_lo = offsets[e], r_hi = offsets[e + 1];
-  r_lo = r_lo < 0 ? 0 : (r_lo > m ? m : r_lo);  // malformed offsets cannot index out of bounds
-  r_hi = r_hi < r_lo ? r_lo : (r_hi > m ? m : r_hi);
-  if (r_hi == r_lo) return;
-  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  for (int i = threadIdx.x; i <= n_exp; i += 256) {
+    int o = offsets[i];
+    soff[i] = o < 0 ? 0 : (o > m ? m : o);  // malformed offsets cannot index out of bounds
+  }
+  __syncthreads();
+  // the expert whose slots contain this one: the largest e with first_slot(e) <= slot
+  int lo = 0, hi = n_exp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first_slot(soff[mid], mid) <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int e_lo = soff[e], e_hi = max(soff[e + 1], e_lo);
+  const int fs = first_slot(e_lo, e);
+  if (slot < fs) return;  // only with malformed (decreasing) offsets
+  const int r_lo = e_lo + (slot - fs) * BM;
+  if (r_lo >= e_hi) return;  // a spare slot of this expert
+  const int r_hi = min(r_lo + BM, e_hi);
+
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = cb * BN + 32 * wave;  // this wave's 32 columns
   const int ngroups = k / GROUP;
-  // per lane: columns n0 + col and n0 + 16 + col; k offset 8 grp within a slab
   const size_t wrow0 = size_t(e) * n + n0 + col, wrow1 = wrow0 + 16;
 
-  for (int p0 = r_lo; p0 < r_hi; p0 += 16 * RT) {
-    const int nt = min(RT, (r_hi - p0 + 15) / 16);  // row tiles in this pass
-    f4 acc[RT][2];
+  // The k loop, for NT row tiles that hold rows (1..4, the same in the whole
+  // workgroup): only those tiles are staged, read and multiplied.
+  auto run = [&](auto nt_c) __attribute__((always_inline)) {
+    constexpr int NT = decltype(nt_c)::value;
+    constexpr int NP = NT;  // 16-byte pieces per thread: NT * 16 rows * 16 pieces / 256 threads
+    // staging of one super-slab of activations: thread tid moves pieces
+    // tid + 256 i (row p / 16, 16 bytes at k = 8 (p % 16)); rows past the
+    // block repeat its last row (their results are dropped)
+    uint32_t goff[NP], loff[NP];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t][0] = acc[t][1] = zero4();
-    // A rows of this lane in each tile (rows past the expert read its last row; their results are dropped)
-    const uint16_t* xrow[RT];
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + 256 * i, r = p >> 4, c = p & 15;
+      goff[i] = uint32_t(min(r_lo + r, r_hi - 1)) * uint32_t(k) + 8 * c;
+      loff[i] = uint32_t(r * AS + 16 * c);
+    }
+    auto fetch_a = [&](v4u (&st)[NP], int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) xrow[t] = x + size_t(min(p0 + 16 * t + col, r_hi - 1)) * k + 8 * grp;
-
-    auto load_b = [&](uint32_t (&d)[2], uint4 (&wb)[2], int k0) __attribute__((always_inline)) {
+      for (int i = 0; i < NP; ++i) st[i] = *reinterpret_cast<const v4u*>(x + goff[i] + ks);
+    };
+    auto commit_a = [&](const v4u (&st)[NP], int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) *reinterpret_cast<v4u*>(sa + buf * ABUF + loff[i]) = st[i];
+    };
+    // weights of one super-slab for both columns: 16 bytes of codes each and
+    // the raw bf16 scale and bias of the lane's group (Q4)
+    auto load_w = [&](uint4 (&c)[2], uint16_t (&sb)[4], int ks) __attribute__((always_inline)) {
       if constexpr (Q4) {
-        d[0] = *reinterpret_cast<const uint32_t*>(wsrc + wrow0 * (k / 2) + k0 / 2 + 4 * grp);
-        d[1] = *reinterpret_cast<const uint32_t*>(wsrc + wrow1 * (k / 2) + k0 / 2 + 4 * grp);
-      } else {
-        const uint16_t* wb16 = reinterpret_cast<const uint16_t*>(wsrc);
-        wb[0] = *reinterpret_cast<const uint4*>(wb16 + wrow0 * k + k0 + 8 * grp);
-        wb[1] = *reinterpret_cast<const uint4*>(wb16 + wrow1 * k + k0 + 8 * grp);
+        c[0] = *reinterpret_cast<const uint4*>(wsrc + wrow0 * (k / 2) + ks / 2 + 16 * grp);
+        c[1] = *reinterpret_cast<const uint4*>(wsrc + wrow1 * (k / 2) + ks / 2 + 16 * grp);
+        const int g = (ks + 32 * grp) / GROUP;
+        sb[0] = scales[wrow0 * ngroups + g], sb[1] = biases[wrow0 * ngroups + g];
+        sb[2] = scales[wrow1 * ngroups + g], sb[3] = biases[wrow1 * ngroups + g];
       }
     };
-    auto load_a = [&](uint4 (&a)[RT], int k0) __attribute__((always_inline)) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        if (t < nt) a[t] = *reinterpret_cast<const uint4*>(xrow[t] + k0);
-    };
 
-    uint32_t dc[2], dn[2];
-    uint4 wc[2], wn[2], ac[RT], an[RT];
-    float s0 = 0.f, b0 = 0.f, s1 = 0.f, b1 = 0.f;
-    load_b(dc, wc, 0);
-    load_a(ac, 0);
-    for (int k0 = 0; k0 < k; k0 += 32) {
-      if constexpr (Q4) {
-        if ((k0 & (GROUP - 1)) == 0) {  // a new group: its scale and bias for both columns
-          const int g = k0 / GROUP;
-          s0 = bf16_bits_to_f32(scales[wrow0 * ngroups + g]), b0 = bf16_bits_to_f32(biases[wrow0 * ngroups + g]);
-          s1 = bf16_bits_to_f32(scales[wrow1 * ngroups + g]), b1 = bf16_bits_to_f32(biases[wrow1 * ngroups + g]);
+    f4 acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = zero4();
+    uint4 c0[2], c1[2], c2[2];
+    v4u stg[NP];
+    uint16_t g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0}, g2[4] = {0, 0, 0, 0};
+    const int nks = k / KS;
+    load_w(c0, g0, 0);
+    load_w(c1, g1, min(KS, k - KS));
+    fetch_a(stg, 0);
+    commit_a(stg, 0);
+    __syncthreads();
+    for (int si = 0; si < nks; ++si) {
+      const int ks = si * KS, buf = si & 1;
+      // the next super-slab's activations first, then the codes two ahead, so
+      // that waiting for the activations leaves the codes in flight; both
+      // unconditional (the end reloads the last) so the memory waits stay exact
+      fetch_a(stg, min(ks + KS, k - KS));
+      load_w(c2, g2, min(ks + 2 * KS, k - KS));
+      const float s0 = bf16_bits_to_f32(g0[0]), b0 = bf16_bits_to_f32(g0[1]);
+      const float s1 = bf16_bits_to_f32(g0[2]), b1 = bf16_bits_to_f32(g0[3]);
+      const uint32_t d0[4] = {c0[0].x, c0[0].y, c0[0].z, c0[0].w}, d1[4] = {c0[1].x, c0[1].y, c0[1].z, c0[1].w};
+      const uint8_t* abase = sa + buf * ABUF + col * AS + 64 * grp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = ks + 8 * j;
+        uint4 bf0, bf1;
+        if constexpr (Q4) {
+          bf0 = rebuild8(d0[j], s0, b0);
+          bf1 = rebuild8(d1[j], s1, b1);
+        } else {
+          const uint16_t* wb16 = reinterpret_cast<const uint16_t*>(wsrc);
+          bf0 = *reinterpret_cast<const uint4*>(wb16 + wrow0 * k + kk + 32 * grp);
+          bf1 = *reinterpret_cast<const uint4*>(wb16 + wrow1 * k + kk + 32 * grp);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint4 a = *reinterpret_cast<const uint4*>(abase + 16 * t * AS + 16 * j);
+          acc[t][0] = mma32(a, bf0, acc[t][0]);
+          acc[t][1] = mma32(a, bf1, acc[t][1]);
         }
       }
-      const int kn = min(k0 + 32, k - 32);  // the next slab (the last one reloads itself)
-      load_b(dn, wn, kn);
-      load_a(an, kn);
-      uint4 bf0, bf1;
-      if constexpr (Q4) {
-        bf0 = rebuild8(dc[0], s0, b0);
-        bf1 = rebuild8(dc[1], s1, b1);
-      } else {
-        bf0 = wc[0], bf1 = wc[1];
-      }
+      commit_a(stg, buf ^ 1);  // the other buffer: its last readers passed the previous barrier
+      __syncthreads();
+      c0[0] = c1[0], c0[1] = c1[1], c1[0] = c2[0], c1[1] = c2[1];
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if (t < nt) {
-          acc[t][0] = mma32(ac[t], bf0, acc[t][0]);
-          acc[t][1] = mma32(ac[t], bf1, acc[t][1]);
-        }
-      }
-      dc[0] = dn[0], dc[1] = dn[1], wc[0] = wn[0], wc[1] = wn[1];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) ac[t] = an[t];
+      for (int i = 0; i < 4; ++i) g0[i] = g1[i], g1[i] = g2[i];
     }
     // D block: lane holds rows 4 grp .. 4 grp + 3 of the tile, column col
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if (t < nt) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = p0 + 16 * t + 4 * grp + qq;
-          if (r < r_hi) {
-            y[size_t(r) * n + n0 + col] = f2bf(acc[t][0][qq]);
-            y[size_t(r) * n + n0 + 16 + col] = f2bf(acc[t][1][qq]);
-          }
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = r_lo + 16 * t + 4 * grp + qq;
+        if (r < r_hi) {
+          y[size_t(r) * n + n0 + col] = f2bf(acc[t][0][qq]);
+          y[size_t(r) * n + n0 + 16 + col] = f2bf(acc[t][1][qq]);
         }
       }
     }
-  }
+  };
+  const int nt = (r_hi - r_lo + 15) / 16;  // row tiles that hold rows, 1..4
+  if (nt == 1) run(std::integral_constant<int, 1>());
+  else if (nt == 2) run(std::integral_constant<int, 2>());
+  else if (nt == 3) run(std::integral_constant<int, 3>());
+  else run(std::integral_constant<int, 4>());
 }
 
 hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const int32_t* offsets,
                            const void* weights, const void* scales, const void* biases, void* y, bool q4,
                            hipStream_t st) {
-  const unsigned blocks = unsigned(n_exp) * unsigned(n / BN);
+  // row-block slots: sum_e ceil(m_e / BM) <= (m + E (BM - 1)) / BM
+  const size_t slots = (size_t(m) + size_t(n_exp) * (BM - 1)) / BM;
+  const unsigned blocks = unsigned(slots * size_t(n / BN));
   if (blocks == 0 || m == 0) return hipSuccess;
   Prof prof(q4 ? "moe_gemm_q4" : "moe_gemm_bf16", st);
+  const size_t lds = moe_lds_bytes(n_exp);
+  const void* fn = q4 ? reinterpret_cast<const void*>(&moe_gemm_kernel<true>)
+                      : reinterpret_cast<const void*>(&moe_gemm_kernel<false>);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
   if (q4)
-    hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(blocks), dim3(256), 0, st, n_exp, m, n, k,
+    hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(blocks), dim3(256), lds, st, n_exp, m, n, k,
                        static_cast<const uint16_t*>(x), offsets, static_cast<const uint8_t*>(weights),
                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
                        static_cast<uint16_t*>(y));
   else
-    hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(blocks), dim3(256), 0, st, n_exp, m, n, k,
+    hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(blocks), dim3(256), lds, st, n_exp, m, n, k,
                        static_cast<const uint16_t*>(x), offsets, static_cast<const uint8_t*>(weights), nullptr,
                        nullptr, static_cast<uint16_t*>(y));
   return hipGetLastError();

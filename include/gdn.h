@@ -243,13 +243,14 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
  *     y        [rows, n]        bf16
  * Weight (e, c, k) = bf16(scale * code + bias), the product and sum formed by
  * one fp32 fma and rounded once (nearest even); y[r, c] = sum_k x[r, k] *
- * weight(e, c, k) for the expert e of row r, fp32 accumulation.  k is a
- * positive multiple of 64, n of 128.  With rows = 0, x and y may be NULL.
+ * weight(e, c, k) for the expert e of row r, fp32 accumulation (in an order
+ * of its own).  k is a positive multiple of 128, n of 128; at most 4096
+ * experts; rows * k below 2^31.  With rows = 0, x and y may be NULL.
  */
 typedef struct {
   int32_t num_experts;  /* E >= 1 */
   int32_t rows;         /* total routed activation rows, >= 0 */
-  int32_t k;            /* contraction size, a multiple of 64 */
+  int32_t k;            /* contraction size, a multiple of 128 */
   int32_t n;            /* output columns, a multiple of 128 */
 } gdn_moe_shape_t;
 

@@ -223,7 +223,8 @@ def test_moe_rejects(lib):
     assert lib.gdn_moe_gemm_q4(None, *p, None) == 1
     assert lib.gdn_moe_gemm_q4(ctypes.byref(S(0, 100, 256, 256)), *p, None) == 1
     assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, -1, 256, 256)), *p, None) == 1
-    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, 100, 96, 256)), *p, None) == 2     # k not a multiple of 64
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, 100, 192, 256)), *p, None) == 2    # k not a multiple of 128
+    assert lib.gdn_moe_gemm_q4(ctypes.byref(S(5000, 100, 256, 256)), *p, None) == 2  # too many experts
     assert lib.gdn_moe_gemm_q4(ctypes.byref(S(8, 100, 256, 192)), *p, None) == 2    # n not a multiple of 128
     assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), None, *p[1:], None) == 1            # x missing with rows > 0
     assert lib.gdn_moe_gemm_q4(ctypes.byref(ok), p[0], None, *p[2:], None) == 1      # offsets missing

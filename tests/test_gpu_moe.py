@@ -58,9 +58,9 @@ def test_dequant_bit_exact():
 
 
 @pytest.mark.parametrize("tokens,E,top_k,K,N", [
-    (64, 4, 2, 64, 128),
+    (64, 4, 2, 128, 128),
     (200, 8, 3, 256, 256),
-    (300, 16, 8, 512, 128),     # experts with hundreds of rows: several passes
+    (300, 16, 8, 512, 128),     # experts with hundreds of rows: several 64-row blocks
     (40, 64, 4, 128, 384),      # many empty experts
 ])
 def test_moe_gemm_parity(tokens, E, top_k, K, N):
@@ -117,7 +117,7 @@ def test_moe_gemm_full_size_sampled():
 
 
 def test_moe_gemm_empty_batch():
-    m = make_moe(16, num_experts=4, top_k=1, k=64, n=128, seed=1)
+    m = make_moe(16, num_experts=4, top_k=1, k=128, n=128, seed=1)
     d = dev(m)
     x0 = d["x"][:0]
     off0 = torch.zeros(5, dtype=torch.int32, device="cuda")
