@@ -326,8 +326,10 @@ static gdn_status_t check_moe(const gdn_moe_shape_t* s, const char* what) {
     return fail(GDN_ERR_UNSUPPORTED, "%s: k (%d) must be a positive multiple of 128", what, s->k);
   if (s->n < 128 || s->n % 128 != 0)
     return fail(GDN_ERR_UNSUPPORTED, "%s: n (%d) must be a positive multiple of 128", what, s->n);
-  if ((long long)s->num_experts * (s->n / 128) > (1ll << 31) - 1)
-    return fail(GDN_ERR_UNSUPPORTED, "%s: num_experts * n / 128 exceeds int32", what);
+  // the grid: one workgroup per (64-row block slot, 128-column block)
+  const long long slots = ((long long)s->rows + (long long)s->num_experts * 63) / 64;
+  if (slots * (s->n / 128) > (1ll << 31) - 1)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: (rows + 63 num_experts) / 64 * n / 128 exceeds int32", what);
   if ((long long)s->rows * s->k > (1ll << 31) - 1 || (long long)s->rows * s->n > (1ll << 40))
     return fail(GDN_ERR_UNSUPPORTED, "%s: rows * k must stay below 2^31", what);
   return GDN_OK;

@@ -78,11 +78,6 @@ __device__ __forceinline__ void mm_ss(const sp8& a, const sp8& b, f4& ch, f4& cl
   cl = mma32(a.lo, b.hi, cl);
 }
 __device__ __forceinline__ void mm_ss(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
-__device__ __forceinline__ void mm_se(const sp8& a, uint4 b, f4& ch, f4& cl) {
-  ch = mma32(a.hi, b, ch);
-  cl = mma32(a.lo, b, cl);
-}
-__device__ __forceinline__ void mm_se(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
 
 template <bool BF>
 struct Types {
@@ -97,11 +92,7 @@ struct Types<false> {
   using IO = float;
 };
 
-__device__ __forceinline__ void zero(uint4& x) { x = uint4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ void zero(f8& x) { x.a = zero4(), x.b = zero4(); }
-__device__ __forceinline__ void zero(sp8& x) { zero(x.hi), zero(x.lo); }
-__device__ __forceinline__ void zero(float& x) { x = 0.f; }
-__device__ __forceinline__ void zero(uint16_t& x) { x = 0; }
 
 // 8 consecutive elements of an LDS/global row as an operand.
 __device__ __forceinline__ void ld8(uint4& d, const uint16_t* p) { d = *reinterpret_cast<const uint4*>(p); }
@@ -120,11 +111,7 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p)));
 }
 
-// 8 elements of a column (stride apart) as an operand.
-__device__ __forceinline__ void ld8col(uint4& d, const uint16_t* p, int stride) {
-  d = uint4{pack2(p[0], p[stride]), pack2(p[2 * stride], p[3 * stride]), pack2(p[4 * stride], p[5 * stride]),
-            pack2(p[6 * stride], p[7 * stride])};
-}
+// 8 fp32 elements of a column (stride apart) as an operand.
 __device__ __forceinline__ void ld8col(f8& d, const float* p, int stride) {
   d.a = f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
   d.b = f4{p[4 * stride], p[5 * stride], p[6 * stride], p[7 * stride]};
@@ -333,26 +320,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return uint4{x[0], x[1], x[2], x[3]};
-}
-__device__ __forceinline__ void bload_op(uint4& d, Rsrc r, uint32_t off) { d = bload16(r, off); }
-__device__ __forceinline__ void bload_op(f8& d, Rsrc r, uint32_t off) {
-  const uint4 a = bload16(r, off), b = bload16(r, off + 16);
-  d.a = f4{__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
-  d.b = f4{__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
-}
-template <typename IO>
-__device__ __forceinline__ IO bload_el(Rsrc r, uint32_t off) {
-  if constexpr (sizeof(IO) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-template <typename IO>
-__device__ __forceinline__ void bstore_el(Rsrc r, uint32_t off, float x) {
-  if constexpr (sizeof(IO) == 2) __builtin_amdgcn_raw_buffer_store_b16(f2bf(x), r, off, 0, 0);
-  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
-}
 // Four consecutive values of one row (8 bytes in bf16, 16 in fp32).
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <typename IO>
@@ -365,8 +332,6 @@ __device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, f4 x) {
         u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
   }
 }
-__device__ __forceinline__ float io_val(uint16_t x) { return bf2f(x); }
-__device__ __forceinline__ float io_val(float x) { return x; }
 // A split (bf16 hi + lo, two planes `plane` bytes apart) or fp32 operand from global memory.
 __device__ __forceinline__ void ld_split(sp8& d, const uint8_t* p, int plane) {
   d.hi = *reinterpret_cast<const uint4*>(p);

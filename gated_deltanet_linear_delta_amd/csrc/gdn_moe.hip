@@ -41,10 +41,8 @@ namespace gdn {
 namespace {
 constexpr int BN = 128;  // output columns per workgroup
 constexpr int BM = 64;   // rows per block (four row tiles of 16)
-constexpr int RT = BM / 16;
 constexpr int GROUP = 64;
-constexpr int KS = 128;        // k per super-slab
-constexpr int MAX_EXPERTS = 4096;  // expert offsets staged in LDS (16 KiB at most)
+constexpr int KS = 128;  // k per super-slab
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 

@@ -55,8 +55,6 @@ __device__ __forceinline__ constexpr int pair_i(int e) {
 __device__ __forceinline__ constexpr int pair_j(int e) {
   return e < 6 ? (e < 3 ? e + 1 : (e < 5 ? e - 1 : 3)) : (e < 10 ? e - 6 : (e < 13 ? e - 9 : (e < 15 ? e - 11 : 3)));
 }
-constexpr int w_idx(int i, int j) { return SB_W + (i == 0 ? j - 1 : (i == 1 ? j + 1 : 5)); }
-constexpr int wq_idx(int i, int j) { return SB_WQ + (i == 0 ? j : (i == 1 ? j + 3 : (i == 2 ? j + 5 : 9))); }
 
 template <typename IO>
 __device__ __forceinline__ void to_f32(const uint4& raw, float* x) {
