@@ -54,6 +54,9 @@ epsilons), closed forms of softplus and sigmoid, and its scale invariances.
 The grouped GEMM on 4-bit weights is pinned by a hand-worked fixture (which
 fixes the nibble order and the bf16 rounding of a rebuilt weight), a
 brute-force triple loop, closed forms and the definition of bf16 rounding.
+Decode attention is pinned by a hand-worked fixture, closed forms (uniform
+scores give the mean value, a dominant key selects its value, two keys give
+a logistic weight), invariance to a shift of all scores and head sharing.
 No function here is "parity unpinned".
 """
 
@@ -72,6 +75,7 @@ __all__ = [
     "round_bf16",
     "dequantize_q4",
     "grouped_gemm_q4",
+    "decode_attention",
 ]
 
 
@@ -348,3 +352,49 @@ def grouped_gemm_q4(x, codes, scales, biases, expert_offsets, group=64):
             y[a:b] = x[a:b] @ w[e].T
     return y
 
+
+# ---------------------------------------------------------------- decode attention over a KV cache
+# Sections "Pack query heads to reuse KV rows" and "Switch attention layouts
+# at long contexts" (es: "Empaquetar los cabezales de consulta para reutilizar
+# las filas KV", "Cambiar los diseños de atención en contextos largos"; sk:
+# "Zbaľovanie hláv dopytu na opätovné použitie riadkov KV", "Prepínanie
+# rozložení pozornosti pri dlhých kontextoch"): a decode step of a
+# full-attention layer reads the whole KV cache; eight query heads share one
+# KV head (grouped-query attention, 16 query and 2 KV heads in the model the
+# pages describe), each head holds 256 values, and a fixed-block layout splits
+# the cache into equal parts processed in parallel.  Packing and the block
+# layout change how the work is scheduled, not what is computed.  Readings
+# taken: softmax attention with the scale passed in by the caller; query head
+# h reads KV head h // (h_q / h_kv) (contiguous groups); sequence b attends to
+# its first context_lens[b] cached positions, which include the current
+# token's key and value; an empty context gives a zero output.
+
+
+def decode_attention(q, k_cache, v_cache, context_lens, scale):
+    """One decode step of softmax attention over a KV cache (fp64).
+
+    q: [B, H_q, d]; k_cache, v_cache: [B, H_kv, T_max, d];
+    context_lens: [B] (0 <= len <= T_max).  Returns o [B, H_q, d] with
+    o[b, h] = sum_t softmax_t(scale * q[b, h] . k[b, j, t]) v[b, j, t] over
+    t < context_lens[b], j = h // (H_q / H_kv); zero where the context is empty.
+    """
+    q, k_cache, v_cache = (_as_f64(a) for a in (q, k_cache, v_cache))
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if h_kv <= 0 or h_q % h_kv != 0:
+        raise ValueError("h_q must be a multiple of h_kv")
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if lens.shape != (B,) or np.any(lens < 0) or np.any(lens > k_cache.shape[2]):
+        raise ValueError("context_lens must be in [0, T_max]")
+    group = h_q // h_kv
+    o = np.zeros((B, h_q, d))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(h_q):
+            j = h // group
+            s = scale * (k_cache[b, j, :n] @ q[b, h])
+            w = np.exp(s - s.max())
+            o[b, h] = (w / w.sum()) @ v_cache[b, j, :n]
+    return o

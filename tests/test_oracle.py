@@ -18,8 +18,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (dequantize_q4, gated_delta_chunk_form, gated_delta_decode_fused, gated_delta_decode_step,
-                    gated_delta_recurrence, grouped_gemm_q4, qk_head_of, round_bf16, sigmoid, softplus)
+from oracle import (decode_attention, dequantize_q4, gated_delta_chunk_form, gated_delta_decode_fused,
+                    gated_delta_decode_step, gated_delta_recurrence, grouped_gemm_q4, qk_head_of, round_bf16, sigmoid, softplus)
 from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -645,3 +645,140 @@ def test_q4_pins_catch_planted_mistakes(kind):
     f = load_q4_fixture()
     y = _q4_mutant(kind)(f["x"], f["codes"], f["scales"], f["biases"], f["offsets"])
     assert not np.allclose(y, f["y"])
+
+
+# ---------------------------------------------------------------- decode attention
+# Sections "Pack query heads to reuse KV rows" and "Switch attention layouts at
+# long contexts": grouped-query softmax attention over a KV cache.  Pinned by a
+# hand-worked fixture with rational answers, closed forms (uniform scores give
+# the mean value, a dominant key its own value, two keys a logistic weight from
+# scipy), invariance to shifting every score and to permuting the cached
+# positions, the contiguous head grouping, and planted mistakes.
+def load_attention_fixture():
+    vals = {}
+    with open(os.path.join(GOLDEN, "hand_worked_decode_attention.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rhs = (x.strip() for x in line.split("=", 1))
+            toks = [t.strip() for t in rhs.split(",")]
+            vals[key] = np.array([np.log(float(Fraction(t[3:-1]))) if t.startswith("ln(") else float(Fraction(t))
+                                  for t in toks])
+    return dict(q=vals["q"].reshape(2, 4, 2), k=vals["k"].reshape(2, 2, 3, 2), v=vals["v"].reshape(2, 2, 3, 2),
+                lens=vals["context_lens"].astype(np.int64), scale=float(vals["scale"][0]),
+                out=vals["out"].reshape(2, 4, 2))
+
+
+def test_golden_decode_attention():
+    f = load_attention_fixture()
+    o = decode_attention(f["q"], f["k"], f["v"], f["lens"], f["scale"])
+    np.testing.assert_allclose(o, f["out"], rtol=1e-13, atol=1e-13)
+
+
+def _attn_problem(seed, B=2, h_q=8, h_kv=2, T=20, d=6):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(B, h_q, d)), rng.normal(size=(B, h_kv, T, d)), rng.normal(size=(B, h_kv, T, d)),
+            rng.integers(1, T + 1, size=B))
+
+
+def test_attention_closed_forms():
+    from scipy.special import expit
+    q, k, v, lens = _attn_problem(1)
+    # scale 0 (or q = 0): every position weighs the same -> the mean of the cached values
+    o = decode_attention(q, k, v, lens, 0.0)
+    for b in range(2):
+        for h in range(8):
+            np.testing.assert_allclose(o[b, h], v[b, h // 4, :lens[b]].mean(axis=0), rtol=1e-12, atol=1e-14)
+    # one key far above the rest takes all the weight, even past fp64's exp range
+    k2 = k.copy()
+    k2[:, :, 3] = 0.0
+    q2 = np.zeros_like(q)
+    q2[..., 0] = 1.0
+    k2[:, :, 3, 0] = 900.0
+    o = decode_attention(q2, k2, v, np.array([20, 20]), 1.0)
+    for h in range(8):
+        np.testing.assert_allclose(o[:, h], v[:, h // 4, 3], rtol=1e-12)
+    # two positions: o = sigmoid(s1 - s2) v1 + (1 - sigmoid(s1 - s2)) v2
+    o = decode_attention(q, k, v, np.array([2, 2]), 0.7)
+    for b in range(2):
+        for h in range(8):
+            j = h // 4
+            w = expit(0.7 * (q[b, h] @ k[b, j, 0] - q[b, h] @ k[b, j, 1]))
+            np.testing.assert_allclose(o[b, h], w * v[b, j, 0] + (1 - w) * v[b, j, 1], rtol=1e-12, atol=1e-14)
+    # an empty context gives zeros; the value of a one-position context is returned as is
+    o = decode_attention(q, k, v, np.array([0, 1]), 1.0)
+    np.testing.assert_array_equal(o[0], 0.0)
+    np.testing.assert_allclose(o[1], np.repeat(v[1, :, 0], 4, axis=0), rtol=1e-15)
+
+
+def test_attention_invariances():
+    q, k, v, lens = _attn_problem(2, d=5)
+    base = decode_attention(q, k, v, lens, 0.4)
+    # shifting every score of a head by c: an extra coordinate with k = 1 and q = c / scale
+    c = np.random.default_rng(3).normal(size=(2, 8)) * 1000.0
+    q_ext = np.concatenate([q, (c / 0.4)[..., None]], axis=-1)
+    k_ext = np.concatenate([k, np.ones(k.shape[:-1] + (1,))], axis=-1)
+    v_ext = np.concatenate([v, np.zeros(v.shape[:-1] + (1,))], axis=-1)
+    np.testing.assert_allclose(decode_attention(q_ext, k_ext, v_ext, lens, 0.4)[..., :5], base, rtol=1e-9, atol=1e-12)
+    # permuting the cached positions (keys and values together) changes nothing
+    T = k.shape[2]
+    lens_full = np.array([T, T])
+    full = decode_attention(q, k, v, lens_full, 0.4)
+    perm = np.random.default_rng(4).permutation(T)
+    np.testing.assert_allclose(decode_attention(q, k[:, :, perm], v[:, :, perm], lens_full, 0.4), full,
+                               rtol=1e-12, atol=1e-14)
+    # positions past the context are never read, whatever they hold
+    k_nan, v_nan = k.copy(), v.copy()
+    for b in range(2):
+        k_nan[b, :, lens[b]:] = np.nan
+        v_nan[b, :, lens[b]:] = np.inf
+    np.testing.assert_array_equal(decode_attention(q, k_nan, v_nan, lens, 0.4), base)
+    # contiguous head groups: sharing 2 KV heads equals 8 KV heads repeated in blocks of 4
+    np.testing.assert_array_equal(decode_attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), lens, 0.4),
+                                  base)
+    # scale folds into q
+    np.testing.assert_allclose(decode_attention(0.4 * q, k, v, lens, 1.0), base, rtol=1e-12, atol=1e-14)
+
+
+def _attn_mutant(kind):
+    def run(q, k, v, lens, scale):
+        B, h_q, d = q.shape
+        h_kv = k.shape[1]
+        o = np.zeros((B, h_q, d))
+        for b in range(B):
+            n = int(lens[b]) + (1 if kind == "one_past_context" else 0)
+            for h in range(h_q):
+                j = h % h_kv if kind == "interleaved_heads" else h // (h_q // h_kv)
+                kk, vv = (v, k) if kind == "keys_values_swapped" else (k, v)
+                sc = 1.0 / np.sqrt(d) if kind == "fixed_scale" else scale
+                s = sc * (kk[b, j, :n] @ q[b, h])
+                if kind == "no_max_shift":
+                    w = np.exp(s)
+                else:
+                    w = np.exp(s - s.max())
+                if kind == "unnormalised":
+                    o[b, h] = w @ vv[b, j, :n]
+                else:
+                    o[b, h] = (w / w.sum()) @ vv[b, j, :n]
+        return o
+    return run
+
+
+@pytest.mark.parametrize("kind", ["one_past_context", "interleaved_heads", "keys_values_swapped", "fixed_scale",
+                                  "unnormalised", "no_max_shift"])
+def test_attention_pins_catch_planted_mistakes(kind):
+    fn = _attn_mutant(kind)
+    f = load_attention_fixture()
+    caught = False
+    with np.errstate(all="ignore"):
+        o = fn(f["q"], f["k"], f["v"], f["lens"], f["scale"])
+        caught |= not np.allclose(o, f["out"])
+        q, k, v, lens = _attn_problem(1)
+        caught |= not np.allclose(fn(q, k, v, lens, 0.0)[0, 0], v[0, 0, :lens[0]].mean(axis=0))
+        k2, q2 = np.zeros_like(k), np.zeros_like(q)
+        q2[..., 0] = 1.0
+        k2[:, :, 3, 0] = 900.0
+        o2 = fn(q2, k2, v, np.array([20, 20]), 1.0)
+        caught |= not np.allclose(o2[:, 0], v[:, 0, 3])
+    assert caught
