@@ -5,7 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -379,6 +381,113 @@ gdn_status_t gdn_moe_gemm_bf16(const gdn_moe_shape_t* shape, const void* x, cons
   }
   return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets,
                                        weights, nullptr, nullptr, y, false, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+// ---------------------------------------------------------------- decode attention
+struct AttnPlan {
+  gdn::AttnDims d;
+  float scale;
+  bool fixed_block;
+  int hp, nb;
+};
+
+// Compute units of the current device (256 on MI355X, also the fallback).
+static int device_cu_count() {
+  static std::atomic<int> cache[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 16) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 16) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static gdn_status_t attn_plan(const gdn_attn_shape_t* s, const gdn_attn_params_t* p, const char* what,
+                              AttnPlan& plan) {
+  if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
+  if (s->batch < 1) return fail(GDN_ERR_INVALID, "%s: batch must be >= 1", what);
+  if (s->h_kv < 1 || s->h_q < s->h_kv || s->h_q % s->h_kv != 0)
+    return fail(GDN_ERR_INVALID, "%s: h_q (%d) must be a positive multiple of h_kv (%d)", what, s->h_q, s->h_kv);
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: head_dim %d; supported sizes are 64, 128, 256", what, s->head_dim);
+  if (s->max_context < 1 || s->max_context > (1 << 24))
+    return fail(GDN_ERR_INVALID, "%s: max_context must be in [1, 2^24] (got %d)", what, s->max_context);
+  if ((long long)s->batch * s->h_q > (1ll << 24))
+    return fail(GDN_ERR_UNSUPPORTED, "%s: batch * h_q too large", what);
+  gdn_attn_params_t d{1.0f / std::sqrt(float(s->head_dim)), GDN_ATTN_AUTO, 0, 0};
+  if (p) d = *p;
+  if (!std::isfinite(d.scale)) return fail(GDN_ERR_INVALID, "%s: scale must be finite", what);
+  const int group = s->h_q / s->h_kv;
+  int hp = d.heads_per_group;
+  if (hp == 0) {
+    hp = 8;
+    while (group % hp) hp /= 2;
+  } else if ((hp != 1 && hp != 2 && hp != 4 && hp != 8) || group % hp) {
+    return fail(GDN_ERR_INVALID, "%s: heads_per_group %d must be 0, or 1, 2, 4 or 8 dividing h_q / h_kv = %d",
+                what, d.heads_per_group, group);
+  }
+  const long long base = (long long)s->batch * s->h_kv * (group / hp);
+  // automatic part count: one workgroup per compute unit, parts of at least 32 positions
+  const long long n_cu = device_cu_count();
+  const int nb_auto = int(std::max(1ll, std::min({(n_cu + base - 1) / base, (s->max_context + 31ll) / 32, 4096ll})));
+  bool fixed;
+  switch (d.layout) {
+    case GDN_ATTN_GENERAL: fixed = false; break;
+    case GDN_ATTN_FIXED_BLOCK: fixed = true; break;
+    case GDN_ATTN_AUTO: fixed = nb_auto > 1; break;
+    default: return fail(GDN_ERR_INVALID, "%s: layout %d is not a gdn_attn_layout_t", what, d.layout);
+  }
+  int nb = 1;
+  if (fixed) {
+    if (d.num_blocks < 0 || d.num_blocks > std::min(s->max_context, 4096))
+      return fail(GDN_ERR_INVALID, "%s: num_blocks must be in [0, min(max_context, 4096)] (got %d)", what,
+                  d.num_blocks);
+    nb = d.num_blocks > 0 ? d.num_blocks : nb_auto;
+  }
+  if (base * nb > (1ll << 31) - 1) return fail(GDN_ERR_UNSUPPORTED, "%s: too many workgroups", what);
+  plan.d = gdn::AttnDims{s->batch, s->h_q, s->h_kv, s->head_dim, s->max_context};
+  plan.scale = d.scale;
+  plan.fixed_block = fixed;
+  plan.hp = hp;
+  plan.nb = nb;
+  return GDN_OK;
+}
+
+size_t gdn_attention_decode_workspace(const gdn_attn_shape_t* shape, const gdn_attn_params_t* params) {
+  AttnPlan plan;
+  if (attn_plan(shape, params, "gdn_attention_decode_workspace", plan) != GDN_OK) return 0;
+  return plan.fixed_block ? gdn::attn_workspace_bytes(plan.d, plan.nb) : 0;
+}
+
+gdn_status_t gdn_attention_decode(const gdn_attn_shape_t* shape, const gdn_attn_params_t* params, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* context_lens, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "gdn_attention_decode";
+  AttnPlan plan;
+  gdn_status_t st = attn_plan(shape, params, what, plan);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"q", q}, {"k_cache", k_cache}, {"v_cache", v_cache}, {"out", out}});
+  if (st != GDN_OK) return st;
+  if (!context_lens) return fail(GDN_ERR_INVALID, "%s: context_lens is NULL", what);
+  if (reinterpret_cast<uintptr_t>(context_lens) & 3u)
+    return fail(GDN_ERR_INVALID, "%s: context_lens is not 4-byte aligned", what);
+  if (out == q || out == k_cache || out == v_cache || out == context_lens)
+    return fail(GDN_ERR_INVALID, "%s: out aliases an input", what);
+  if (plan.fixed_block) {
+    const size_t need = gdn::attn_workspace_bytes(plan.d, plan.nb);
+    if (!workspace) return fail(GDN_ERR_INVALID, "%s: workspace is NULL", what);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(GDN_ERR_INVALID, "%s: workspace is not 256-byte aligned", what);
+    if (workspace_bytes < need)
+      return fail(GDN_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", what, workspace_bytes, need);
+  }
+  return launched(gdn::launch_attn_decode(plan.d, plan.scale, plan.fixed_block, plan.hp, plan.nb, q, k_cache,
+                                          v_cache, context_lens, out, workspace, static_cast<hipStream_t>(stream)),
                   what);
 }
 

@@ -1,0 +1,373 @@
+// Decode attention over a grouped-query KV cache.
+//
+// Perplexity, "Optimizing on-device inference for Apple Silicon", sections
+// "Pack query heads to reuse KV rows" and "Switch attention layouts at long
+// contexts": in a decode step of a full-attention layer every query head reads
+// the whole KV cache of its KV head, and the query heads of one group (eight
+// in the model described there) read the same rows.  Packing several query
+// heads into one workgroup loads each KV row once for all of them; the
+// fixed-block layout splits each context into equal parts that run in
+// parallel and are merged afterwards.  Neither changes the result.
+//
+// o[b, h] = sum_t softmax_t(scale q[b, h] . k[b, j, t]) v[b, j, t] over the
+// first context_lens[b] positions, j = h / (h_q / h_kv).
+//
+// One workgroup of four waves serves HP query heads of one KV head over a
+// range of positions (the whole context in the general layout, one of nb
+// equal parts in the fixed-block layout).  Wave w takes the 16-position tiles
+// w, w + 4, ... of that range.  Per tile:
+//   * scores on the matrix unit: S[16 positions, 16 columns] = K_tile Q^T with
+//     v_mfma_f32_16x16x32_bf16; the key rows are the A fragments, loaded
+//     straight from memory (lane = 16 grp + row holds 8 consecutive values of
+//     one key row per 32-wide slab), the HP queries are the B fragments, held
+//     in registers for the whole range (columns past HP are zero);
+//   * an online softmax per head in base 2 (scores times scale * log2 e): the
+//     running maximum m, the rescale factor 2^(m_old - m_new), the
+//     probabilities p and a per-lane partial sum l of them;
+//   * p and the rescale factors go through a small LDS buffer of the wave and
+//     the value rows are applied on the vector ALU in fp32: lane cq of a token
+//     row owns four value columns, so a 256-wide row is one 8-byte load per
+//     lane (for narrower heads 256 / d positions share a load instruction).
+// The waves' (m, l, o) are merged through LDS at the end.  The general layout
+// divides by l and writes bf16; the fixed-block layout writes the part's
+// (m, l, o) in fp32 and attn_combine_kernel merges the parts of each head.
+// Every head's arithmetic is the same whatever HP is, so packed and unpacked
+// launches give the same bytes.
+#include "gdn_common.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 16;  // positions per wave step
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+struct AttnArgs {
+  const uint16_t* q;     // [B, h_q, DK]
+  const uint16_t* k;     // [B, h_kv, t_max, DK]
+  const uint16_t* v;     // [B, h_kv, t_max, DK]
+  const int32_t* lens;   // [B]
+  uint16_t* out;         // [B, h_q, DK]         (general layout)
+  float* part_o;         // [B, h_q, nb, DK]     (fixed-block layout)
+  float* part_ml;        // [B, h_q, nb, 2]
+  int h_q, h_kv, t_max, group, packs, nb;
+  float c;               // scale * log2(e)
+};
+
+__device__ __forceinline__ f4 mfma_kq(v4u a, v4u b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0,
+                                                 0);
+}
+
+// LDS written by some lanes of a wave and read by others of the same wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int DK, int HP, bool PARTIAL>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+  static_assert(DK == 64 || DK == 128 || DK == 256, "head size");
+  static_assert(HP == 1 || HP == 2 || HP == 4 || HP == 8, "heads per workgroup");
+  constexpr int KS = DK / 32;      // 32-wide slabs of the score product
+  constexpr int LPT = DK / 4;      // lanes per value row
+  constexpr int TP = 64 / LPT;     // value rows per load instruction
+  constexpr int TPL = kTile / TP;  // value rows per lane and tile
+
+  __shared__ float sp[kWaves][HP][kTile];  // probabilities, [head][position]
+  __shared__ float sa[kWaves][HP];         // rescale factors
+  __shared__ float sm[kWaves][HP], sl[kWaves][HP];
+  __shared__ __align__(16) float so[kWaves][HP][DK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int wg = blockIdx.x;
+  const int blk = wg % a.nb;
+  wg /= a.nb;
+  const int pk = wg % a.packs;
+  wg /= a.packs;
+  const int j = wg % a.h_kv, b = wg / a.h_kv;
+  const int h0 = j * a.group + pk * HP;
+
+  int len = a.lens[b];
+  len = len < 0 ? 0 : (len > a.t_max ? a.t_max : len);
+  int start = 0, end = len;
+  if (PARTIAL) {
+    const int part = ((len + a.nb - 1) / a.nb + kTile - 1) / kTile * kTile;
+    start = min(blk * part, len);
+    end = min(start + part, len);
+  }
+  const size_t kv_off = (size_t(b) * a.h_kv + j) * size_t(a.t_max) * DK;
+  const uint16_t* kb = a.k + kv_off;
+  const uint16_t* vb = a.v + kv_off;
+
+  const int col = lane & 15, grp = lane >> 4;  // fragment coordinates
+  const int tp = lane / LPT, cq = lane % LPT;  // value-row coordinates
+
+  v4u qf[KS];
+  {
+    const uint16_t* qp = a.q + (size_t(b) * a.h_q + h0 + (col < HP ? col : 0)) * DK + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = col < HP ? *reinterpret_cast<const v4u*>(qp + 32 * kk) : v4u{0, 0, 0, 0};
+  }
+
+  float o[HP][4];
+#pragma unroll
+  for (int h = 0; h < HP; ++h) o[h][0] = o[h][1] = o[h][2] = o[h][3] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Tile loads: key rows as A fragments, value rows four columns per lane.
+  // Rows past the range are clamped to its last row (read, then masked).
+  auto load_tile = [&](int t0, v4u (&kf)[KS], v2u (&vf)[TPL]) {
+    const int tr = min(t0 + col, end - 1);
+    const uint16_t* kp = kb + size_t(tr) * DK + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = *reinterpret_cast<const v4u*>(kp + 32 * kk);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const int tv = min(t0 + TP * i + tp, end - 1);
+      vf[i] = *reinterpret_cast<const v2u*>(vb + size_t(tv) * DK + 4 * cq);
+    }
+  };
+
+  v4u kf[KS];
+  v2u vf[TPL];
+  if (start + wave * kTile < end) load_tile(start + wave * kTile, kf, vf);
+  for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
+    // the next tile's rows are in flight while this one is processed
+    v4u kn[KS];
+    v2u vn[TPL];
+    load_tile(t0 + kWaves * kTile, kn, vn);
+
+    f4 s = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) s = mfma_kq(kf[kk], qf[kk], s);
+
+    // lane (col, grp) holds the scores of head col at positions t0 + 4 grp + r
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = t0 + 4 * grp + r < end ? s[r] * a.c : -INFINITY;
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float al = exp2_(m_run - m_use);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = exp2_(x[r] - m_use);
+    l_run = l_run * al + ((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    if (col < HP) {
+      *reinterpret_cast<f4*>(&sp[wave][col][4 * grp]) = f4{p[0], p[1], p[2], p[3]};
+      if (grp == 0) sa[wave][col] = al;
+    }
+    wave_sync();
+
+#pragma unroll
+    for (int h = 0; h < HP; ++h) {
+      const float ah = sa[wave][h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[h][e] *= ah;
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const float v0 = __uint_as_float(vf[i].x << 16), v1 = __uint_as_float(vf[i].x & 0xffff0000u);
+      const float v2 = __uint_as_float(vf[i].y << 16), v3 = __uint_as_float(vf[i].y & 0xffff0000u);
+#pragma unroll
+      for (int h = 0; h < HP; ++h) {
+        const float ph = sp[wave][h][TP * i + tp];
+        o[h][0] = fmaf(ph, v0, o[h][0]);
+        o[h][1] = fmaf(ph, v1, o[h][1]);
+        o[h][2] = fmaf(ph, v2, o[h][2]);
+        o[h][3] = fmaf(ph, v3, o[h][3]);
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = kn[kk];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) vf[i] = vn[i];
+  }
+
+  // per-wave totals: l over the four lane groups, o over the value-row groups
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int sft = LPT; sft < 64; sft <<= 1)
+#pragma unroll
+    for (int h = 0; h < HP; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[h][e] += __shfl_xor(o[h][e], sft);
+  if (col < HP && grp == 0) {
+    sm[wave][col] = m_run;
+    sl[wave][col] = l_run;
+  }
+  if (tp == 0) {
+#pragma unroll
+    for (int h = 0; h < HP; ++h) *reinterpret_cast<f4*>(&so[wave][h][4 * cq]) = f4{o[h][0], o[h][1], o[h][2], o[h][3]};
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < HP * LPT; idx += 256) {
+    const int h = idx / LPT, c4 = idx % LPT;
+    float mx = sm[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm[w][h]);
+    float L = 0.f;
+    f4 O = zero4();
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = exp2_(sm[w][h] - mx);
+        L += wt * sl[w][h];
+        const f4 ow = *reinterpret_cast<const f4*>(&so[w][h][4 * c4]);
+        O += wt * ow;
+      }
+    }
+    const size_t row = size_t(b) * a.h_q + h0 + h;
+    if (PARTIAL) {
+      const size_t pr = row * a.nb + blk;
+      *reinterpret_cast<f4*>(a.part_o + pr * DK + 4 * c4) = O;
+      if (c4 == 0) *reinterpret_cast<f2v*>(a.part_ml + pr * 2) = f2v{mx, L};
+    } else {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      *reinterpret_cast<v2u*>(a.out + row * DK + 4 * c4) =
+          v2u{pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
+    }
+  }
+}
+
+// Merge the nb parts of each (sequence, query head): workgroup (row, chunk)
+// owns 64 output columns of one row.  The largest part maximum M and the
+// weights 2^(m_c - M) come first (every workgroup of the row recomputes them
+// from the nb (m, l) pairs), then sixteen slices of parts, each 16 lanes x 4
+// columns, sum weight x partial output with independent loads, and the
+// slices are added through LDS.
+constexpr int kMaxParts = 4096;
+
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, const float* part_ml, uint16_t* out,
+                                                           int nb, int dk) {
+  __shared__ float sw[kMaxParts];
+  __shared__ float red[2][kWaves];
+  __shared__ __align__(16) float co[16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunks = dk / 64;
+  const size_t row = blockIdx.x / chunks;
+  const int c0 = (blockIdx.x % chunks) * 64;
+  const float* pml = part_ml + row * nb * 2;
+
+  float mx = -INFINITY;
+  for (int c = tid; c < nb; c += 256) mx = fmaxf(mx, pml[2 * c]);
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float L = 0.f;
+  for (int c = tid; c < nb; c += 256) {
+    const f2v ml = *reinterpret_cast<const f2v*>(pml + 2 * c);
+    const float w = (mx == -INFINITY || ml[0] == -INFINITY) ? 0.f : exp2_(ml[0] - mx);
+    sw[c] = w;
+    L += w * ml[1];
+  }
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) L += __shfl_xor(L, sft);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+
+  const int slice = tid >> 4, c4 = tid & 15;
+  const float* po = part_o + row * nb * size_t(dk) + c0 + 4 * c4;
+  f4 O = zero4();
+#pragma unroll 4
+  for (int c = slice; c < nb; c += 16) O += sw[c] * *reinterpret_cast<const f4*>(po + size_t(c) * dk);
+  *reinterpret_cast<f4*>(&co[slice][4 * c4]) = O;
+  __syncthreads();
+  if (tid < 16) {
+    f4 Ot = zero4();
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) Ot += *reinterpret_cast<const f4*>(&co[sl][4 * tid]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<v2u*>(out + row * dk + c0 + 4 * tid) =
+        v2u{pack_bf16x2(Ot[0] * inv, Ot[1] * inv), pack_bf16x2(Ot[2] * inv, Ot[3] * inv)};
+  }
+}
+
+template <int DK, int HP>
+hipError_t launch_attn_t(const AttnDims& d, const AttnArgs& a, bool fixed_block, hipStream_t st) {
+  const unsigned blocks = unsigned(size_t(d.batch) * d.h_kv * a.packs * a.nb);
+  if (fixed_block) {
+    {
+      Prof prof("attn_decode_parts", st);
+      hipLaunchKernelGGL((attn_decode_kernel<DK, HP, true>), dim3(blocks), dim3(256), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    Prof prof("attn_combine", st);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(size_t(d.batch) * d.h_q * (DK / 64))), dim3(256), 0, st,
+                       a.part_o, a.part_ml, a.out, a.nb, DK);
+    return hipGetLastError();
+  }
+  Prof prof("attn_decode", st);
+  hipLaunchKernelGGL((attn_decode_kernel<DK, HP, false>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_attn_dk(const AttnDims& d, const AttnArgs& a, int hp, bool fixed_block, hipStream_t st) {
+  switch (hp) {
+    case 1: return launch_attn_t<DK, 1>(d, a, fixed_block, st);
+    case 2: return launch_attn_t<DK, 2>(d, a, fixed_block, st);
+    case 4: return launch_attn_t<DK, 4>(d, a, fixed_block, st);
+    default: return launch_attn_t<DK, 8>(d, a, fixed_block, st);
+  }
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(const AttnDims& d, int nb) {
+  const size_t rows = size_t(d.batch) * d.h_q * size_t(nb);
+  const size_t o_bytes = (rows * d.head_dim * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * 2 * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const AttnDims& d, float scale, bool fixed_block, int hp, int nb, const void* q,
+                              const void* k, const void* v, const int32_t* lens, void* out, void* workspace,
+                              hipStream_t st) {
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.lens = lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.h_q = d.h_q;
+  a.h_kv = d.h_kv;
+  a.t_max = d.t_max;
+  a.group = d.h_q / d.h_kv;
+  a.packs = a.group / hp;
+  a.nb = fixed_block ? nb : 1;
+  a.c = scale * 1.4426950408889634f;
+  if (fixed_block) {
+    const size_t rows = size_t(d.batch) * d.h_q * size_t(nb);
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         (rows * d.head_dim * sizeof(float) + 255) / 256 * 256);
+  } else {
+    a.part_o = a.part_ml = nullptr;
+  }
+  switch (d.head_dim) {
+    case 64: return launch_attn_dk<64>(d, a, hp, fixed_block, st);
+    case 128: return launch_attn_dk<128>(d, a, hp, fixed_block, st);
+    default: return launch_attn_dk<256>(d, a, hp, fixed_block, st);
+  }
+}
+
+}  // namespace gdn

@@ -71,4 +71,15 @@ hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const 
 hipError_t launch_dequant_q4(int n_exp, int n, int k, const void* codes, const void* scales, const void* biases,
                              void* w, hipStream_t st);
 
+// Decode attention over a grouped-query KV cache: hp query heads per
+// workgroup; the fixed-block layout splits each context into nb equal parts
+// whose partial results go to the workspace and are merged by a second kernel.
+struct AttnDims {
+  int batch, h_q, h_kv, head_dim, t_max;
+};
+size_t attn_workspace_bytes(const AttnDims& d, int nb);
+hipError_t launch_attn_decode(const AttnDims& d, float scale, bool fixed_block, int hp, int nb, const void* q,
+                              const void* k, const void* v, const int32_t* lens, void* out, void* workspace,
+                              hipStream_t st);
+
 }  // namespace gdn

@@ -21,8 +21,11 @@ GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_scan_blockwise", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace",
            "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_decode_step", "gdn_decode_step_fused",
-           "gdn_moe_gemm_q4", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_profile_enable", "gdn_profile_collect",
-           "gdn_status_string", "gdn_last_error")
+           "gdn_moe_gemm_q4", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_attention_decode",
+           "gdn_attention_decode_workspace", "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string",
+           "gdn_last_error")
+GDN_ATTN_AUTO, GDN_ATTN_GENERAL, GDN_ATTN_FIXED_BLOCK = 0, 1, 2
+ATTN_LAYOUTS = {"auto": GDN_ATTN_AUTO, "general": GDN_ATTN_GENERAL, "fixed_block": GDN_ATTN_FIXED_BLOCK}
 
 
 class GdnShape(ctypes.Structure):
@@ -39,6 +42,16 @@ class GdnFusedParams(ctypes.Structure):
 class GdnMoeShape(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("rows", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("n", ctypes.c_int32)]
+
+
+class GdnAttnShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_context", ctypes.c_int32)]
+
+
+class GdnAttnParams(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("layout", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -85,6 +98,11 @@ def load_library(path: str | None = None):
     lib.gdn_dequant_q4.restype = ctypes.c_int
     lib.gdn_moe_gemm_bf16.argtypes = [mshp, vp, vp, vp, vp, vp]
     lib.gdn_moe_gemm_bf16.restype = ctypes.c_int
+    ashp, apar = ctypes.POINTER(GdnAttnShape), ctypes.POINTER(GdnAttnParams)
+    lib.gdn_attention_decode_workspace.argtypes = [ashp, apar]
+    lib.gdn_attention_decode_workspace.restype = ctypes.c_size_t
+    lib.gdn_attention_decode.argtypes = [ashp, apar, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gdn_attention_decode.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [ctypes.c_int]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
@@ -376,6 +394,57 @@ def moe_gemm_bf16(x, expert_offsets, weights, y=None, stream=None):
     _check(lib.gdn_moe_gemm_bf16(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(weights), _ptr(y),
                                  _stream(stream)))
     return y
+
+
+def _attn_params(head_dim, scale, layout, heads_per_group, num_blocks):
+    if layout not in ATTN_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(ATTN_LAYOUTS)}")
+    sc = 1.0 / head_dim ** 0.5 if scale is None else float(scale)
+    return GdnAttnParams(sc, ATTN_LAYOUTS[layout], int(heads_per_group), int(num_blocks))
+
+
+def attention_decode_workspace_bytes(batch, h_q, h_kv, head_dim, max_context, scale=None, layout="auto",
+                                     heads_per_group=0, num_blocks=0):
+    lib = load_library()
+    shape = GdnAttnShape(batch, h_q, h_kv, head_dim, max_context)
+    params = _attn_params(head_dim, scale, layout, heads_per_group, num_blocks)
+    return int(lib.gdn_attention_decode_workspace(ctypes.byref(shape), ctypes.byref(params)))
+
+
+def attention_decode(q, k_cache, v_cache, context_lens, scale=None, layout="auto", heads_per_group=0, num_blocks=0,
+                     out=None, workspace=None, stream=None):
+    """Decode attention over a grouped-query KV cache (gdn_attention_decode).
+    q [B, h_q, d] bf16; k_cache, v_cache [B, h_kv, T_max, d] bf16;
+    context_lens [B] int32.  ``layout`` is "auto", "general" or
+    "fixed_block"; scale None means 1 / sqrt(d).  Returns out [B, h_q, d]
+    bf16."""
+    lib = load_library()
+    if k_cache.dim() != 4 or q.dim() != 3:
+        raise ValueError("q must be [B, h_q, d] and k_cache [B, h_kv, T_max, d]")
+    B, h_kv, T, d = k_cache.shape
+    h_q = q.shape[1]
+    _need(q, "q", torch.bfloat16, (B, h_q, d))
+    _need(k_cache, "k_cache", torch.bfloat16, (B, h_kv, T, d))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, h_kv, T, d))
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, (B, h_q, d))
+    shape = GdnAttnShape(B, h_q, h_kv, d, T)
+    params = _attn_params(d, scale, layout, heads_per_group, num_blocks)
+    need = int(lib.gdn_attention_decode_workspace(ctypes.byref(shape), ctypes.byref(params)))
+    wp, wn = 0, 0
+    if need > 0:
+        if workspace is None:
+            workspace = alloc_workspace(need, q.device)
+        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+            raise TypeError("workspace must be a uint8 GPU tensor")
+        wp, wn = _aligned_ptr(workspace)
+    _check(lib.gdn_attention_decode(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(context_lens), _ptr(out), ctypes.c_void_p(wp),
+                                    ctypes.c_size_t(max(wn, 0)), _stream(stream)))
+    return out
 
 
 def profile_enable(enabled: bool = True):

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Inputs", "DecodeInputs", "RawDecodeInputs", "round_to_bf16", "make_prefill", "make_decode",
-           "make_decode_raw", "MoeInputs", "make_moe", "config"]
+           "make_decode_raw", "MoeInputs", "make_moe", "AttentionInputs", "make_attention", "attention_device",
+           "config"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -246,6 +247,55 @@ def make_moe(tokens, num_experts=256, top_k=8, k=2048, n=1024, weight_std=0.02, 
     biases = round_to_bf16(-rngs / np.float32(2.0) + shift)
     return MoeInputs(xt[token_of_row], offsets, codes, scales, biases, token_of_row,
                      dict(tokens=tokens, num_experts=num_experts, top_k=top_k, k=k, n=n, skew=skew, seed=seed))
+
+
+@dataclass
+class AttentionInputs:
+    """One decode step of grouped-query attention over a KV cache (sections
+    "Pack query heads to reuse KV rows" and "Switch attention layouts at long
+    contexts": 16 query heads, 2 KV heads, 256 values per head in the model
+    described there).  q [B, h_q, d]; k_cache, v_cache [B, h_kv, T_max, d]
+    (bf16 values in float32 arrays); context_lens [B]; scale 1 / sqrt(d)."""
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    context_lens: np.ndarray
+    scale: float
+
+
+def make_attention(context_lens, h_q=16, h_kv=2, head_dim=256, max_context=None, seed=0, rng=None):
+    """Entries N(0, 1) rounded to bf16, so that scale * q . k is about N(0, 1);
+    positions past a context hold random values too (they must not be read)."""
+    rng = rng or np.random.default_rng(seed)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    B = len(lens)
+    T = int(max_context if max_context is not None else max(1, int(lens.max(initial=1))))
+    q = round_to_bf16(rng.standard_normal((B, h_q, head_dim), dtype=np.float32))
+    k = round_to_bf16(rng.standard_normal((B, h_kv, T, head_dim), dtype=np.float32))
+    v = round_to_bf16(rng.standard_normal((B, h_kv, T, head_dim), dtype=np.float32))
+    return AttentionInputs(q, k, v, lens, 1.0 / math.sqrt(head_dim))
+
+
+def attention_device(context_lens, h_q=16, h_kv=2, head_dim=256, max_context=None, seed=0, device="cuda"):
+    """The same distribution drawn on the device (for caches of hundreds of
+    MiB): returns bf16 torch tensors q, k_cache, v_cache, int32 context_lens
+    and the scale."""
+    import torch
+
+    lens = [int(x) for x in context_lens]
+    T = int(max_context if max_context is not None else max(1, max(lens)))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B = len(lens)
+    q = torch.randn((B, h_q, head_dim), generator=gen, device=device).to(torch.bfloat16)
+    k = torch.empty((B, h_kv, T, head_dim), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    for t in (k, v):  # drawn a slice at a time to bound the fp32 temporary
+        for b in range(B):
+            for j in range(h_kv):
+                t[b, j] = torch.randn((T, head_dim), generator=gen, device=device).to(torch.bfloat16)
+    cl = torch.tensor(lens, dtype=torch.int32, device=device)
+    return q, k, v, cl, 1.0 / math.sqrt(head_dim)
 
 
 def ragged_lengths(rng, n, lo=256, hi=8192):

@@ -272,6 +272,78 @@ gdn_status_t gdn_moe_gemm_bf16(const gdn_moe_shape_t* shape, const void* x, cons
                                const void* weights, void* y, void* stream);
 
 /*
+ * Decode attention over a grouped-query KV cache (sections "Pack query heads
+ * to reuse KV rows" and "Switch attention layouts at long contexts": in a
+ * decode step of a full-attention layer each query head reads its KV head's
+ * whole cache; eight query heads share one KV head in the model described
+ * there, each head holds 256 values, and past 32K positions a fixed-block
+ * layout splits the cache into equal parts processed in parallel).  Per
+ * sequence b and query head h, with j = h / (h_q / h_kv) and
+ * n = context_lens[b]:
+ *
+ *     o[b, h] = sum_{t < n} softmax_t(scale * q[b, h] . k[b, j, t]) v[b, j, t]
+ *
+ * and o[b, h] = 0 when n = 0.  The caller has already written the current
+ * token's key and value at position n - 1.  Scores, the softmax and the sums
+ * are fp32 (products of bf16 inputs are exact); the output is rounded once to
+ * bf16.  Shapes (dense, last index fastest, 16-byte aligned):
+ *     q              [batch, h_q, head_dim]              bf16
+ *     k_cache,
+ *     v_cache        [batch, h_kv, max_context, head_dim] bf16
+ *     context_lens   [batch] int32, device, 4-byte aligned; each value is
+ *                    clamped to [0, max_context] on the device
+ *     out            [batch, h_q, head_dim]              bf16, aliasing no input
+ * head_dim is 64, 128 or 256; h_q is a multiple of h_kv; max_context is at
+ * most 2^24.
+ *
+ * Scheduling, which changes no value beyond fp32 summation order:
+ *  - heads_per_group query heads of one KV head share a workgroup, which
+ *    loads each key and value row once for all of them (1, 2, 4 or 8,
+ *    dividing h_q / h_kv; 0 = the largest of those that divides it).  The
+ *    output bytes do not depend on it.
+ *  - GDN_ATTN_GENERAL: one workgroup per (sequence, KV head, head pack)
+ *    walks the whole context; no workspace.  GDN_ATTN_FIXED_BLOCK: each
+ *    context is cut into num_blocks equal parts (0 = chosen from the shape
+ *    and the device's compute-unit count), one workgroup each, and a second
+ *    kernel merges the parts; it needs gdn_attention_decode_workspace()
+ *    bytes of 256-byte aligned device workspace.  The automatic part count
+ *    is min(ceil(CUs / (batch * h_kv * packs)), ceil(max_context / 32)),
+ *    with CUs the current device's compute units and packs = h_q / h_kv /
+ *    heads_per_group.  GDN_ATTN_AUTO takes the fixed-block layout when that
+ *    count exceeds 1, i.e. when one workgroup per head pack would leave
+ *    compute units idle.
+ */
+typedef enum {
+  GDN_ATTN_AUTO = 0,
+  GDN_ATTN_GENERAL = 1,
+  GDN_ATTN_FIXED_BLOCK = 2
+} gdn_attn_layout_t;
+
+typedef struct {
+  int32_t batch;        /* sequences, >= 1 */
+  int32_t h_q;          /* query heads, a multiple of h_kv */
+  int32_t h_kv;         /* KV heads, >= 1 */
+  int32_t head_dim;     /* 64, 128 or 256 */
+  int32_t max_context;  /* cache positions per (sequence, KV head), 1 .. 2^24 */
+} gdn_attn_shape_t;
+
+typedef struct {
+  float scale;              /* multiplies q . k; finite */
+  int32_t layout;           /* a gdn_attn_layout_t */
+  int32_t heads_per_group;  /* 0, 1, 2, 4 or 8 */
+  int32_t num_blocks;       /* fixed-block parts per context, 0 = automatic, at most min(max_context, 4096) */
+} gdn_attn_params_t;
+
+/* Workspace bytes for these arguments (0 when the general layout is chosen).
+ * `params` is a HOST pointer, or NULL for {1 / sqrt(head_dim), AUTO, 0, 0}.
+ * Returns 0 for invalid arguments as well; gdn_attention_decode reports them. */
+size_t gdn_attention_decode_workspace(const gdn_attn_shape_t* shape, const gdn_attn_params_t* params);
+
+gdn_status_t gdn_attention_decode(const gdn_attn_shape_t* shape, const gdn_attn_params_t* params, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* context_lens, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing for benchmarks and profiling.  While enabled (process-wide),
  * every kernel the library enqueues is bracketed by two hipEvents recorded on
  * the stream it is launched on.  Off by default; when off, no events are

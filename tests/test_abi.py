@@ -234,3 +234,72 @@ def test_moe_rejects(lib):
     assert lib.gdn_dequant_q4(ctypes.byref(ok), p[2], p[3], p[4], None, None) == 1   # weights missing
     assert lib.gdn_moe_gemm_bf16(ctypes.byref(S(8, 100, 100, 256)), p[0], p[1], p[2], p[5], None) == 2
     assert lib.gdn_moe_gemm_bf16(ctypes.byref(ok), p[0], p[1], None, p[5], None) == 1
+
+
+def attn_ws_expected(B, h_q, d, nb):
+    """part_o [B, h_q, nb, d] fp32 padded to 256 bytes, then (max, sum) pairs."""
+    rows = B * h_q * nb
+    return (rows * d * 4 + 255) // 256 * 256 + rows * 8
+
+
+def test_attention_workspace_size(lib):
+    A, P = gdn.GdnAttnShape, gdn.GdnAttnParams
+    s = A(1, 16, 2, 256, 32768)
+    fixed = P(0.0625, gdn.GDN_ATTN_FIXED_BLOCK, 8, 128)
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(s), ctypes.byref(fixed)) == attn_ws_expected(1, 16, 256, 128)
+    general = P(0.0625, gdn.GDN_ATTN_GENERAL, 0, 0)
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(s), ctypes.byref(general)) == 0
+    # the automatic choice: fixed blocks when (batch x KV heads x packs) leaves compute units idle
+    auto = lib.gdn_attention_decode_workspace(ctypes.byref(s), None)
+    # (compute units / 2 groups parts, at least 32 positions each: 128 on a 256-CU device)
+    assert auto in [attn_ws_expected(1, 16, 256, nb) for nb in range(2, 1025)]
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(A(1, 16, 2, 256, 32)), None) == 0  # one part anyway
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(A(512, 16, 2, 256, 4096)), None) == 0  # enough groups
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(A(1, 16, 2, 256, 64)), None) == attn_ws_expected(1, 16, 256, 2)
+    assert lib.gdn_attention_decode_workspace(ctypes.byref(A(1, 16, 2, 96, 4096)), None) == 0  # invalid -> 0
+
+
+def test_attention_rejects(lib):
+    A, P = gdn.GdnAttnShape, gdn.GdnAttnParams
+    p = [FAKE + 256 * i for i in range(6)]  # q, k, v, lens, out, workspace
+    s = A(1, 16, 2, 256, 1024)
+    ws = attn_ws_expected(1, 16, 256, 4)
+    fixed = P(0.0625, gdn.GDN_ATTN_FIXED_BLOCK, 0, 4)
+
+    def call(shape=s, params=fixed, ptrs=p, nbytes=ws):
+        return lib.gdn_attention_decode(None if shape is None else ctypes.byref(shape),
+                                        None if params is None else ctypes.byref(params), *ptrs[:5], ptrs[5],
+                                        nbytes, None)
+    assert call(shape=None) == 1
+    assert call(shape=A(0, 16, 2, 256, 1024)) == 1
+    assert call(shape=A(1, 12, 8, 256, 1024)) == 1                 # h_q not a multiple of h_kv
+    assert call(shape=A(1, 16, 2, 96, 1024)) == 2                  # head size not built
+    assert call(shape=A(1, 16, 2, 256, 0)) == 1
+    assert call(shape=A(1, 16, 2, 256, (1 << 24) + 1)) == 1
+    assert call(params=P(float("nan"), 2, 0, 4)) == 1
+    assert call(params=P(0.1, 7, 0, 4)) == 1                       # not a layout
+    assert call(params=P(0.1, 2, 3, 4)) == 1                       # 3 heads per workgroup
+    assert call(params=P(0.1, 2, 16, 4)) == 1                      # more than 8
+    assert call(shape=A(1, 12, 2, 256, 1024), params=P(0.1, 2, 4, 4)) == 1  # 4 does not divide 6
+    assert call(params=P(0.1, 2, 0, 1025)) == 1                    # more parts than positions
+    assert call(params=P(0.1, 2, 0, -1)) == 1
+    for i in range(5):                                             # each pointer missing
+        ptrs = list(p)
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == 1
+    ptrs = list(p)
+    ptrs[0] += 8                                                   # misaligned q
+    assert call(ptrs=ptrs) == 1 and "aligned" in lib.gdn_last_error().decode()
+    ptrs = list(p)
+    ptrs[3] += 2                                                   # misaligned context_lens
+    assert call(ptrs=ptrs) == 1
+    ptrs = list(p)
+    ptrs[4] = ptrs[1]                                              # out aliases the key cache
+    assert call(ptrs=ptrs) == 1
+    ptrs = list(p)
+    ptrs[5] = None
+    assert call(ptrs=ptrs) == 1                                    # workspace missing
+    ptrs[5] = FAKE + 128
+    assert call(ptrs=ptrs) == 1                                    # not 256-byte aligned
+    assert call(nbytes=ws - 1) == 1
+    assert "needs" in lib.gdn_last_error().decode()
