@@ -29,6 +29,15 @@ same JSON line also carries:
               top 8, K = 2048, N = 1024) at 512- and 2048-token prompts:
               rebuilt in the GEMM against the two-pass ablation, with the
               HBM and MFMA fractions of the fused kernel;
+  attention_decode  one decode step of grouped-query attention (16 query
+              heads on 2 KV heads, 256 values per head, bf16 cache drawn on
+              the device) at contexts of 32K, 64K and 128K positions: the
+              fixed-block layout with all 8 query heads of a group packed in
+              a workgroup, beside the pages' two ablations (one query head
+              per workgroup; the general layout, one workgroup per head pack
+              over the whole context) and the pages' own pack of 4; timed by
+              graph replay, with per-kernel HIP event times and the cache's
+              HBM fraction;
   segmented_prefill  a 131072-token prompt (drawn on the device) chunked in
               one call and through gdn_prefill_segmented in 8192- and
               4096-token segments: time, workspace, and output equality;
@@ -154,6 +163,7 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the 4-bit expert GEMM leg")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 131072-token segmented-prefill and the ragged-batch legs")
+    ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -518,6 +528,67 @@ def main():
         torch.cuda.empty_cache()
         log(f"expert GEMM on 4-bit weights: {moe}")
 
+    # ------------------------------------------------------------ decode attention at long contexts
+    # One decode step of the attention layer at the pages' long contexts:
+    # fixed-block with packed query heads (the library's choice), the
+    # unpacked and general-layout ablations, and packs of 4.
+    attention = None
+    if not args.no_attention:
+        from gated_deltanet_linear_delta_amd.workloads import attention_device
+        attention = {"shape": {"batch": 1, "h_q": 16, "h_kv": 2, "head_dim": 256, "cache": "bf16"}}
+        variants = (("fixed_block_packed8", "fixed_block", 8), ("fixed_block_packed4", "fixed_block", 4),
+                    ("fixed_block_unpacked", "fixed_block", 1), ("general_packed8", "general", 8))
+        for TA in (32768, 65536, 131072):
+            qa, ka, va, cla, sca = attention_device([TA], seed=TA)
+            oa = torch.empty_like(qa)
+            cache_bytes = 2 * ka.numel() * 2
+            res = {"cache_bytes": cache_bytes}
+            for name, layout, hp in variants:
+                wsa = gdn.alloc_workspace(gdn.attention_decode_workspace_bytes(1, 16, 2, 256, TA, sca, layout, hp, 0),
+                                          dev)
+
+                def att(_i=0):
+                    gdn.attention_decode(qa, ka, va, cla, sca, layout=layout, heads_per_group=hp, out=oa,
+                                         workspace=wsa)
+
+                att()
+                torch.cuda.synchronize()
+                gdn.profile_enable(True)
+                for _ in range(5):
+                    att()
+                torch.cuda.synchronize()
+                gdn.profile_enable(False)
+                kern = {n_: round(m_ * 1e3, 2) for n_, (m_, _) in mean_by_name(gdn.profile_collect()).items()}
+                slow = layout == "general"
+                per_graph = 2 if slow else 20
+                graph = torch.cuda.CUDAGraph()
+                sa = torch.cuda.Stream()
+                sa.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(sa):
+                    with torch.cuda.graph(graph, stream=sa):
+                        for _ in range(per_graph):
+                            att()
+                torch.cuda.current_stream().wait_stream(sa)
+                graph.replay()
+                torch.cuda.synchronize()
+                reps = 5 if slow else 50
+                t3 = time.perf_counter()
+                for _ in range(reps):
+                    graph.replay()
+                torch.cuda.synchronize()
+                us = (time.perf_counter() - t3) * 1e6 / (reps * per_graph)
+                res[name] = {"us": round(us, 2), "kernels_us": kern,
+                             "cache_gbs": round(cache_bytes / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(cache_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                del graph, wsa
+            best = res["fixed_block_packed8"]["us"]
+            res["packing_speedup"] = round(res["fixed_block_unpacked"]["us"] / best, 3)
+            res["fixed_block_speedup"] = round(res["general_packed8"]["us"] / best, 3)
+            attention[f"context_{TA}"] = res
+            log(f"decode attention at {TA}: {res}")
+            del qa, ka, va, oa
+            torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ bounded prompt segments
     # One 131072-token prompt (the long workload's shape; inputs drawn on the
     # device with the same distributions), chunked in one call with a
@@ -619,6 +690,7 @@ def main():
         "segmented_prefill": segmented,
         "ragged_prefill": ragged,
         "moe_gemm_q4": moe,
+        "attention_decode": attention,
         "scan": scan,
         "cpu_baseline": cpu,
     }

@@ -246,15 +246,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 }
 
 // Merge the nb parts of each (sequence, query head): workgroup (row, chunk)
-// owns 64 output columns of one row.  The largest part maximum M and the
-// weights 2^(m_c - M) come first (every workgroup of the row recomputes them
-// from the nb (m, l) pairs), then sixteen slices of parts, each 16 lanes x 4
-// columns, sum weight x partial output with independent loads, and the
-// slices are added through LDS.
+// owns 64 output columns of one row, in sixteen slices of parts (16 lanes x 4
+// columns each).  Every load is issued up front: each slice's first eight
+// partial outputs and the (m, l) pairs, one per thread.  Then the largest
+// maximum M, the weights 2^(m_c - M) (through LDS) and their l-weighted sum,
+// and the weighted sum of the partial outputs, added over the slices through
+// LDS.  Every workgroup of a row recomputes M and the weights from the nb
+// pairs.
 constexpr int kMaxParts = 4096;
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, const float* part_ml, uint16_t* out,
                                                            int nb, int dk) {
+  constexpr int kAhead = 8;  // partial outputs per slice loaded before the weights are known
   __shared__ float sw[kMaxParts];
   __shared__ float red[2][kWaves];
   __shared__ __align__(16) float co[16][64];
@@ -263,9 +266,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, 
   const size_t row = blockIdx.x / chunks;
   const int c0 = (blockIdx.x % chunks) * 64;
   const float* pml = part_ml + row * nb * 2;
+  const int slice = tid >> 4, c4 = tid & 15;
+  const float* po = part_o + row * nb * size_t(dk) + c0 + 4 * c4;
 
-  float mx = -INFINITY;
-  for (int c = tid; c < nb; c += 256) mx = fmaxf(mx, pml[2 * c]);
+  f4 x[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    const int c = slice + 16 * i;
+    x[i] = c < nb ? *reinterpret_cast<const f4*>(po + size_t(c) * dk) : zero4();
+  }
+  f2v ml0 = tid < nb ? *reinterpret_cast<const f2v*>(pml + 2 * tid) : f2v{-INFINITY, 0.f};
+
+  float mx = ml0[0];
+  for (int c = tid + 256; c < nb; c += 256) mx = fmaxf(mx, pml[2 * c]);
 #pragma unroll
   for (int sft = 1; sft < 64; sft <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
   if (lane == 0) red[0][wave] = mx;
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, 
   mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   float L = 0.f;
   for (int c = tid; c < nb; c += 256) {
-    const f2v ml = *reinterpret_cast<const f2v*>(pml + 2 * c);
+    const f2v ml = c == tid ? ml0 : *reinterpret_cast<const f2v*>(pml + 2 * c);
     const float w = (mx == -INFINITY || ml[0] == -INFINITY) ? 0.f : exp2_(ml[0] - mx);
     sw[c] = w;
     L += w * ml[1];
@@ -284,11 +297,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, 
   __syncthreads();
   L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
 
-  const int slice = tid >> 4, c4 = tid & 15;
-  const float* po = part_o + row * nb * size_t(dk) + c0 + 4 * c4;
   f4 O = zero4();
-#pragma unroll 4
-  for (int c = slice; c < nb; c += 16) O += sw[c] * *reinterpret_cast<const f4*>(po + size_t(c) * dk);
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    const int c = slice + 16 * i;
+    if (c < nb) O += sw[c] * x[i];
+  }
+  for (int c = slice + 16 * kAhead; c < nb; c += 16) O += sw[c] * *reinterpret_cast<const f4*>(po + size_t(c) * dk);
   *reinterpret_cast<f4*>(&co[slice][4 * c4]) = O;
   __syncthreads();
   if (tid < 16) {
