@@ -15,24 +15,31 @@
 // One workgroup of four waves serves HP query heads of one KV head over a
 // range of positions (the whole context in the general layout, one of nb
 // equal parts in the fixed-block layout).  Wave w takes the 16-position tiles
-// w, w + 4, ... of that range.  Per tile:
-//   * scores on the matrix unit: S[16 positions, 16 columns] = K_tile Q^T with
-//     v_mfma_f32_16x16x32_bf16; the key rows are the A fragments, loaded
-//     straight from memory (lane = 16 grp + row holds 8 consecutive values of
-//     one key row per 32-wide slab), the HP queries are the B fragments, held
-//     in registers for the whole range (columns past HP are zero);
+// w, w + 4, ... of that range, and loads the next tile's key and value rows
+// while it works on the current one.  Per tile, all on the matrix unit
+// except the softmax bookkeeping:
+//   * scores S[16 positions, 16 columns] = K_tile Q^T, four-wide bf16
+//     v_mfma_f32_16x16x32_bf16 slabs: the key rows are the A fragments,
+//     loaded straight from memory (lane = 16 grp + row holds 8 consecutive
+//     values of one key row per 32-wide slab); the HP queries are the B
+//     fragments, held in registers for the whole range (columns past HP are
+//     zero and their rows of the output are dropped);
 //   * an online softmax per head in base 2 (scores times scale * log2 e): the
-//     running maximum m, the rescale factor 2^(m_old - m_new), the
-//     probabilities p and a per-lane partial sum l of them;
-//   * p and the rescale factors go through a small LDS buffer of the wave and
-//     the value rows are applied on the vector ALU in fp32: lane cq of a token
-//     row owns four value columns, so a 256-wide row is one 8-byte load per
-//     lane (for narrower heads 256 / d positions share a load instruction).
-// The waves' (m, l, o) are merged through LDS at the end.  The general layout
+//     running maximum m, the rescale factor 2^(m_old - m_new) applied to the
+//     output rows when it is not 1, the probabilities p and a per-lane sum l;
+//   * O[heads, columns] += P V_tile with v_mfma_f32_16x16x16_bf16: the score
+//     block's lane layout (head = col, positions 4 grp + r) is already the A
+//     fragment of P, split into a bf16 high part and a bf16 residue so that
+//     p reaches the product to 2^-17 relative; the value tile goes through a
+//     per-wave LDS buffer (rows padded by 8 bytes, so that the four row groups
+//     a fragment read touches fall on disjoint banks) and each B fragment
+//     lane reads four positions of one column.
+// The waves' (m, l, O) are merged through LDS at the end.  The general layout
 // divides by l and writes bf16; the fixed-block layout writes the part's
-// (m, l, o) in fp32 and attn_combine_kernel merges the parts of each head.
-// Every head's arithmetic is the same whatever HP is, so packed and unpacked
-// launches give the same bytes.
+// (m, l, O) in fp32 and attn_combine_kernel merges the parts of each head.
+// Every head's arithmetic is the same whatever HP is (its column of the score
+// block and its row of the output block are computed independently of the
+// others), so packed and unpacked launches give the same bytes.
 #include "gdn_common.hpp"
 #include "gdn_internal.hpp"
 
@@ -76,13 +83,14 @@ template <int DK, int HP, bool PARTIAL>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   static_assert(DK == 64 || DK == 128 || DK == 256, "head size");
   static_assert(HP == 1 || HP == 2 || HP == 4 || HP == 8, "heads per workgroup");
-  constexpr int KS = DK / 32;      // 32-wide slabs of the score product
-  constexpr int LPT = DK / 4;      // lanes per value row
-  constexpr int TP = 64 / LPT;     // value rows per load instruction
-  constexpr int TPL = kTile / TP;  // value rows per lane and tile
+  constexpr int KS = DK / 32;          // 32-wide slabs of the score product
+  constexpr int CB = DK / 16;          // 16-column blocks of the output
+  constexpr int VS = DK + 4;           // LDS row stride of a value tile (bf16): 4 rows apart -> 32 bytes of banks apart
+  constexpr int CPR = DK / 8;          // 16-byte chunks per value row
+  constexpr int RPI = 64 / CPR;        // value rows per load instruction
+  constexpr int VLD = kTile / RPI;     // value load instructions per tile
 
-  __shared__ float sp[kWaves][HP][kTile];  // probabilities, [head][position]
-  __shared__ float sa[kWaves][HP];         // rescale factors
+  __shared__ __align__(16) uint16_t vt[kWaves][kTile * VS];
   __shared__ float sm[kWaves][HP], sl[kWaves][HP];
   __shared__ __align__(16) float so[kWaves][HP][DK];
 
@@ -108,8 +116,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const uint16_t* kb = a.k + kv_off;
   const uint16_t* vb = a.v + kv_off;
 
-  const int col = lane & 15, grp = lane >> 4;  // fragment coordinates
-  const int tp = lane / LPT, cq = lane % LPT;  // value-row coordinates
+  const int col = lane & 15, grp = lane >> 4;          // fragment coordinates
+  const int vrow = lane / CPR, vch = lane % CPR;       // value-load coordinates
 
   v4u qf[KS];
   {
@@ -118,33 +126,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     for (int kk = 0; kk < KS; ++kk) qf[kk] = col < HP ? *reinterpret_cast<const v4u*>(qp + 32 * kk) : v4u{0, 0, 0, 0};
   }
 
-  float o[HP][4];
+  f4 o[CB];
 #pragma unroll
-  for (int h = 0; h < HP; ++h) o[h][0] = o[h][1] = o[h][2] = o[h][3] = 0.f;
+  for (int c = 0; c < CB; ++c) o[c] = zero4();
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Tile loads: key rows as A fragments, value rows four columns per lane.
   // Rows past the range are clamped to its last row (read, then masked).
-  auto load_tile = [&](int t0, v4u (&kf)[KS], v2u (&vf)[TPL]) {
-    const int tr = min(t0 + col, end - 1);
-    const uint16_t* kp = kb + size_t(tr) * DK + 8 * grp;
+  auto load_k = [&](int t0, v4u (&kf)[KS]) {
+    const uint16_t* kp = kb + size_t(min(t0 + col, end - 1)) * DK + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) kf[kk] = *reinterpret_cast<const v4u*>(kp + 32 * kk);
+  };
+  auto load_v = [&](int t0, v4u (&vr)[VLD]) {
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const int tv = min(t0 + TP * i + tp, end - 1);
-      vf[i] = *reinterpret_cast<const v2u*>(vb + size_t(tv) * DK + 4 * cq);
-    }
+    for (int i = 0; i < VLD; ++i)
+      vr[i] = *reinterpret_cast<const v4u*>(vb + size_t(min(t0 + RPI * i + vrow, end - 1)) * DK + 8 * vch);
   };
 
-  v4u kf[KS];
-  v2u vf[TPL];
-  if (start + wave * kTile < end) load_tile(start + wave * kTile, kf, vf);
+  v4u kf[KS], vr[VLD];
+  uint16_t* vw = &vt[wave][0];
+  if (start + wave * kTile < end) {
+    load_k(start + wave * kTile, kf);
+    load_v(start + wave * kTile, vr);
+  }
   for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
-    // the next tile's rows are in flight while this one is processed
+    // this tile's value rows to LDS, the next tile's rows in flight
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vw + (RPI * i + vrow) * VS + 8 * vch);
+      *reinterpret_cast<v2u*>(dst) = v2u{vr[i].x, vr[i].y};
+      *reinterpret_cast<v2u*>(dst + 2) = v2u{vr[i].z, vr[i].w};
+    }
     v4u kn[KS];
-    v2u vn[TPL];
-    load_tile(t0 + kWaves * kTile, kn, vn);
+    load_k(t0 + kWaves * kTile, kn);
+    load_v(t0 + kWaves * kTile, vr);
 
     f4 s = zero4();
 #pragma unroll
@@ -160,62 +175,54 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float al = exp2_(m_run - m_use);
-    float p[4];
+    f4 p;
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = exp2_(x[r] - m_use);
     l_run = l_run * al + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
-    if (col < HP) {
-      *reinterpret_cast<f4*>(&sp[wave][col][4 * grp]) = f4{p[0], p[1], p[2], p[3]};
-      if (grp == 0) sa[wave][col] = al;
+    // p is the A fragment of P (rows = heads, k = positions 4 grp + r); hi + lo bf16 carry it to 2^-17
+    const sfrag ps = split4(p);
+
+    // rescale the output rows (head 4 grp + r) by their heads' factors, unless all are 1
+    if (__any(al != 1.f)) {
+      float ah[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ah[r] = __shfl(al, 4 * grp + r);
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[c][r] *= ah[r];
     }
     wave_sync();
-
+    // O[head, 16 c + col] += sum_positions P[head, pos] V[pos, 16 c + col]; the B fragment
+    // lane (col, grp) holds V[4 grp + r][16 c + col]
 #pragma unroll
-    for (int h = 0; h < HP; ++h) {
-      const float ah = sa[wave][h];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[h][e] *= ah;
-    }
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const float v0 = __uint_as_float(vf[i].x << 16), v1 = __uint_as_float(vf[i].x & 0xffff0000u);
-      const float v2 = __uint_as_float(vf[i].y << 16), v3 = __uint_as_float(vf[i].y & 0xffff0000u);
-#pragma unroll
-      for (int h = 0; h < HP; ++h) {
-        const float ph = sp[wave][h][TP * i + tp];
-        o[h][0] = fmaf(ph, v0, o[h][0]);
-        o[h][1] = fmaf(ph, v1, o[h][1]);
-        o[h][2] = fmaf(ph, v2, o[h][2]);
-        o[h][3] = fmaf(ph, v3, o[h][3]);
-      }
+    for (int c = 0; c < CB; ++c) {
+      const uint16_t* vp = vw + 4 * grp * VS + 16 * c + col;
+      const s4 vf = pack4(vp[0], vp[VS], vp[2 * VS], vp[3 * VS]);
+      o[c] = mma_bf(ps.lo, vf, o[c]);
+      o[c] = mma_bf(ps.hi, vf, o[c]);
     }
     wave_sync();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) kf[kk] = kn[kk];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) vf[i] = vn[i];
   }
 
-  // per-wave totals: l over the four lane groups, o over the value-row groups
+  // per-wave totals: l over the four lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int sft = LPT; sft < 64; sft <<= 1)
-#pragma unroll
-    for (int h = 0; h < HP; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[h][e] += __shfl_xor(o[h][e], sft);
   if (col < HP && grp == 0) {
     sm[wave][col] = m_run;
     sl[wave][col] = l_run;
   }
-  if (tp == 0) {
 #pragma unroll
-    for (int h = 0; h < HP; ++h) *reinterpret_cast<f4*>(&so[wave][h][4 * cq]) = f4{o[h][0], o[h][1], o[h][2], o[h][3]};
-  }
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * grp + r < HP) so[wave][4 * grp + r][16 * c + col] = o[c][r];
   __syncthreads();
 
+  constexpr int LPT = DK / 4;
   for (int idx = tid; idx < HP * LPT; idx += 256) {
     const int h = idx / LPT, c4 = idx % LPT;
     float mx = sm[0][h];
