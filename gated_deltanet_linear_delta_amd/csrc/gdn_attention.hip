@@ -47,7 +47,8 @@ namespace gdn {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves per workgroup of the decode kernel (8 measured no faster)
+constexpr int kCombineWaves = 4;
 constexpr int kTile = 16;  // positions per wave step
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -80,7 +81,7 @@ __device__ __forceinline__ void wave_sync() {
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int DK, int HP, bool PARTIAL>
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
   static_assert(DK == 64 || DK == 128 || DK == 256, "head size");
   static_assert(HP == 1 || HP == 2 || HP == 4 || HP == 8, "heads per workgroup");
   constexpr int KS = DK / 32;          // 32-wide slabs of the score product
@@ -90,9 +91,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   constexpr int RPI = 64 / CPR;        // value rows per load instruction
   constexpr int VLD = kTile / RPI;     // value load instructions per tile
 
-  __shared__ __align__(16) uint16_t vt[kWaves][kTile * VS];
+  // the value tiles during the loop, the waves' outputs after it
+  constexpr int kVtBytes = kWaves * kTile * VS * 2, kSoBytes = kWaves * HP * DK * 4;
+  __shared__ __align__(16) unsigned char lds_raw[kVtBytes > kSoBytes ? kVtBytes : kSoBytes];
   __shared__ float sm[kWaves][HP], sl[kWaves][HP];
-  __shared__ __align__(16) float so[kWaves][HP][DK];
+  auto vt = reinterpret_cast<uint16_t(*)[kTile * VS]>(lds_raw);
+  auto so = reinterpret_cast<float(*)[HP][DK]>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,6 +219,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     sm[wave][col] = m_run;
     sl[wave][col] = l_run;
   }
+  __syncthreads();  // every wave is done with its value tile before the outputs overwrite them
 #pragma unroll
   for (int c = 0; c < CB; ++c)
 #pragma unroll
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   __syncthreads();
 
   constexpr int LPT = DK / 4;
-  for (int idx = tid; idx < HP * LPT; idx += 256) {
+  for (int idx = tid; idx < HP * LPT; idx += 64 * kWaves) {
     const int h = idx / LPT, c4 = idx % LPT;
     float mx = sm[0][h];
 #pragma unroll
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, 
                                                            int nb, int dk) {
   constexpr int kAhead = 8;  // partial outputs per slice loaded before the weights are known
   __shared__ float sw[kMaxParts];
-  __shared__ float red[2][kWaves];
+  __shared__ float red[2][kCombineWaves];
   __shared__ __align__(16) float co[16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunks = dk / 64;
@@ -329,7 +334,7 @@ hipError_t launch_attn_t(const AttnDims& d, const AttnArgs& a, bool fixed_block,
   if (fixed_block) {
     {
       Prof prof("attn_decode_parts", st);
-      hipLaunchKernelGGL((attn_decode_kernel<DK, HP, true>), dim3(blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_decode_kernel<DK, HP, true>), dim3(blocks), dim3(64 * kWaves), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -339,7 +344,7 @@ hipError_t launch_attn_t(const AttnDims& d, const AttnArgs& a, bool fixed_block,
     return hipGetLastError();
   }
   Prof prof("attn_decode", st);
-  hipLaunchKernelGGL((attn_decode_kernel<DK, HP, false>), dim3(blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_decode_kernel<DK, HP, false>), dim3(blocks), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 
