@@ -48,7 +48,6 @@ namespace gdn {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup of the decode kernel (8 measured no faster)
-constexpr int kCombineWaves = 4;
 constexpr int kTile = 16;  // positions per wave step
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -259,70 +258,65 @@ __global__ __launch_bounds__(64 * kWaves) void attn_decode_kernel(AttnArgs a) {
 
 // Merge the nb parts of each (sequence, query head): workgroup (row, chunk)
 // owns 64 output columns of one row, in sixteen slices of parts (16 lanes x 4
-// columns each).  Every load is issued up front: each slice's first eight
-// partial outputs and the (m, l) pairs, one per thread.  Then the largest
-// maximum M, the weights 2^(m_c - M) (through LDS) and their l-weighted sum,
-// and the weighted sum of the partial outputs, added over the slices through
-// LDS.  Every workgroup of a row recomputes M and the weights from the nb
-// pairs.
-constexpr int kMaxParts = 4096;
-
+// columns each).  A slice merges its parts c = slice, slice + 16, ... in
+// registers, online (running maximum, rescaled sum and output), with the
+// loads of eight parts issued before their merge; the sixteen slices are then
+// merged through LDS.  The order is fixed, so the result is deterministic.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part_o, const float* part_ml, uint16_t* out,
                                                            int nb, int dk) {
-  constexpr int kAhead = 8;  // partial outputs per slice loaded before the weights are known
-  __shared__ float sw[kMaxParts];
-  __shared__ float red[2][kCombineWaves];
+  constexpr int kAhead = 8;  // parts per slice whose loads are in flight together
+  __shared__ float cm[16], cl[16];
   __shared__ __align__(16) float co[16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int chunks = dk / 64;
   const size_t row = blockIdx.x / chunks;
   const int c0 = (blockIdx.x % chunks) * 64;
-  const float* pml = part_ml + row * nb * 2;
   const int slice = tid >> 4, c4 = tid & 15;
+  const float* pml = part_ml + row * nb * 2;
   const float* po = part_o + row * nb * size_t(dk) + c0 + 4 * c4;
 
-  f4 x[kAhead];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) {
-    const int c = slice + 16 * i;
-    x[i] = c < nb ? *reinterpret_cast<const f4*>(po + size_t(c) * dk) : zero4();
-  }
-  f2v ml0 = tid < nb ? *reinterpret_cast<const f2v*>(pml + 2 * tid) : f2v{-INFINITY, 0.f};
-
-  float mx = ml0[0];
-  for (int c = tid + 256; c < nb; c += 256) mx = fmaxf(mx, pml[2 * c]);
-#pragma unroll
-  for (int sft = 1; sft < 64; sft <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sft));
-  if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  float L = 0.f;
-  for (int c = tid; c < nb; c += 256) {
-    const f2v ml = c == tid ? ml0 : *reinterpret_cast<const f2v*>(pml + 2 * c);
-    const float w = (mx == -INFINITY || ml[0] == -INFINITY) ? 0.f : exp2_(ml[0] - mx);
-    sw[c] = w;
-    L += w * ml[1];
-  }
-#pragma unroll
-  for (int sft = 1; sft < 64; sft <<= 1) L += __shfl_xor(L, sft);
-  if (lane == 0) red[1][wave] = L;
-  __syncthreads();
-  L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-
+  float M = -INFINITY, L = 0.f;
   f4 O = zero4();
+  for (int base = slice; base < nb; base += 16 * kAhead) {
+    f2v ml[kAhead];
+    f4 x[kAhead];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) {
-    const int c = slice + 16 * i;
-    if (c < nb) O += sw[c] * x[i];
+    for (int i = 0; i < kAhead; ++i) {
+      const int c = base + 16 * i;
+      ml[i] = c < nb ? *reinterpret_cast<const f2v*>(pml + 2 * c) : f2v{-INFINITY, 0.f};
+      x[i] = c < nb ? *reinterpret_cast<const f4*>(po + size_t(c) * dk) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      if (ml[i][0] == -INFINITY) continue;  // an empty part (or past the last)
+      const float mn = fmaxf(M, ml[i][0]);
+      const float a1 = exp2_(M - mn), a2 = exp2_(ml[i][0] - mn);
+      L = L * a1 + ml[i][1] * a2;
+      O = O * a1 + x[i] * a2;
+      M = mn;
+    }
   }
-  for (int c = slice + 16 * kAhead; c < nb; c += 16) O += sw[c] * *reinterpret_cast<const f4*>(po + size_t(c) * dk);
+  if (c4 == 0) {
+    cm[slice] = M;
+    cl[slice] = L;
+  }
   *reinterpret_cast<f4*>(&co[slice][4 * c4]) = O;
   __syncthreads();
   if (tid < 16) {
-    f4 Ot = zero4();
+    float mx = cm[0];
 #pragma unroll
-    for (int sl = 0; sl < 16; ++sl) Ot += *reinterpret_cast<const f4*>(&co[sl][4 * tid]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int sl = 1; sl < 16; ++sl) mx = fmaxf(mx, cm[sl]);
+    float Lt = 0.f;
+    f4 Ot = zero4();
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) {
+        const float wt = exp2_(cm[sl] - mx);
+        Lt += wt * cl[sl];
+        Ot += wt * *reinterpret_cast<const f4*>(&co[sl][4 * tid]);
+      }
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     *reinterpret_cast<v2u*>(out + row * dk + c0 + 4 * tid) =
         v2u{pack_bf16x2(Ot[0] * inv, Ot[1] * inv), pack_bf16x2(Ot[2] * inv, Ot[3] * inv)};
   }
