@@ -167,13 +167,13 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no multi-GPU path "
-              "in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no "
+              "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     from gated_deltanet_linear_delta_amd import gdn
-    from gated_deltanet_linear_delta_amd.workloads import config, make_decode
+    from gated_deltanet_linear_delta_amd.workloads import make_decode, prefill_4096
 
     gdn.load_library()
     dev = torch.device("cuda:0")
@@ -182,7 +182,7 @@ def main():
 
     # ------------------------------------------------------------ inputs
     log("generating the 4096-token prefill workload")
-    inp = config(2)
+    inp = prefill_4096()
 
     def io(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).to(dev)

@@ -10,7 +10,7 @@ on-device inference for Apple Silicon", section "Qwen creates three distinct
 workload shapes" (a recurrent layer with a fixed-size per-head state) and
 section "Keeping the recurrent state on chip" (fp32 state and gate, bf16
 query/key activations).  The pages give no head counts for this layer; the
-named configurations below fix them (16 query/key heads shared by 32 value
+named workloads at the end fix them (16 query/key heads shared by 32 value
 heads, d_k = d_v = 128).
 
 All arrays are numpy: activations are float32 arrays whose values are exactly
@@ -27,7 +27,7 @@ import numpy as np
 
 __all__ = ["Inputs", "DecodeInputs", "RawDecodeInputs", "round_to_bf16", "make_prefill", "make_decode",
            "make_decode_raw", "MoeInputs", "make_moe", "AttentionInputs", "make_attention", "attention_device",
-           "config"]
+           "tiny_fp32_prefill", "decode_1000_steps", "prefill_4096", "prefill_131072", "ragged_32_then_decode"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -304,36 +304,38 @@ def ragged_lengths(rng, n, lo=256, hi=8192):
     return np.clip(np.rint(x), lo, hi).astype(np.int64)
 
 
-# The five named workloads.  Seeds are 1000 + index.
-CONFIG_NAMES = {
-    0: "tiny fp32: T=64, H=2, d=16, chunk 16",
-    1: "decode B=1, 16 qk / 32 v heads, d=128, bf16, 1000 carried steps",
-    2: "prefill T=4096, B=1, 16 qk / 32 v heads, d=128, bf16, chunk 64",
-    3: "long prefill T=131072, B=1, 16 qk / 32 v heads, d=128, bf16, chunk 64",
-    4: "ragged prefill 32 seqs log-uniform [256, 8192] + 256 decode steps at B=32",
-}
+# The five named workloads.  Each draws from its own seed (1000 .. 1004).
+def tiny_fp32_prefill():
+    """T = 64, 2 query/key and 2 value heads, d = 16, fp32, chunk 16, zero initial state."""
+    return make_prefill([64], 2, 2, 16, 16, "f32", 0.0, None, rng=np.random.default_rng(1000), chunk_size=16)
 
 
-def config(index: int, decode_steps: int | None = None):
-    """Return the inputs of a named workload.
+def decode_1000_steps(decode_steps: int | None = None):
+    """B = 1, 16 query/key heads shared by 32 value heads, d = 128, bf16, an
+    N(0, 0.02) state carried over 1000 steps (or ``decode_steps``)."""
+    steps = 1000 if decode_steps is None else decode_steps
+    return make_decode(steps, 1, 16, 32, 128, 128, "bf16", 0.0, 0.02, rng=np.random.default_rng(1001))
 
-    0 -> Inputs; 1 -> DecodeInputs; 2, 3 -> Inputs; 4 -> (Inputs, DecodeInputs).
-    ``decode_steps`` shortens the decode part of configs 1 and 4.
-    """
-    rng = np.random.default_rng(1000 + index)
-    if index == 0:
-        return make_prefill([64], 2, 2, 16, 16, "f32", 0.0, None, rng=rng, chunk_size=16)
-    if index == 1:
-        steps = 1000 if decode_steps is None else decode_steps
-        return make_decode(steps, 1, 16, 32, 128, 128, "bf16", 0.0, 0.02, rng=rng)
-    if index in (2, 3):
-        T = 4096 if index == 2 else 131072
-        return make_prefill([T], 16, 32, 128, 128, "bf16", 2.0, None, rng=rng, chunk_size=64)
-    if index == 4:
-        lengths = ragged_lengths(rng, 32)
-        pre = make_prefill(lengths, 16, 32, 128, 128, "bf16", 2.0, 0.02, rng=rng, chunk_size=64)
-        steps = 256 if decode_steps is None else decode_steps
-        dec = make_decode(steps, 32, 16, 32, 128, 128, "bf16", 2.0, rng=rng,
-                          state=np.zeros((32, 32, 128, 128), np.float32))
-        return pre, dec
-    raise ValueError(f"no config {index}")
+
+def prefill_4096():
+    """One 4096-token prompt, 16 / 32 heads, d = 128, bf16, gate shift 2, chunk 64, zero initial state."""
+    return make_prefill([4096], 16, 32, 128, 128, "bf16", 2.0, None, rng=np.random.default_rng(1002), chunk_size=64)
+
+
+def prefill_131072():
+    """One 131072-token prompt, otherwise as prefill_4096."""
+    return make_prefill([131072], 16, 32, 128, 128, "bf16", 2.0, None, rng=np.random.default_rng(1003),
+                        chunk_size=64)
+
+
+def ragged_32_then_decode(decode_steps: int | None = None):
+    """32 sequences, lengths log-uniform in [256, 8192], each with an N(0, 0.02)
+    initial state, then 256 decode steps (or ``decode_steps``) at B = 32.
+    Returns (Inputs, DecodeInputs)."""
+    rng = np.random.default_rng(1004)
+    lengths = ragged_lengths(rng, 32)
+    pre = make_prefill(lengths, 16, 32, 128, 128, "bf16", 2.0, 0.02, rng=rng, chunk_size=64)
+    steps = 256 if decode_steps is None else decode_steps
+    dec = make_decode(steps, 32, 16, 32, 128, 128, "bf16", 2.0, rng=rng,
+                      state=np.zeros((32, 32, 128, 128), np.float32))
+    return pre, dec

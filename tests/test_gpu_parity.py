@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from gated_deltanet_linear_delta_amd import gdn
-from gated_deltanet_linear_delta_amd.workloads import config, make_decode, make_prefill
+from gated_deltanet_linear_delta_amd.workloads import (decode_1000_steps, make_decode, make_prefill, prefill_4096, prefill_131072,
+                                                     ragged_32_then_decode, tiny_fp32_prefill)
 from oracle import gated_delta_decode_step, gated_delta_recurrence
 
 from helpers import TOL, dev_prefill, f32, host, max_rel_out, max_rel_state, torch_io
@@ -77,14 +78,14 @@ def test_ragged_tails_and_empty(kind):
 
 
 # ---------------------------------------------------------------- the named workloads
-def test_config0_tiny_fp32():
-    inp = config(0)
+def test_tiny_fp32():
+    inp = tiny_fp32_prefill()
     check_prefill(inp, "chunked", 16)
     check_prefill(inp, "scan")
 
 
-def test_config1_decode_1000_steps():
-    dec = config(1)
+def test_decode_1000_steps():
+    dec = decode_1000_steps()
     steps = dec.q.shape[0]
     state = f32(dec.state)
     outs = []
@@ -106,15 +107,15 @@ def test_config1_decode_1000_steps():
 
 
 @pytest.mark.parametrize("kind", ["chunked", "scan"])
-def test_config2_prefill_4096(kind):
-    check_prefill(config(2), kind, 64)
+def test_prefill_4096(kind):
+    check_prefill(prefill_4096(), kind, 64)
 
 
-def test_config3_long_prefill_sampled_heads():
+def test_long_prefill_131072_sampled_heads():
     """T = 131072: the chunked kernel over all 32 heads; the oracle on two
     sampled value heads (heads are independent), all tokens and the final
     state of those heads."""
-    inp = config(3)
+    inp = prefill_131072()
     d = dev_prefill(inp)
     o, s = gdn.prefill_chunked(**d, chunk_size=64)
     torch.cuda.synchronize()
@@ -130,11 +131,11 @@ def test_config3_long_prefill_sampled_heads():
 
 
 @pytest.mark.parametrize("kind", ["chunked", "scan"])
-def test_config4_ragged_then_decode(kind):
+def test_ragged_32_then_decode(kind):
     """32 ragged sequences with their own initial state, then 256 decode
     steps at B=32 carried from the prefill state.  The oracle runs on a sample
     of sequences (shortest, longest, two others), all heads."""
-    pre, dec = config(4)
+    pre, dec = ragged_32_then_decode()
     d = dev_prefill(pre)
     o, s = run_prefill(kind, d, 64)
     steps = dec.q.shape[0] if kind == "chunked" else 16

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from gated_deltanet_linear_delta_amd import gdn
-from gated_deltanet_linear_delta_amd.workloads import config, make_prefill
+from gated_deltanet_linear_delta_amd.workloads import make_prefill, prefill_4096, tiny_fp32_prefill
 from oracle import gated_delta_recurrence
 
 from helpers import TOL, dev_prefill, host, max_rel_out, max_rel_state
@@ -93,7 +93,7 @@ def test_segmented_fp32_in_place_and_empty():
 
 def test_segmented_4096_prompt_bit_exact():
     # the 4096-token prompt in 1024-token segments equals one chunked call
-    inp = config(2)
+    inp = prefill_4096()
     d = dev_prefill(inp)
     o1, s1 = gdn.prefill_chunked(**d, chunk_size=64)
     o2, s2 = gdn.prefill_segmented(**d, chunk_size=64, segment_tokens=1024)
@@ -115,7 +115,7 @@ def test_blockwise_scan_equals_resident(block):
 
 
 def test_blockwise_scan_fp32_vs_oracle():
-    inp = config(0)
+    inp = tiny_fp32_prefill()
     d = dev_prefill(inp)
     o, s = gdn.prefill_scan_blockwise(**d, state_block=8)
     torch.cuda.synchronize()

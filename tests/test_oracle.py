@@ -20,7 +20,7 @@ import pytest
 
 from oracle import (decode_attention, dequantize_q4, gated_delta_chunk_form, gated_delta_decode_fused,
                     gated_delta_decode_step, gated_delta_recurrence, grouped_gemm_q4, qk_head_of, round_bf16, sigmoid, softplus)
-from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, config
+from gated_deltanet_linear_delta_amd.workloads import make_prefill, round_to_bf16, tiny_fp32_prefill
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -299,8 +299,8 @@ def test_round_to_bf16_ties_even():
     assert np.all(bits & 0xFFFF == 0)
 
 
-def test_config0_shapes_and_distributions():
-    inp = config(0)
+def test_tiny_fp32_shapes_and_distributions():
+    inp = tiny_fp32_prefill()
     assert inp.q.shape == (64, 2, 16) and inp.v.shape == (64, 2, 16) and inp.chunk_size == 16
     assert np.allclose(np.linalg.norm(inp.q, axis=-1), 1, atol=1e-6)
     assert np.all(inp.g < 0) and np.all((inp.beta > 0) & (inp.beta < 1))
