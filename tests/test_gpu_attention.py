@@ -179,3 +179,18 @@ def test_attention_long_context_sampled(T, layout):
     err = max_rel_heads(oh[:, heads], ref)
     print(f"attention T={T} {layout} heads {heads}: err={err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+def test_attention_context_lengths_clamped():
+    # context lengths are clamped on the device to [0, max_context]: a negative
+    # one reads nothing (zero output), one past the cache reads the whole cache
+    inp = make_attention([300, 300], 8, 2, 128, 300, seed=8)
+    q, k, v, _ = dev(inp)
+    for layout in ("general", "fixed_block"):
+        o_bad = gdn.attention_decode(q, k, v, torch.tensor([-5, 10**6], dtype=torch.int32, device="cuda"),
+                                     inp.scale, layout=layout)
+        o_ref = gdn.attention_decode(q, k, v, torch.tensor([0, 300], dtype=torch.int32, device="cuda"),
+                                     inp.scale, layout=layout)
+        torch.cuda.synchronize()
+        assert torch.equal(o_bad, o_ref)
+        assert bool((o_bad[0] == 0).all())
