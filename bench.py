@@ -52,7 +52,8 @@ same JSON line also carries:
               counters on a copy of known size), or null once the kernel
               source differs from the one the counters were taken on.
 --prefill-only runs just the headline calls and one 512 MiB device copy (the
-counter calibration), for counter runs under rocprofv3.
+counter calibration), for counter runs under rocprofv3; --attention-counters
+runs just three eager decode-attention calls at 32K and 128K and the same copy.
 Before the W warmup steps the headline step runs untimed for 0.25 s so that
 the GPU clocks have settled; the timed region is exactly K steps.
 Prints exactly one JSON line on stdout; progress goes to stderr.
@@ -165,6 +166,8 @@ def main():
                     help="skip the 131072-token segmented-prefill and the ragged-batch legs")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-attention leg")
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
+    ap.add_argument("--attention-counters", action="store_true",
+                    help="eager decode-attention calls at 32K and 128K and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no "
@@ -179,6 +182,31 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
+
+    if args.attention_counters:
+        # counter runs: graph replays are left out (rocprofv3's counter
+        # collection does not survive them); three eager calls per context of
+        # the fixed-block layout with packs of 8, then the calibration copy
+        from gated_deltanet_linear_delta_amd.workloads import attention_device
+        for TA in (32768, 131072):
+            qa, ka, va, cla, sca = attention_device([TA], seed=TA)
+            oa = torch.empty_like(qa)
+            wsa = gdn.alloc_workspace(gdn.attention_decode_workspace_bytes(1, 16, 2, 256, TA, sca, "fixed_block", 8),
+                                      dev)
+            for _ in range(3):
+                gdn.attention_decode(qa, ka, va, cla, sca, layout="fixed_block", heads_per_group=8, out=oa,
+                                     workspace=wsa)
+            torch.cuda.synchronize()
+            log(f"attention at {TA}: three calls")
+            del qa, ka, va, oa, wsa
+            torch.cuda.empty_cache()
+        src = torch.ones(1 << 28, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 536870912 bytes read, 536870912 written")
+        print(json.dumps({"attention_counters": True}), flush=True)
+        return
 
     # ------------------------------------------------------------ inputs
     log("generating the 4096-token prefill workload")
