@@ -81,10 +81,17 @@ __device__ __forceinline__ int first_slot(int off, int e) { return (off + e * (B
 
 // LDS: the expert offsets, then two buffers of the row block's activations for
 // one super-slab, [BM rows][KS k] bf16 with rows AS bytes apart (32 mod 128,
-// so the 16-lane fragment reads of 16 rows are free of bank conflicts).
+// so the 16-lane fragment reads of 16 rows are free of bank conflicts), then
+// two buffers of the block's scales and biases for a window of four
+// super-slabs (eight groups), [2 arrays][BN columns][8 groups] bf16.
 constexpr int AS = KS * 2 + 32;
 constexpr int ABUF = BM * AS;
-__host__ __device__ constexpr size_t moe_lds_bytes(int n_exp) { return (size_t(n_exp + 1) * 4 + 15) / 16 * 16 + 2 * ABUF; }
+constexpr int WIN = 4;                        // super-slabs per scale/bias window
+constexpr int WG_GROUPS = WIN * KS / GROUP;  // groups per window (8)
+constexpr int SBBUF = 2 * BN * WG_GROUPS * 2;
+__host__ __device__ constexpr size_t moe_lds_bytes(int n_exp) {
+  return (size_t(n_exp + 1) * 4 + 15) / 16 * 16 + 2 * ABUF + 2 * SBBUF;
+}
 
 template <bool Q4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemm_kernel(
@@ -94,6 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* soff = reinterpret_cast<int*>(smem);
   uint8_t* sa = smem + (size_t(n_exp + 1) * 4 + 15) / 16 * 16;
+  uint8_t* ssb = sa + 2 * ABUF;
   const int ncb = n / BN;
   const int slot = blockIdx.x / ncb, cb = blockIdx.x % ncb;
   for (int i = threadIdx.x; i <= n_exp; i += 256) {
@@ -145,16 +153,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
 #pragma unroll
       for (int i = 0; i < NP; ++i) *reinterpret_cast<v4u*>(sa + buf * ABUF + loff[i]) = st[i];
     };
-    // weights of one super-slab for both columns: 16 bytes of codes each and
-    // the raw bf16 scale and bias of the lane's group (Q4)
-    auto load_w = [&](uint4 (&c)[2], uint16_t (&sb)[4], int ks) __attribute__((always_inline)) {
+    // codes of one super-slab for both columns: 16 bytes each (Q4)
+    auto load_w = [&](uint4 (&c)[2], int ks) __attribute__((always_inline)) {
       if constexpr (Q4) {
         c[0] = *reinterpret_cast<const uint4*>(wsrc + wrow0 * (k / 2) + ks / 2 + 16 * grp);
         c[1] = *reinterpret_cast<const uint4*>(wsrc + wrow1 * (k / 2) + ks / 2 + 16 * grp);
-        const int g = (ks + 32 * grp) / GROUP;
-        sb[0] = scales[wrow0 * ngroups + g], sb[1] = biases[wrow0 * ngroups + g];
-        sb[2] = scales[wrow1 * ngroups + g], sb[3] = biases[wrow1 * ngroups + g];
       }
+    };
+    // scales and biases of window w (8 groups) for the block's 128 columns:
+    // thread t loads array t / 128, column t % 128, as four 4-byte pieces
+    // (a scattered 2-byte load per lane and super-slab costs far more), and
+    // the window goes to LDS at the barrier before it is used
+    const int sb_arr = tid >> 7, sb_col = tid & (BN - 1);
+    const uint16_t* sb_row =
+        Q4 ? (sb_arr ? biases : scales) + (size_t(e) * n + size_t(cb) * BN + sb_col) * ngroups : nullptr;
+    auto fetch_sb = [&](uint32_t (&r)[4], int w) __attribute__((always_inline)) {
+      if constexpr (Q4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = WG_GROUPS * w + 2 * i;
+          r[i] = g < ngroups ? *reinterpret_cast<const uint32_t*>(sb_row + g) : 0u;
+        }
+      }
+    };
+    auto commit_sb = [&](const uint32_t (&r)[4], int w) __attribute__((always_inline)) {
+      if constexpr (Q4)
+        *reinterpret_cast<uint4*>(ssb + (w & 1) * SBBUF + (sb_arr * BN + sb_col) * (WG_GROUPS * 2)) =
+            uint4{r[0], r[1], r[2], r[3]};
     };
 
     f4 acc[NT][2];
@@ -162,11 +187,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = zero4();
     uint4 c0[2], c1[2], c2[2];
     v4u stg[NP];
-    uint16_t g0[4] = {0, 0, 0, 0}, g1[4] = {0, 0, 0, 0}, g2[4] = {0, 0, 0, 0};
-    const int nks = k / KS;
-    load_w(c0, g0, 0);
-    load_w(c1, g1, min(KS, k - KS));
+    uint32_t sbr[4];
+    const int nks = k / KS, nwin = (nks + WIN - 1) / WIN;
+    load_w(c0, 0);
+    load_w(c1, min(KS, k - KS));
+    fetch_sb(sbr, 0);
     fetch_a(stg, 0);
+    commit_sb(sbr, 0);
     commit_a(stg, 0);
     __syncthreads();
     for (int si = 0; si < nks; ++si) {
@@ -174,10 +201,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
       // the next super-slab's activations first, then the codes two ahead, so
       // that waiting for the activations leaves the codes in flight; both
       // unconditional (the end reloads the last) so the memory waits stay exact
+      const int w = si / WIN;
       fetch_a(stg, min(ks + KS, k - KS));
-      load_w(c2, g2, min(ks + 2 * KS, k - KS));
-      const float s0 = bf16_bits_to_f32(g0[0]), b0 = bf16_bits_to_f32(g0[1]);
-      const float s1 = bf16_bits_to_f32(g0[2]), b1 = bf16_bits_to_f32(g0[3]);
+      load_w(c2, min(ks + 2 * KS, k - KS));
+      if (si % WIN == 0 && w + 1 < nwin) fetch_sb(sbr, w + 1);  // the next window, committed at this one's end
+      float s0 = 0.f, b0 = 0.f, s1 = 0.f, b1 = 0.f;
+      if constexpr (Q4) {
+        // group of the lane's k in this super-slab: 2 (si % WIN) + grp / 2 within the window
+        const uint16_t* sbw = reinterpret_cast<const uint16_t*>(ssb + (w & 1) * SBBUF);
+        const int gl = 2 * (si % WIN) + (grp >> 1), c0l = 32 * wave + col;
+        s0 = bf16_bits_to_f32(sbw[c0l * WG_GROUPS + gl]);
+        b0 = bf16_bits_to_f32(sbw[(BN + c0l) * WG_GROUPS + gl]);
+        s1 = bf16_bits_to_f32(sbw[(c0l + 16) * WG_GROUPS + gl]);
+        b1 = bf16_bits_to_f32(sbw[(BN + c0l + 16) * WG_GROUPS + gl]);
+      }
       const uint32_t d0[4] = {c0[0].x, c0[0].y, c0[0].z, c0[0].w}, d1[4] = {c0[1].x, c0[1].y, c0[1].z, c0[1].w};
       const uint8_t* abase = sa + buf * ABUF + col * AS + 64 * grp;
 #pragma unroll
@@ -200,10 +237,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
         }
       }
       commit_a(stg, buf ^ 1);  // the other buffer: its last readers passed the previous barrier
+      if (si % WIN == WIN - 1 && w + 1 < nwin) commit_sb(sbr, w + 1);  // likewise for window w - 1's buffer
       __syncthreads();
       c0[0] = c1[0], c0[1] = c1[1], c1[0] = c2[0], c1[1] = c2[1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g0[i] = g1[i], g1[i] = g2[i];
     }
     // D block: lane holds rows 4 grp .. 4 grp + 3 of the tile, column col
 #pragma unroll
