@@ -329,9 +329,10 @@ static gdn_status_t check_moe(const gdn_moe_shape_t* s, const char* what) {
   if (s->n < 128 || s->n % 128 != 0)
     return fail(GDN_ERR_UNSUPPORTED, "%s: n (%d) must be a positive multiple of 128", what, s->n);
   // the grid: one workgroup per (64-row block slot, 128-column block)
-  const long long slots = ((long long)s->rows + (long long)s->num_experts * 63) / 64;
+  const long long slots = (((long long)s->rows + (long long)s->num_experts * 63) / 64 + 7) / 8 * 8;
   if (slots * (s->n / 128) > (1ll << 31) - 1)
-    return fail(GDN_ERR_UNSUPPORTED, "%s: (rows + 63 num_experts) / 64 * n / 128 exceeds int32", what);
+    return fail(GDN_ERR_UNSUPPORTED, "%s: (rows + 63 num_experts) / 64 (rounded up to 8) * n / 128 exceeds int32",
+                what);
   if ((long long)s->rows * s->k > (1ll << 31) - 1 || (long long)s->rows * s->n > (1ll << 40))
     return fail(GDN_ERR_UNSUPPORTED, "%s: rows * k must stay below 2^31", what);
   return GDN_OK;

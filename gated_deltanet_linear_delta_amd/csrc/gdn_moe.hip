@@ -102,8 +102,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   int* soff = reinterpret_cast<int*>(smem);
   uint8_t* sa = smem + (size_t(n_exp + 1) * 4 + 15) / 16 * 16;
   uint8_t* ssb = sa + 2 * ABUF;
+  // Workgroups reach the eight XCDs round-robin (workgroup i on XCD i % 8).
+  // The ncb column blocks of one row-block slot all go to the same XCD, so
+  // the slot's activation rows come from HBM once and from that XCD's L2 for
+  // the other column blocks: workgroup i is column block (i / 8) % ncb of
+  // slot 8 ((i / 8) / ncb) + i % 8.
   const int ncb = n / BN;
-  const int slot = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  const int xi = int(blockIdx.x >> 3);
+  const int slot = 8 * (xi / ncb) + int(blockIdx.x & 7), cb = xi % ncb;
   for (int i = threadIdx.x; i <= n_exp; i += 256) {
     int o = offsets[i];
     soff[i] = o < 0 ? 0 : (o > m ? m : o);  // malformed offsets cannot index out of bounds
@@ -264,8 +270,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
 hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const int32_t* offsets,
                            const void* weights, const void* scales, const void* biases, void* y, bool q4,
                            hipStream_t st) {
-  // row-block slots: sum_e ceil(m_e / BM) <= (m + E (BM - 1)) / BM
-  const size_t slots = (size_t(m) + size_t(n_exp) * (BM - 1)) / BM;
+  // row-block slots: sum_e ceil(m_e / BM) <= (m + E (BM - 1)) / BM, rounded up
+  // to a multiple of 8 for the XCD mapping (the spare slots return at once)
+  const size_t slots = ((size_t(m) + size_t(n_exp) * (BM - 1)) / BM + 7) / 8 * 8;
   const unsigned blocks = unsigned(slots * size_t(n / BN));
   if (blocks == 0 || m == 0) return hipSuccess;
   Prof prof(q4 ? "moe_gemm_q4" : "moe_gemm_bf16", st);
