@@ -79,6 +79,11 @@ __global__ __launch_bounds__(256) void dequant_q4_kernel(size_t n_dwords, int k,
 
 __device__ __forceinline__ int first_slot(int off, int e) { return (off + e * (BM - 1)) / BM; }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its global loads (__syncthreads would also drain the
+// codes and activations prefetched for later super-slabs).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // LDS: the expert offsets, then two buffers of the row block's activations for
 // one super-slab, [BM rows][KS k] bf16 with rows AS bytes apart (32 mod 128,
 // so the 16-lane fragment reads of 16 rows are free of bank conflicts), then
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     fetch_a(stg, 0);
     commit_sb(sbr, 0);
     commit_a(stg, 0);
-    __syncthreads();
+    lds_barrier();
     for (int si = 0; si < nks; ++si) {
       const int ks = si * KS, buf = si & 1;
       // the next super-slab's activations first, then the codes two ahead, so
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
       }
       commit_a(stg, buf ^ 1);  // the other buffer: its last readers passed the previous barrier
       if (si % WIN == WIN - 1 && w + 1 < nwin) commit_sb(sbr, w + 1);  // likewise for window w - 1's buffer
-      __syncthreads();
+      lds_barrier();
       c0[0] = c1[0], c0[1] = c1[1], c1[0] = c2[0], c1[1] = c2[1];
     }
     // D block: lane holds rows 4 grp .. 4 grp + 3 of the tile, column col
