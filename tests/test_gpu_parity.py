@@ -77,6 +77,16 @@ def test_ragged_tails_and_empty(kind):
         assert torch.equal(s[n], d["state_in"][n])
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("h_qk,h_v", [(2, 2), (2, 6), (1, 4), (2, 16)])
+def test_chunked_group_sizes(h_qk, h_v, io):
+    # 1, 3, 4 and 8 value heads per query/key head: every value head of a
+    # group reads its query/key head's rows and fragments
+    args = ("f32", 0.0, 0.5) if io == "f32" else ("bf16", 2.0, 0.05)
+    inp = make_prefill([200, 70], h_qk, h_v, 64, 64, *args, seed=70 + h_v)
+    check_prefill(inp, "chunked", 64)
+
+
 # ---------------------------------------------------------------- the named workloads
 def test_tiny_fp32():
     inp = tiny_fp32_prefill()
