@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="headline calls and the copy calibration only")
     ap.add_argument("--attention-counters", action="store_true",
                     help="eager decode-attention calls at 32K and 128K and the copy calibration only")
+    ap.add_argument("--moe-counters", action="store_true",
+                    help="eager 4-bit expert GEMM calls at 512 and 2048 tokens and the copy calibration only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no "
@@ -182,6 +184,33 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
+
+    def copy_calibration():
+        src = torch.ones(1 << 28, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 536870912 bytes read, 536870912 written")
+
+    if args.moe_counters:
+        # counter runs: three eager calls of the fused expert GEMM per prompt
+        # size (the bench leg's inputs), then the calibration copy
+        from gated_deltanet_linear_delta_amd.workloads import make_moe
+        for tok in (512, 2048):
+            mi = make_moe(tok, num_experts=256, top_k=8, k=2048, n=1024, seed=5000 + tok)
+            bfd = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
+            xm, offm = bfd(mi.x), torch.from_numpy(mi.expert_offsets.astype(np.int32)).to(dev)
+            cm, sm, bm = torch.from_numpy(mi.codes).to(dev), bfd(mi.scales), bfd(mi.biases)
+            ym = torch.empty((xm.shape[0], 1024), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                gdn.moe_gemm_q4(xm, offm, cm, sm, bm, y=ym)
+            torch.cuda.synchronize()
+            log(f"expert GEMM at {tok} tokens: three calls")
+            del xm, offm, cm, sm, bm, ym
+            torch.cuda.empty_cache()
+        copy_calibration()
+        print(json.dumps({"moe_counters": True}), flush=True)
+        return
 
     if args.attention_counters:
         # counter runs: graph replays are left out (rocprofv3's counter
@@ -200,11 +229,7 @@ def main():
             log(f"attention at {TA}: three calls")
             del qa, ka, va, oa, wsa
             torch.cuda.empty_cache()
-        src = torch.ones(1 << 28, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 536870912 bytes read, 536870912 written")
+        copy_calibration()
         print(json.dumps({"attention_counters": True}), flush=True)
         return
 
