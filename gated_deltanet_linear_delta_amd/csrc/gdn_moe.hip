@@ -108,13 +108,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   uint8_t* sa = smem + (size_t(n_exp + 1) * 4 + 15) / 16 * 16;
   uint8_t* ssb = sa + 2 * ABUF;
   // Workgroups reach the eight XCDs round-robin (workgroup i on XCD i % 8).
-  // The ncb column blocks of one row-block slot all go to the same XCD, so
-  // the slot's activation rows come from HBM once and from that XCD's L2 for
-  // the other column blocks: workgroup i is column block (i / 8) % ncb of
-  // slot 8 ((i / 8) / ncb) + i % 8.
+  // XCD x takes the contiguous slots [x S8, x S8 + S8) (S8 = slots / 8, the
+  // slot count being a multiple of 8), in order, each with its ncb column
+  // blocks together: the column blocks share the slot's activation rows, and
+  // the row blocks of one expert, adjacent slots, share its codes, through
+  // that XCD's L2.  Workgroup i is column block (i / 8) % ncb of slot
+  // (i % 8) S8 + (i / 8) / ncb.
   const int ncb = n / BN;
+  const int S8 = int(gridDim.x) / (8 * ncb);
   const int xi = int(blockIdx.x >> 3);
-  const int slot = 8 * (xi / ncb) + int(blockIdx.x & 7), cb = xi % ncb;
+  const int slot = int(blockIdx.x & 7) * S8 + xi / ncb, cb = xi % ncb;
   for (int i = threadIdx.x; i <= n_exp; i += 256) {
     int o = offsets[i];
     soff[i] = o < 0 ? 0 : (o > m ? m : o);  // malformed offsets cannot index out of bounds
