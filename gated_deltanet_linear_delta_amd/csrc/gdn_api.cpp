@@ -219,7 +219,8 @@ gdn_status_t gdn_prefill_chunked(const gdn_shape_t* shape, const void* q, const 
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
     return fail(GDN_ERR_UNSUPPORTED, "%s: chunk_size %d; supported sizes are 16, 32, 64", what, chunk_size);
   const gdn::Dims d = dims_of(shape);
-  if (gdn::chunked_max_chunks(d, chunk_size) > size_t(1u << 31) - 1)
+  // the prep runs one workgroup per (chunk, value head), indexed in int
+  if (gdn::chunked_max_chunks(d, chunk_size) * size_t(d.h_v) > size_t(1u << 31) - 8)
     return fail(GDN_ERR_UNSUPPORTED, "%s: too many chunks", what);
   const size_t need = gdn::chunked_workspace_bytes(d, chunk_size);
   if (!workspace) return fail(GDN_ERR_INVALID, "%s: workspace is NULL", what);
@@ -259,7 +260,7 @@ gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, cons
   if (chunk_size > 0) {
     gdn::Dims dw = d;
     dw.total_tokens = d.total_tokens < segment_tokens ? d.total_tokens : segment_tokens;
-    if (gdn::chunked_max_chunks(dw, chunk_size) > size_t(1u << 31) - 1)
+    if (gdn::chunked_max_chunks(dw, chunk_size) * size_t(d.h_v) > size_t(1u << 31) - 8)
       return fail(GDN_ERR_UNSUPPORTED, "%s: too many chunks per segment", what);
   }
   const size_t need = gdn::segmented_workspace_bytes(d, chunk_size, segment_tokens);

@@ -30,7 +30,9 @@
 //   1. chunk_table_kernel (only for more than one sequence): per slot, the
 //      chunk's (first token, length), or (0, 0) for an unused slot.  With one
 //      sequence slot j is simply tokens [j C, min(T, j C + C)).
-//   2. chunk_prep_kernel, one workgroup per (chunk, value head), fully
+//   2. chunk_prep_kernel, one workgroup per (chunk, value head) (each XCD a
+//      contiguous range of them, so value heads sharing K and Q meet in its
+//      L2), fully
 //      parallel: Gram products on MFMA, gate prefix sums, A, T = (I + A)^{-1}
 //      (16x16 diagonal blocks by forward substitution in registers,
 //      off-diagonal blocks by fp32 MFMA block products), R = QKm T, P, and the
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int C, i
 template <typename IO, int DK, int C>
 __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
                                                          const IO* __restrict__ k, const float* __restrict__ g,
-                                                         const float* __restrict__ beta, int num_seqs, int T,
+                                                         const float* __restrict__ beta, int num_seqs, int T, int num_items,
                                                          const int2* __restrict__ tab, uint8_t* __restrict__ ws,
                                                          uint8_t* __restrict__ qf) {
   constexpr bool BF = sizeof(IO) == 2;
@@ -400,7 +402,13 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
   float* sDec = reinterpret_cast<float*>(smem + Lds::D_OFF);
 
-  const int gc = blockIdx.x, h = blockIdx.y;
+  // items p = chunk * h_v + value head, the items of XCD x (workgroups i
+  // with i % 8 == x) contiguous: value heads of one query/key head run on one
+  // XCD back to back and share its L2 for their K and Q tiles
+  const int per = int(gridDim.x) >> 3;
+  const int p = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+  if (p >= num_items) return;
+  const int gc = p / h_v, h = p % h_v;
   const int2 ch = num_seqs == 1 ? make_int2(gc * C, min(C, T - gc * C)) : tab[gc];
   const int t0 = ch.x, nc = ch.y;
   if (nc <= 0) return;
@@ -1134,9 +1142,10 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
       if (e != hipSuccess) return e;
     }
     Prof prof("chunk_prep", st);
-    hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned(max_chunks), unsigned(d.h_v)), dim3(512), lds,
+    const size_t items = max_chunks * size_t(d.h_v);
+    hipLaunchKernelGGL((chunk_prep_kernel<IO, DK, C>), dim3(unsigned((items + 7) / 8 * 8)), dim3(512), lds,
                        st, d.h_qk, d.h_v, static_cast<const IO*>(q), static_cast<const IO*>(k), g, beta, d.num_seqs,
-                       d.total_tokens, tab, ws, qf);
+                       d.total_tokens, int(items), tab, ws, qf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
