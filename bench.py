@@ -19,6 +19,9 @@ same JSON line also carries:
               unfused (torch prologue and epilogue around gdn_decode_step);
   scan        gdn_prefill_scan over the same 4096-token prompt (the
               direct-scan alternative, kept for the crossover);
+  crossover   scan against chunked on one sequence of 64 ... 131072 tokens,
+              50 timed calls each after 10 warm-ups, in alternating order,
+              with medians, p10 and p90 (the scan skipped at 131072);
   state_residency_ablation  the first 2048 tokens through the resident scan
               and through gdn_prefill_scan_blockwise (state to memory and
               back every 32 or 16 tokens), with the state bytes moved;
@@ -44,9 +47,10 @@ same JSON line also carries:
   roofline    for the longest kernel of the chunked call: algorithmic bytes
               per launch over its mean duration, from HIP events that the
               library records on the launch stream while profiling is on;
-  cpu_baseline  the fp64 oracle timed on this host on the same prompt: a
-              prefix of it, or whole passes repeated, about --cpu-seconds
-              of single-threaded work.
+  cpu_baseline  the fp64 oracle timed on this host's cores: a process pool,
+              one process per core (at most 16), over (sequence, value head)
+              items of bounded samples of the four bf16 workloads, and the
+              oracle as it stands (all heads in one process) on one core.
   traffic     HBM bytes per launch of that kernel as the FETCH_SIZE and
               WRITE_SIZE counters saw them (profiles/, scaled by the same
               counters on a copy of known size), or null once the kernel
@@ -153,12 +157,115 @@ def mean_by_name(records):
     return {k: (float(np.mean(v)), len(v)) for k, v in acc.items()}
 
 
+def _oracle_item(item):
+    """CPU baseline worker: the fp64 oracle on one (sequence, value head) item
+    (prefill tokens, or decode steps one at a time).  Runs in a spawn-started
+    process that imports numpy and the oracle only."""
+    from oracle import gated_delta_decode_step, gated_delta_recurrence
+    if item["kind"] == "prefill":
+        gated_delta_recurrence(item["q"], item["k"], item["v"], item["g"], item["beta"], state_in=item["s0"])
+    else:
+        S = item["s0"]
+        for t in range(item["q"].shape[0]):
+            _, S = gated_delta_decode_step(item["q"][t], item["k"][t], item["v"][t], item["g"][t],
+                                           item["beta"][t], S)
+    return 0
+
+
+def _host_cores(cap=16):
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def cpu_baseline_leg(log_fn):
+    """The fp64 oracle on the host cores: a process pool, one process per core,
+    over (sequence, value head) items, on bounded samples of the four bf16
+    workloads, plus the oracle as it stands (all heads in one process) on one
+    core.  Tokens/s per workload."""
+    import multiprocessing as mp
+    from gated_deltanet_linear_delta_amd.workloads import make_decode, make_prefill, ragged_lengths
+
+    def f32(a):
+        return np.ascontiguousarray(a, dtype=np.float32)
+
+    def prefill_items(inp, seqs):
+        G = inp.v.shape[1] // inp.q.shape[1]
+        cu = inp.cu_seqlens
+        for n in seqs:
+            a, b = int(cu[n]), int(cu[n + 1])
+            for h in range(inp.v.shape[1]):
+                j = h // G
+                yield {"kind": "prefill", "q": f32(inp.q[a:b, j:j + 1]), "k": f32(inp.k[a:b, j:j + 1]),
+                       "v": f32(inp.v[a:b, h:h + 1]), "g": f32(inp.g[a:b, h:h + 1]),
+                       "beta": f32(inp.beta[a:b, h:h + 1]),
+                       "s0": None if inp.state_in is None else f32(inp.state_in[n:n + 1, h:h + 1])}
+
+    def decode_items(dec):
+        G = dec.v.shape[2] // dec.q.shape[2]
+        for h in range(dec.v.shape[2]):
+            j = h // G
+            yield {"kind": "decode", "q": f32(dec.q[:, :, j:j + 1]), "k": f32(dec.k[:, :, j:j + 1]),
+                   "v": f32(dec.v[:, :, h:h + 1]), "g": f32(dec.g[:, :, h:h + 1]), "beta": f32(dec.beta[:, :, h:h + 1]),
+                   "s0": f32(dec.state[:, h:h + 1])}
+
+    cores = _host_cores()
+    rng4 = np.random.default_rng(1004)
+    lens4 = ragged_lengths(rng4, 32)
+    cases = {
+        "decode_1000_steps": ("decode", make_decode(1000, 1, HQK, HV, DK, DV, "bf16", 0.0, 0.02,
+                                                   rng=np.random.default_rng(1001)), None,
+                              "all 1000 steps, 32 value heads"),
+        "prefill_4096": ("prefill", make_prefill([4096], HQK, HV, DK, DV, "bf16", 2.0, None,
+                                                 rng=np.random.default_rng(1002)), [0],
+                         "all 4096 tokens, 32 value heads"),
+        "prefill_131072": ("prefill", make_prefill([8192], HQK, HV, DK, DV, "bf16", 2.0, None,
+                                                   rng=np.random.default_rng(1003)), [0],
+                           "the first 8192 tokens (same distributions), 32 value heads"),
+        "ragged_32_then_decode": ("prefill", make_prefill(lens4[:4], HQK, HV, DK, DV, "bf16", 2.0, 0.02,
+                                                          rng=np.random.default_rng(1004)), [0, 1, 2, 3],
+                                  f"prefill of 4 of the 32 sequences ({int(sum(lens4[:4]))} tokens, "
+                                  "the workload's first four lengths), 32 value heads"),
+    }
+    per = {}
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_item, [{"kind": "decode", "q": np.zeros((1, 1, 1, 4), np.float32),
+                                 "k": np.zeros((1, 1, 1, 4), np.float32), "v": np.zeros((1, 1, 1, 4), np.float32),
+                                 "g": np.zeros((1, 1, 1), np.float32), "beta": np.zeros((1, 1, 1), np.float32),
+                                 "s0": np.zeros((1, 1, 4, 4), np.float32)}] * cores)  # start the workers
+        for name, (kind, inp, seqs, what) in cases.items():
+            items = list(decode_items(inp) if kind == "decode" else prefill_items(inp, seqs))
+            tokens = inp.q.shape[0] * (inp.q.shape[1] if kind == "decode" else 1)
+            t0 = time.perf_counter()
+            pool.map(_oracle_item, items, chunksize=1)
+            el = time.perf_counter() - t0
+            per[name] = {"tokens_per_s": round(tokens / el, 1), "seconds": round(el, 2), "items": len(items),
+                         "sample": what}
+            log_fn(f"cpu baseline {name}: {per[name]}")
+    # the oracle as it stands, on one core: all heads vectorised in one process
+    from oracle import gated_delta_recurrence
+    inp2 = cases["prefill_4096"][1]
+    n_tok = 512
+    t0 = time.perf_counter()
+    gated_delta_recurrence(inp2.q[:n_tok], inp2.k[:n_tok], inp2.v[:n_tok], inp2.g[:n_tok], inp2.beta[:n_tok])
+    el1 = time.perf_counter() - t0
+    single = {"tokens_per_s": round(n_tok / el1, 1), "seconds": round(el1, 2),
+              "sample": f"the first {n_tok} tokens of the 4096-token prompt, all 32 value heads in one process"}
+    return {"value": per["prefill_4096"]["tokens_per_s"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"prefill_4096: {per['prefill_4096']['sample']}, fp64 NumPy token loop, one process per "
+                      f"core over {per['prefill_4096']['items']} (sequence, value head) items "
+                      f"({per['prefill_4096']['seconds']} s)",
+            "per_workload": per, "single_core": single, "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the 4-bit expert GEMM leg")
@@ -170,6 +277,11 @@ def main():
                     help="eager decode-attention calls at 32K and 128K and the copy calibration only")
     ap.add_argument("--moe-counters", action="store_true",
                     help="eager 4-bit expert GEMM calls at 512 and 2048 tokens and the copy calibration only")
+    ap.add_argument("--decode-counters", action="store_true",
+                    help="eager decode steps (B=1 and B=32, state sets rotating past the Infinity Cache) and the "
+                         "copy calibration only")
+    ap.add_argument("--no-crossover", action="store_true", help="skip the scan-vs-chunked prompt-length sweep")
+    ap.add_argument("--crossover-reps", type=int, default=50, help="timed calls per kernel and prompt length")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer core has no "
@@ -210,6 +322,28 @@ def main():
             torch.cuda.empty_cache()
         copy_calibration()
         print(json.dumps({"moe_counters": True}), flush=True)
+        return
+
+    if args.decode_counters:
+        # counter runs: eager steps (no graphs), each batch rotating over state
+        # sets larger than the Infinity Cache, so every step streams its state
+        # from HBM; then the calibration copy
+        for B, n_sets in ((1, 256), (32, 8)):
+            dec = make_decode(n_sets, B, HQK, HV, DK, DV, "bf16", 2.0 if B > 1 else 0.0, 0.02, seed=1001 + B)
+            bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
+            dq, dk_, dv_ = bf(dec.q), bf(dec.k), bf(dec.v)
+            dg, db = torch.from_numpy(dec.g).to(dev), torch.from_numpy(dec.beta).to(dev)
+            states = [torch.from_numpy(dec.state).to(dev).clone() for _ in range(n_sets)]
+            dout = torch.empty((B, HV, DV), dtype=torch.bfloat16, device=dev)
+            for i in range(2 * n_sets):
+                s_ = i % n_sets
+                gdn.decode_step(dq[s_], dk_[s_], dv_[s_], dg[s_], db[s_], states[s_], out=dout, state_out=states[s_])
+            torch.cuda.synchronize()
+            log(f"decode B={B}: {2 * n_sets} eager steps over {n_sets} state sets")
+            del states, dq, dk_, dv_, dg, db, dout
+            torch.cuda.empty_cache()
+        copy_calibration()
+        print(json.dumps({"decode_counters": True}), flush=True)
         return
 
     if args.attention_counters:
@@ -269,6 +403,20 @@ def main():
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
     log(f"chunked prefill: {ms_step * 1e3:.1f} us per call (wall, {K} calls)")
+
+    # per-call distribution: HIP events around each call, max(50, K) calls
+    n_ev = max(50, K)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for e0, e1 in evs:
+        e0.record()
+        prefill()
+        e1.record()
+    torch.cuda.synchronize()
+    call_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    call_stats = {"calls": n_ev, "median_us": round(float(np.median(call_us)), 2),
+                  "p10_us": round(float(np.percentile(call_us, 10)), 2),
+                  "p90_us": round(float(np.percentile(call_us, 90)), 2)}
+    log(f"chunked prefill per call (events): {call_stats}")
 
     gdn.profile_enable(True)
     for _ in range(K):
@@ -416,8 +564,10 @@ def main():
 
     log("decode legs")
     dec_b1 = decode_leg(1, 1, 200, 1001)
+    dec_b1_cold = decode_leg(1, 256, 256, 1001)
     dec_b32 = decode_leg(32, 8, 64, 1004)
     log(f"decode B=1: {dec_b1}")
+    log(f"decode B=1 cold: {dec_b1_cold}")
     log(f"decode B=32 cold: {dec_b32}")
     fused_b1 = fused_leg(1, 1, 200, 2001)
     fused_b32 = fused_leg(32, 8, 64, 2004)
@@ -444,6 +594,70 @@ def main():
                 "tokens_per_s": round(T / (scan_wall * 1e-3), 1),
                 "chunked_speedup": round(scan_wall / ms_step, 2)}
         log(f"direct scan: {scan}")
+
+    # ------------------------------------------------------------ scan vs chunked over prompt length
+    # One sequence of T tokens (16 q/k and 32 v heads, d = 128, bf16, inputs
+    # drawn on the device with the workloads' distributions), both kernels,
+    # 10 untimed calls each, then reps rounds whose order alternates (scan
+    # first in even rounds, chunked first in odd ones), each call timed by
+    # HIP events; median, p10 and p90 per kernel.  The scan is skipped at
+    # 131072 tokens (about 30 ms a call).
+    crossover = None
+    if not args.no_crossover and not args.no_scan:
+        crossover = {"reps": args.crossover_reps, "warmup": 10, "lengths": {}}
+        gen = torch.Generator(device=dev)
+        for TC in (64, 256, 1024, 4096, 16384, 65536, 131072):
+            gen.manual_seed(7000 + TC)
+            unit = lambda x: (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+            qC = unit(torch.randn((TC, HQK, DK), generator=gen, device=dev))
+            kC = unit(torch.randn((TC, HQK, DK), generator=gen, device=dev))
+            vC = torch.randn((TC, HV, DV), generator=gen, device=dev).to(torch.bfloat16)
+            bC = torch.sigmoid(torch.randn((TC, HV), generator=gen, device=dev))
+            gC = -torch.nn.functional.softplus(torch.randn((TC, HV), generator=gen, device=dev) + 2.0)
+            cuC = torch.tensor([0, TC], dtype=torch.int32, device=dev)
+            oC = torch.empty((TC, HV, DV), dtype=torch.bfloat16, device=dev)
+            sC = torch.empty((1, HV, DV, DK), dtype=torch.float32, device=dev)
+            wsC = gdn.alloc_workspace(gdn.chunked_workspace_bytes(1, TC, HQK, HV, DK, DV, gdn.GDN_DTYPE_BF16, CHUNK),
+                                      dev)
+            calls = {"chunked": lambda: gdn.prefill_chunked(qC, kC, vC, gC, bC, cuC, None, out=oC, state_out=sC,
+                                                             chunk_size=CHUNK, workspace=wsC)}
+            if TC < 131072:
+                calls["scan"] = lambda: gdn.prefill_scan(qC, kC, vC, gC, bC, cuC, None, out=oC, state_out=sC)
+            for fn in calls.values():
+                for _ in range(10):
+                    fn()
+            torch.cuda.synchronize()
+            times = {name: [] for name in calls}
+            names = list(calls)
+            for r in range(args.crossover_reps):
+                order = names if r % 2 == 0 else names[::-1]
+                evs = []
+                for name in order:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    calls[name]()
+                    e1.record()
+                    evs.append((name, e0, e1))
+                torch.cuda.synchronize()
+                for name, e0, e1 in evs:
+                    times[name].append(e0.elapsed_time(e1) * 1e3)
+            res = {}
+            for name, ts in times.items():
+                ts = np.array(ts)
+                med = float(np.median(ts))
+                res[name] = {"median_us": round(med, 2), "p10_us": round(float(np.percentile(ts, 10)), 2),
+                             "p90_us": round(float(np.percentile(ts, 90)), 2),
+                             "tokens_per_s": round(TC / (med * 1e-6), 1)}
+            if "scan" in res:
+                res["chunked_speedup"] = round(res["scan"]["median_us"] / res["chunked"]["median_us"], 3)
+            crossover["lengths"][str(TC)] = res
+            log(f"crossover T={TC}: {res}")
+            del qC, kC, vC, bC, gC, oC, sC, wsC
+            torch.cuda.empty_cache()
+        # the shortest measured length from which on the chunked form is faster at every measured length
+        sp = {int(t): r["chunked_speedup"] for t, r in crossover["lengths"].items() if "chunked_speedup" in r}
+        crossover["chunked_faster_from_tokens"] = next(
+            (t for t in sorted(sp) if all(sp[u] > 1.0 for u in sp if u >= t)), None)
 
     # ------------------------------------------------------------ state on chip vs blockwise
     # The pages' ablation: a 2K-token prompt, the register-resident scan against
@@ -703,24 +917,7 @@ def main():
     # ------------------------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import gated_delta_recurrence
-        n_tok = 32
-        t3 = time.perf_counter()
-        gated_delta_recurrence(inp.q[:n_tok], inp.k[:n_tok], inp.v[:n_tok], inp.g[:n_tok], inp.beta[:n_tok])
-        per_tok = (time.perf_counter() - t3) / n_tok
-        n_tok = int(min(T, max(64, args.cpu_seconds / per_tok)))
-        # When the whole prompt takes less than the budget, repeat whole passes
-        # until it is spent, so that the sample is long enough to time.
-        passes = 1 if n_tok < T else max(1, int(round(args.cpu_seconds / (per_tok * T))))
-        t3 = time.perf_counter()
-        for _ in range(passes):
-            gated_delta_recurrence(inp.q[:n_tok], inp.k[:n_tok], inp.v[:n_tok], inp.g[:n_tok], inp.beta[:n_tok])
-        el = time.perf_counter() - t3
-        what = (f"first {n_tok} of the {T} prompt tokens" if passes == 1
-                else f"{passes} passes over all {T} prompt tokens")
-        cpu = {"value": round(passes * n_tok / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{what}, all 32 value heads, fp64 NumPy token loop ({el:.1f} s)",
-               "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+        cpu = cpu_baseline_leg(log)
         log(f"cpu baseline: {cpu}")
 
     line = {
@@ -742,10 +939,11 @@ def main():
         "mfma_util": round(mfma_util, 4),
         "algorithmic_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {n: round(m * 1e3, 2) for n, (m, _) in per_kernel.items()},
+        "call_us_events": call_stats,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
-        "decode": {"b1_warm": dec_b1, "b32_cold": dec_b32},
+        "decode": {"b1_warm": dec_b1, "b1_cold": dec_b1_cold, "b32_cold": dec_b32},
         "decode_fused": {"b1_warm": fused_b1, "b32_cold": fused_b32},
         "state_residency_ablation": ablation,
         "segmented_prefill": segmented,
@@ -753,6 +951,7 @@ def main():
         "moe_gemm_q4": moe,
         "attention_decode": attention,
         "scan": scan,
+        "crossover": crossover,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -9,6 +9,7 @@ every entry point raises.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -154,6 +155,14 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocate on the stream the kernels run on.  torch's caching allocator
+    hands a freed block only to later allocations on the stream it was
+    allocated on, so a workspace (or output) allocated under `stream` cannot
+    be reused by other work while the kernels still read it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in):
     io = _io_dtype(q)
     T, h_qk, d_k = q.shape
@@ -186,11 +195,12 @@ def _outputs(shape: GdnShape, like, out, state_out):
 def prefill_scan(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, stream=None):
     """Direct token scan (gdn_prefill_scan).  Returns (out, state_out)."""
     lib = load_library()
-    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
-    out, state_out = _outputs(shape, q, out, state_out)
-    _check(lib.gdn_prefill_scan(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+        out, state_out = _outputs(shape, q, out, state_out)
+        _check(lib.gdn_prefill_scan(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
+        return out, state_out
 
 
 def prefill_scan_blockwise(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, state_block=32,
@@ -199,12 +209,13 @@ def prefill_scan_blockwise(q, k, v, g, beta, cu_seqlens, state_in=None, out=None
     scan with its state moved to state_out and back every ``state_block``
     tokens.  Returns (out, state_out)."""
     lib = load_library()
-    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
-    out, state_out = _outputs(shape, q, out, state_out)
-    _check(lib.gdn_prefill_scan_blockwise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                          _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out),
-                                          int(state_block), _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+        out, state_out = _outputs(shape, q, out, state_out)
+        _check(lib.gdn_prefill_scan_blockwise(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                              _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                              int(state_block), _stream(stream)))
+        return out, state_out
 
 
 def chunked_workspace_bytes(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype=GDN_DTYPE_BF16, chunk_size=64):
@@ -229,18 +240,19 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state
     ``workspace`` is a uint8 device tensor from alloc_workspace (allocated
     here if None)."""
     lib = load_library()
-    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
-    out, state_out = _outputs(shape, q, out, state_out)
-    need = int(lib.gdn_prefill_chunked_workspace(ctypes.byref(shape), int(chunk_size)))
-    if workspace is None:
-        workspace = alloc_workspace(need, q.device)
-    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
-        raise TypeError("workspace must be a uint8 GPU tensor")
-    wp, wn = _aligned_ptr(workspace)
-    _check(lib.gdn_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
-                                   ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)), _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+        out, state_out = _outputs(shape, q, out, state_out)
+        need = int(lib.gdn_prefill_chunked_workspace(ctypes.byref(shape), int(chunk_size)))
+        if workspace is None:
+            workspace = alloc_workspace(need, q.device)
+        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+            raise TypeError("workspace must be a uint8 GPU tensor")
+        wp, wn = _aligned_ptr(workspace)
+        _check(lib.gdn_prefill_chunked(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
+                                       ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)), _stream(stream)))
+        return out, state_out
 
 
 def segmented_workspace_bytes(num_seqs, total_tokens, h_qk, h_v, d_k, d_v, io_dtype=GDN_DTYPE_BF16, chunk_size=64,
@@ -256,19 +268,20 @@ def prefill_segmented(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, sta
     carried between them (gdn_prefill_segmented); chunk_size 0 runs the
     direct scan in each window.  Returns (out, state_out)."""
     lib = load_library()
-    shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
-    out, state_out = _outputs(shape, q, out, state_out)
-    need = int(lib.gdn_prefill_segmented_workspace(ctypes.byref(shape), int(chunk_size), int(segment_tokens)))
-    if workspace is None:
-        workspace = alloc_workspace(need, q.device)
-    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
-        raise TypeError("workspace must be a uint8 GPU tensor")
-    wp, wn = _aligned_ptr(workspace)
-    _check(lib.gdn_prefill_segmented(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                     _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
-                                     int(segment_tokens), ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)),
-                                     _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+        out, state_out = _outputs(shape, q, out, state_out)
+        need = int(lib.gdn_prefill_segmented_workspace(ctypes.byref(shape), int(chunk_size), int(segment_tokens)))
+        if workspace is None:
+            workspace = alloc_workspace(need, q.device)
+        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+            raise TypeError("workspace must be a uint8 GPU tensor")
+        wp, wn = _aligned_ptr(workspace)
+        _check(lib.gdn_prefill_segmented(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
+                                         int(segment_tokens), ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)),
+                                         _stream(stream)))
+        return out, state_out
 
 
 def decode_step(q, k, v, g, beta, state_in, out=None, state_out=None, stream=None):
@@ -277,26 +290,27 @@ def decode_step(q, k, v, g, beta, state_in, out=None, state_out=None, stream=Non
     ``state_out`` may be ``state_in`` for an in-place update.  Returns
     (out, state_out)."""
     lib = load_library()
-    io = _io_dtype(q)
-    B, h_qk, d_k = q.shape
-    h_v, d_v = v.shape[1], v.shape[2]
-    _need(k, "k", q.dtype, (B, h_qk, d_k))
-    _need(q, "q", q.dtype, (B, h_qk, d_k))
-    _need(v, "v", q.dtype, (B, h_v, d_v))
-    _need(g, "g", torch.float32, (B, h_v))
-    _need(beta, "beta", torch.float32, (B, h_v))
-    _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
-    if out is None:
-        out = torch.empty((B, h_v, d_v), dtype=q.dtype, device=q.device)
-    else:
-        _need(out, "out", q.dtype, (B, h_v, d_v))
-    if state_out is None:
-        state_out = torch.empty_like(state_in)
-    else:
-        _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
-    _check(lib.gdn_decode_step(B, h_qk, h_v, d_k, d_v, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        io = _io_dtype(q)
+        B, h_qk, d_k = q.shape
+        h_v, d_v = v.shape[1], v.shape[2]
+        _need(k, "k", q.dtype, (B, h_qk, d_k))
+        _need(q, "q", q.dtype, (B, h_qk, d_k))
+        _need(v, "v", q.dtype, (B, h_v, d_v))
+        _need(g, "g", torch.float32, (B, h_v))
+        _need(beta, "beta", torch.float32, (B, h_v))
+        _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
+        if out is None:
+            out = torch.empty((B, h_v, d_v), dtype=q.dtype, device=q.device)
+        else:
+            _need(out, "out", q.dtype, (B, h_v, d_v))
+        if state_out is None:
+            state_out = torch.empty_like(state_in)
+        else:
+            _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
+        _check(lib.gdn_decode_step(B, h_qk, h_v, d_k, d_v, io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(state_in), _ptr(out), _ptr(state_out), _stream(stream)))
+        return out, state_out
 
 
 def decode_step_fused(q_raw, k_raw, v, g_raw, beta_raw, state_in, gate_bias=None, gate_scale=None,
@@ -307,32 +321,33 @@ def decode_step_fused(q_raw, k_raw, v, g_raw, beta_raw, state_in, gate_bias=None
     state_in [B, h_v, d_v, d_k]; gate_bias, gate_scale [h_v] and norm_weight
     [d_v] fp32 or None.  Returns (out, state_out)."""
     lib = load_library()
-    io = _io_dtype(q_raw)
-    B, h_qk, d_k = q_raw.shape
-    h_v, d_v = v.shape[1], v.shape[2]
-    _need(q_raw, "q_raw", q_raw.dtype, (B, h_qk, d_k))
-    _need(k_raw, "k_raw", q_raw.dtype, (B, h_qk, d_k))
-    _need(v, "v", q_raw.dtype, (B, h_v, d_v))
-    _need(g_raw, "g_raw", torch.float32, (B, h_v))
-    _need(beta_raw, "beta_raw", torch.float32, (B, h_v))
-    _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
-    for t, name, n in ((gate_bias, "gate_bias", h_v), (gate_scale, "gate_scale", h_v),
-                       (norm_weight, "norm_weight", d_v)):
-        if t is not None:
-            _need(t, name, torch.float32, (n,))
-    if out is None:
-        out = torch.empty((B, h_v, d_v), dtype=q_raw.dtype, device=q_raw.device)
-    else:
-        _need(out, "out", q_raw.dtype, (B, h_v, d_v))
-    if state_out is None:
-        state_out = torch.empty_like(state_in)
-    else:
-        _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
-    params = GdnFusedParams(_ptr(gate_bias), _ptr(gate_scale), _ptr(norm_weight), float(qk_eps), float(norm_eps))
-    _check(lib.gdn_decode_step_fused(B, h_qk, h_v, d_k, d_v, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_raw),
-                                     _ptr(beta_raw), ctypes.byref(params), _ptr(state_in), _ptr(out),
-                                     _ptr(state_out), _stream(stream)))
-    return out, state_out
+    with _on(stream):
+        io = _io_dtype(q_raw)
+        B, h_qk, d_k = q_raw.shape
+        h_v, d_v = v.shape[1], v.shape[2]
+        _need(q_raw, "q_raw", q_raw.dtype, (B, h_qk, d_k))
+        _need(k_raw, "k_raw", q_raw.dtype, (B, h_qk, d_k))
+        _need(v, "v", q_raw.dtype, (B, h_v, d_v))
+        _need(g_raw, "g_raw", torch.float32, (B, h_v))
+        _need(beta_raw, "beta_raw", torch.float32, (B, h_v))
+        _need(state_in, "state_in", torch.float32, (B, h_v, d_v, d_k))
+        for t, name, n in ((gate_bias, "gate_bias", h_v), (gate_scale, "gate_scale", h_v),
+                           (norm_weight, "norm_weight", d_v)):
+            if t is not None:
+                _need(t, name, torch.float32, (n,))
+        if out is None:
+            out = torch.empty((B, h_v, d_v), dtype=q_raw.dtype, device=q_raw.device)
+        else:
+            _need(out, "out", q_raw.dtype, (B, h_v, d_v))
+        if state_out is None:
+            state_out = torch.empty_like(state_in)
+        else:
+            _need(state_out, "state_out", torch.float32, (B, h_v, d_v, d_k))
+        params = GdnFusedParams(_ptr(gate_bias), _ptr(gate_scale), _ptr(norm_weight), float(qk_eps), float(norm_eps))
+        _check(lib.gdn_decode_step_fused(B, h_qk, h_v, d_k, d_v, io, _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_raw),
+                                         _ptr(beta_raw), ctypes.byref(params), _ptr(state_in), _ptr(out),
+                                         _ptr(state_out), _stream(stream)))
+        return out, state_out
 
 
 def _moe_shape(x, expert_offsets, codes_or_weights, packed):
@@ -350,50 +365,53 @@ def moe_gemm_q4(x, expert_offsets, codes, scales, biases, y=None, stream=None):
     [E, N, K / 2] uint8; scales, biases [E, N, K / 64] bf16.  Returns y [M, N]
     bf16."""
     lib = load_library()
-    shape = _moe_shape(x, expert_offsets, codes, True)
-    E, N, K = shape.num_experts, shape.n, shape.k
-    _need(codes, "codes", torch.uint8, (E, N, K // 2))
-    _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
-    _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
-    if y is None:
-        y = torch.empty((shape.rows, N), dtype=torch.bfloat16, device=x.device)
-    else:
-        _need(y, "y", torch.bfloat16, (shape.rows, N))
-    _check(lib.gdn_moe_gemm_q4(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(codes), _ptr(scales),
-                               _ptr(biases), _ptr(y), _stream(stream)))
-    return y
+    with _on(stream):
+        shape = _moe_shape(x, expert_offsets, codes, True)
+        E, N, K = shape.num_experts, shape.n, shape.k
+        _need(codes, "codes", torch.uint8, (E, N, K // 2))
+        _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
+        _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
+        if y is None:
+            y = torch.empty((shape.rows, N), dtype=torch.bfloat16, device=x.device)
+        else:
+            _need(y, "y", torch.bfloat16, (shape.rows, N))
+        _check(lib.gdn_moe_gemm_q4(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(codes), _ptr(scales),
+                                   _ptr(biases), _ptr(y), _stream(stream)))
+        return y
 
 
 def dequant_q4(codes, scales, biases, weights=None, stream=None):
     """The whole bf16 weight matrix [E, N, K] rebuilt from 4-bit codes
     (gdn_dequant_q4, the ablation's separate pass)."""
     lib = load_library()
-    E, N, K = codes.shape[0], codes.shape[1], codes.shape[2] * 2
-    _need(codes, "codes", torch.uint8, (E, N, K // 2))
-    _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
-    _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
-    if weights is None:
-        weights = torch.empty((E, N, K), dtype=torch.bfloat16, device=codes.device)
-    else:
-        _need(weights, "weights", torch.bfloat16, (E, N, K))
-    shape = GdnMoeShape(E, 0, K, N)
-    _check(lib.gdn_dequant_q4(ctypes.byref(shape), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(weights),
-                              _stream(stream)))
-    return weights
+    with _on(stream):
+        E, N, K = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+        _need(codes, "codes", torch.uint8, (E, N, K // 2))
+        _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
+        _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
+        if weights is None:
+            weights = torch.empty((E, N, K), dtype=torch.bfloat16, device=codes.device)
+        else:
+            _need(weights, "weights", torch.bfloat16, (E, N, K))
+        shape = GdnMoeShape(E, 0, K, N)
+        _check(lib.gdn_dequant_q4(ctypes.byref(shape), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(weights),
+                                  _stream(stream)))
+        return weights
 
 
 def moe_gemm_bf16(x, expert_offsets, weights, y=None, stream=None):
     """The same grouped GEMM on bf16 weights [E, N, K] (gdn_moe_gemm_bf16)."""
     lib = load_library()
-    shape = _moe_shape(x, expert_offsets, weights, False)
-    _need(weights, "weights", torch.bfloat16, (shape.num_experts, shape.n, shape.k))
-    if y is None:
-        y = torch.empty((shape.rows, shape.n), dtype=torch.bfloat16, device=x.device)
-    else:
-        _need(y, "y", torch.bfloat16, (shape.rows, shape.n))
-    _check(lib.gdn_moe_gemm_bf16(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(weights), _ptr(y),
-                                 _stream(stream)))
-    return y
+    with _on(stream):
+        shape = _moe_shape(x, expert_offsets, weights, False)
+        _need(weights, "weights", torch.bfloat16, (shape.num_experts, shape.n, shape.k))
+        if y is None:
+            y = torch.empty((shape.rows, shape.n), dtype=torch.bfloat16, device=x.device)
+        else:
+            _need(y, "y", torch.bfloat16, (shape.rows, shape.n))
+        _check(lib.gdn_moe_gemm_bf16(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(weights), _ptr(y),
+                                     _stream(stream)))
+        return y
 
 
 def _attn_params(head_dim, scale, layout, heads_per_group, num_blocks):
@@ -419,32 +437,33 @@ def attention_decode(q, k_cache, v_cache, context_lens, scale=None, layout="auto
     "fixed_block"; scale None means 1 / sqrt(d).  Returns out [B, h_q, d]
     bf16."""
     lib = load_library()
-    if k_cache.dim() != 4 or q.dim() != 3:
-        raise ValueError("q must be [B, h_q, d] and k_cache [B, h_kv, T_max, d]")
-    B, h_kv, T, d = k_cache.shape
-    h_q = q.shape[1]
-    _need(q, "q", torch.bfloat16, (B, h_q, d))
-    _need(k_cache, "k_cache", torch.bfloat16, (B, h_kv, T, d))
-    _need(v_cache, "v_cache", torch.bfloat16, (B, h_kv, T, d))
-    _need(context_lens, "context_lens", torch.int32, (B,))
-    if out is None:
-        out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
-    else:
-        _need(out, "out", torch.bfloat16, (B, h_q, d))
-    shape = GdnAttnShape(B, h_q, h_kv, d, T)
-    params = _attn_params(d, scale, layout, heads_per_group, num_blocks)
-    need = int(lib.gdn_attention_decode_workspace(ctypes.byref(shape), ctypes.byref(params)))
-    wp, wn = 0, 0
-    if need > 0:
-        if workspace is None:
-            workspace = alloc_workspace(need, q.device)
-        if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
-            raise TypeError("workspace must be a uint8 GPU tensor")
-        wp, wn = _aligned_ptr(workspace)
-    _check(lib.gdn_attention_decode(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_cache),
-                                    _ptr(v_cache), _ptr(context_lens), _ptr(out), ctypes.c_void_p(wp),
-                                    ctypes.c_size_t(max(wn, 0)), _stream(stream)))
-    return out
+    with _on(stream):
+        if k_cache.dim() != 4 or q.dim() != 3:
+            raise ValueError("q must be [B, h_q, d] and k_cache [B, h_kv, T_max, d]")
+        B, h_kv, T, d = k_cache.shape
+        h_q = q.shape[1]
+        _need(q, "q", torch.bfloat16, (B, h_q, d))
+        _need(k_cache, "k_cache", torch.bfloat16, (B, h_kv, T, d))
+        _need(v_cache, "v_cache", torch.bfloat16, (B, h_kv, T, d))
+        _need(context_lens, "context_lens", torch.int32, (B,))
+        if out is None:
+            out = torch.empty((B, h_q, d), dtype=torch.bfloat16, device=q.device)
+        else:
+            _need(out, "out", torch.bfloat16, (B, h_q, d))
+        shape = GdnAttnShape(B, h_q, h_kv, d, T)
+        params = _attn_params(d, scale, layout, heads_per_group, num_blocks)
+        need = int(lib.gdn_attention_decode_workspace(ctypes.byref(shape), ctypes.byref(params)))
+        wp, wn = 0, 0
+        if need > 0:
+            if workspace is None:
+                workspace = alloc_workspace(need, q.device)
+            if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
+                raise TypeError("workspace must be a uint8 GPU tensor")
+            wp, wn = _aligned_ptr(workspace)
+        _check(lib.gdn_attention_decode(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(context_lens), _ptr(out), ctypes.c_void_p(wp),
+                                        ctypes.c_size_t(max(wn, 0)), _stream(stream)))
+        return out
 
 
 def profile_enable(enabled: bool = True):

@@ -1,13 +1,16 @@
 """GPU parity: the HIP kernels behind the C ABI against the fp64 oracle.
 
 Every test calls libgdn.so through the Python binding and compares with the
-oracle on the same seeded inputs, per (sequence, value head) slice, within
-1e-5 (fp32 inputs) or 3e-3 (bf16 inputs, fp32 state) relative Frobenius
-error.  Shapes are those of Perplexity's "Optimizing on-device inference for
-Apple Silicon" recurrent layer as configured here (16 query/key heads shared by
-32 value heads, d = 128, chunk 64), plus small shapes that span several
-chunks and ragged tails.  At the full long-sequence size the oracle runs on a
-sample of heads or sequences.
+oracle on the same seeded inputs, per (sequence, value head) slice, on three
+measures (metrics.py): relative Frobenius error within 1e-5 (fp32 inputs) or
+3e-3 (bf16 inputs, fp32 state), the largest elementwise error against the
+slice's largest element, and a per-token bound that a single wrong token
+cannot pass.  Shapes are those of Perplexity's "Optimizing on-device
+inference for Apple Silicon" recurrent layer as configured here (16
+query/key heads shared by 32 value heads, d = 128, chunk 64), plus small
+shapes that span several chunks and ragged tails.  At the long and ragged
+workloads every head and sequence is compared, with the oracle spread over
+the host's cores (oracle_pool.py).
 """
 import numpy as np
 import pytest
@@ -18,7 +21,8 @@ from gated_deltanet_linear_delta_amd.workloads import (decode_1000_steps, make_d
                                                      ragged_32_then_decode, tiny_fp32_prefill)
 from oracle import gated_delta_decode_step, gated_delta_recurrence
 
-from helpers import TOL, dev_prefill, f32, host, max_rel_out, max_rel_state, torch_io
+from helpers import TOL, Errors, dev_prefill, f32, host, max_rel_out, max_rel_state, out_errors, state_errors, torch_io
+from oracle_pool import check_prefill_item, host_workers, pool_map
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +40,12 @@ def check_prefill(inp, kind, chunk=None, tol=None):
     o, s = run_prefill(kind, d, chunk or inp.chunk_size)
     torch.cuda.synchronize()
     o_ref, s_ref = gated_delta_recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, inp.state_in)
-    tol = tol or TOL[inp.io_dtype]
-    eo, es = max_rel_out(host(o), o_ref, inp.cu_seqlens), max_rel_state(host(s), s_ref)
-    print(f"{kind} chunk={chunk} err_out={eo:.3e} err_state={es:.3e}", flush=True)
-    assert eo <= tol and es <= tol, (eo, es)
+    eo, es = out_errors(host(o), o_ref, inp.cu_seqlens), state_errors(host(s), s_ref)
+    print(f"{kind} chunk={chunk} out: {eo}; state: {es}", flush=True)
+    if tol is None:
+        assert eo.ok(inp.io_dtype) and es.ok(inp.io_dtype), (eo, es)
+    else:
+        assert eo.frob <= tol and es.frob <= tol, (eo, es)
     return eo, es
 
 
@@ -110,10 +116,10 @@ def test_decode_1000_steps():
     o_ref = np.zeros(o_gpu.shape)
     for t in range(steps):
         o_ref[t], S = gated_delta_decode_step(dec.q[t], dec.k[t], dec.v[t], dec.g[t], dec.beta[t], S)
-    eo = max_rel_out(o_gpu[:, 0], o_ref[:, 0], [0, steps])
-    es = max_rel_state(host(state), S)
-    print(f"decode 1000 steps err_out={eo:.3e} err_state={es:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    eo = out_errors(o_gpu[:, 0], o_ref[:, 0], [0, steps])
+    es = state_errors(host(state), S)
+    print(f"decode 1000 steps out: {eo}; state: {es}", flush=True)
+    assert eo.ok("bf16") and es.ok("bf16"), (eo, es)
 
 
 @pytest.mark.parametrize("kind", ["chunked", "scan"])
@@ -121,63 +127,79 @@ def test_prefill_4096(kind):
     check_prefill(prefill_4096(), kind, 64)
 
 
-def test_long_prefill_131072_sampled_heads():
-    """T = 131072: the chunked kernel over all 32 heads; the oracle on two
-    sampled value heads (heads are independent), all tokens and the final
-    state of those heads."""
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def test_long_prefill_131072_all_heads():
+    """T = 131072: the chunked kernel over all 32 value heads, and the oracle
+    on every head (one item per query/key head and its two value heads, in a
+    pool of host processes): all tokens and the final state."""
     inp = prefill_131072()
     d = dev_prefill(inp)
     o, s = gdn.prefill_chunked(**d, chunk_size=64)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
-    for h in (5, 30):
-        j = h // 2
-        o_ref, s_ref = gated_delta_recurrence(inp.q[:, j:j + 1], inp.k[:, j:j + 1], inp.v[:, h:h + 1],
-                                              inp.g[:, h:h + 1], inp.beta[:, h:h + 1])
-        eo = max_rel_out(host(o[:, h:h + 1]), o_ref, inp.cu_seqlens)
-        es = max_rel_state(host(s[:, h:h + 1]), s_ref)
-        print(f"T=131072 head {h}: err_out={eo:.3e} err_state={es:.3e}", flush=True)
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    o_h, s_h = o.float().cpu().numpy(), s.cpu().numpy()
+    del d, o, s
+    G = inp.v.shape[1] // inp.q.shape[1]
+
+    def items():
+        for j in range(inp.q.shape[1]):
+            hs = slice(G * j, G * j + G)
+            yield {"q": _f32(inp.q[:, j:j + 1]), "k": _f32(inp.k[:, j:j + 1]), "v": _f32(inp.v[:, hs]),
+                   "g": _f32(inp.g[:, hs]), "beta": _f32(inp.beta[:, hs]), "o": _f32(o_h[:, hs]),
+                   "s": _f32(s_h[:, hs]), "tag": f"heads {G * j}-{G * j + G - 1}"}
+
+    print(f"oracle on {host_workers()} host processes", flush=True)
+    eo, es = Errors(), Errors()
+    for res in pool_map(check_prefill_item, items()):
+        print(f"T=131072 {res['tag']}: out {res['out']}; state {res['state']}", flush=True)
+        eo, es = eo.merge(res["out"]), es.merge(res["state"])
+    print(f"T=131072 all heads: out {eo}; state {es}", flush=True)
+    assert eo.ok("bf16") and es.ok("bf16"), (eo, es)
 
 
 @pytest.mark.parametrize("kind", ["chunked", "scan"])
 def test_ragged_32_then_decode(kind):
     """32 ragged sequences with their own initial state, then 256 decode
-    steps at B=32 carried from the prefill state.  The oracle runs on a sample
-    of sequences (shortest, longest, two others), all heads."""
+    steps at B=32 carried from the prefill state.  The oracle runs on every
+    sequence, all heads, the prefill and all 256 decode steps (one item per
+    sequence in a pool of host processes)."""
     pre, dec = ragged_32_then_decode()
     d = dev_prefill(pre)
     o, s = run_prefill(kind, d, 64)
-    steps = dec.q.shape[0] if kind == "chunked" else 16
-    q, k, v = (torch_io(x[:steps], "bf16") for x in (dec.q, dec.k, dec.v))
-    g, beta = f32(dec.g[:steps]), f32(dec.beta[:steps])
+    steps = dec.q.shape[0]
+    q, k, v = (torch_io(x, "bf16") for x in (dec.q, dec.k, dec.v))
+    g, beta = f32(dec.g), f32(dec.beta)
     state = s.clone()
     outs = []
     for t in range(steps):
         od, state = gdn.decode_step(q[t], k[t], v[t], g[t], beta[t], state, state_out=state)
         outs.append(od)
     torch.cuda.synchronize()
-    o_dec = host(torch.stack(outs))
-    lens = np.diff(pre.cu_seqlens)
-    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 19})
+    o_dec = torch.stack(outs).float().cpu().numpy()
+    o_h, s_h, sd_h = o.float().cpu().numpy(), s.cpu().numpy(), state.cpu().numpy()
     cu = pre.cu_seqlens
-    for n in sample:
-        a, b = int(cu[n]), int(cu[n + 1])
-        o_ref, s_ref = gated_delta_recurrence(pre.q[a:b], pre.k[a:b], pre.v[a:b], pre.g[a:b], pre.beta[a:b],
-                                              state_in=pre.state_in[n:n + 1])
-        eo = max_rel_out(host(o[a:b]), o_ref, [0, b - a])
-        es = max_rel_state(host(s[n:n + 1]), s_ref)
-        S = s_ref
-        od_ref = np.zeros((steps,) + o_dec.shape[2:])
-        for t in range(steps):
-            ot, S = gated_delta_decode_step(dec.q[t, n:n + 1], dec.k[t, n:n + 1], dec.v[t, n:n + 1],
-                                            dec.g[t, n:n + 1], dec.beta[t, n:n + 1], S)
-            od_ref[t] = ot[0]
-        ed = max_rel_out(o_dec[:, n], od_ref, [0, steps])
-        esd = max_rel_state(host(state[n:n + 1]), S)
-        print(f"{kind} seq {n} (len {b - a}): prefill out {eo:.3e} state {es:.3e}; "
-              f"decode out {ed:.3e} state {esd:.3e}", flush=True)
-        assert max(eo, es, ed, esd) <= TOL["bf16"]
+
+    def items():
+        for n in range(len(cu) - 1):
+            a, b = int(cu[n]), int(cu[n + 1])
+            yield {"q": _f32(pre.q[a:b]), "k": _f32(pre.k[a:b]), "v": _f32(pre.v[a:b]), "g": _f32(pre.g[a:b]),
+                   "beta": _f32(pre.beta[a:b]), "state_in": _f32(pre.state_in[n:n + 1]), "o": _f32(o_h[a:b]),
+                   "s": _f32(s_h[n:n + 1]), "tag": f"seq {n} (len {b - a})",
+                   "dec": {"q": _f32(dec.q[:, n:n + 1]), "k": _f32(dec.k[:, n:n + 1]), "v": _f32(dec.v[:, n:n + 1]),
+                           "g": _f32(dec.g[:, n:n + 1]), "beta": _f32(dec.beta[:, n:n + 1]),
+                           "o": _f32(o_dec[:, n]), "s": _f32(sd_h[n:n + 1])}}
+
+    worst = {key: Errors() for key in ("out", "state", "dec_out", "dec_state")}
+    for res in pool_map(check_prefill_item, items()):
+        print(f"{kind} {res['tag']}: prefill out {res['out']}; state {res['state']}; "
+              f"decode out {res['dec_out']}; state {res['dec_state']}", flush=True)
+        for key in worst:
+            worst[key] = worst[key].merge(res[key])
+    print(f"{kind} all 32 sequences: " + "; ".join(f"{key} {e}" for key, e in worst.items()), flush=True)
+    assert all(e.ok("bf16") for e in worst.values()), worst
 
 
 # ---------------------------------------------------------------- properties
