@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgdn.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_scan.hip", "gdn_chunked.hip", "gdn_segmented.hip", "gdn_moe.hip",
-           "gdn_attention.hip"]
+           "gdn_attention.hip", "gdn_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are kept out of the device code.  MFMA

@@ -242,11 +242,11 @@ size_t gdn_prefill_segmented_workspace(const gdn_shape_t* shape, int32_t chunk_s
   return gdn::segmented_workspace_bytes(dims_of(shape), chunk_size, segment_tokens);
 }
 
-gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
-                                   const float* g, const float* beta, const int32_t* cu_seqlens,
-                                   const float* state_in, void* out, float* state_out, int32_t chunk_size,
-                                   int32_t segment_tokens, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* what = "gdn_prefill_segmented";
+namespace {
+// Checks shared by the segmented prefill and its allocation-free variant.
+gdn_status_t check_segmented(const gdn_shape_t* shape, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const int32_t* cu_seqlens, const float* state_in, const void* out,
+                             const float* state_out, int32_t chunk_size, int32_t segment_tokens, const char* what) {
   gdn_status_t st = check_prefill(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, what);
   if (st != GDN_OK) return st;
   if (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
@@ -263,6 +263,19 @@ gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, cons
     if (gdn::chunked_max_chunks(dw, chunk_size) * size_t(d.h_v) > size_t(1u << 31) - 8)
       return fail(GDN_ERR_UNSUPPORTED, "%s: too many chunks per segment", what);
   }
+  return GDN_OK;
+}
+}  // namespace
+
+gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* state_in, void* out, float* state_out, int32_t chunk_size,
+                                   int32_t segment_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "gdn_prefill_segmented";
+  gdn_status_t st = check_segmented(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, chunk_size,
+                                    segment_tokens, what);
+  if (st != GDN_OK) return st;
+  const gdn::Dims d = dims_of(shape);
   const size_t need = gdn::segmented_workspace_bytes(d, chunk_size, segment_tokens);
   if (!workspace) return fail(GDN_ERR_INVALID, "%s: workspace is NULL", what);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -271,6 +284,31 @@ gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape, const void* q, cons
     return fail(GDN_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", what, workspace_bytes, need);
   return launched(gdn::launch_segmented(d, chunk_size, segment_tokens, q, k, v, g, beta, cu_seqlens, state_in, out,
                                         state_out, workspace, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_prefill_segmented_noalloc(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                           const float* g, const float* beta, const int32_t* cu_seqlens,
+                                           const float* state_in, void* out, float* state_out, int32_t chunk_size,
+                                           int32_t segment_tokens, void* stream) {
+  const char* what = "gdn_prefill_segmented_noalloc";
+  gdn_status_t st = check_segmented(shape, q, k, v, g, beta, cu_seqlens, state_in, out, state_out, chunk_size,
+                                    segment_tokens, what);
+  if (st != GDN_OK) return st;
+  const gdn::Dims d = dims_of(shape);
+  const size_t need = gdn::segmented_workspace_bytes(d, chunk_size, segment_tokens);
+  if (need > size_t(GDN_STATIC_SCRATCH_BYTES))
+    return fail(GDN_ERR_INVALID,
+                "%s: these shapes need %zu bytes of scratch per segment of %d tokens; the static scratch holds %zu "
+                "(use fewer segment_tokens)",
+                what, need, segment_tokens, size_t(GDN_STATIC_SCRATCH_BYTES));
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  hipError_t e = gdn::static_scratch(&scratch, &scratch_bytes);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: static scratch address: %s", what, hipGetErrorString(e));
+  if (scratch_bytes < need) return fail(GDN_ERR_INVALID, "%s: static scratch too small", what);
+  return launched(gdn::launch_segmented(d, chunk_size, segment_tokens, q, k, v, g, beta, cu_seqlens, state_in, out,
+                                        state_out, scratch, static_cast<hipStream_t>(stream)),
                   what);
 }
 

@@ -62,6 +62,10 @@ hipError_t launch_segmented(const Dims& d, int chunk, int L, const void* q, cons
                             const float* g, const float* beta, const int32_t* cu, const float* s_in, void* out,
                             float* s_out, void* workspace, hipStream_t st);
 
+// Device address and size of the static scratch array on the current device
+// (taken once per device; the array lives in gdn_noalloc.hip).
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 // Grouped expert GEMM: y[r] = W_e x[r] over expert row groups; q4 selects
 // 4-bit group-affine weights rebuilt in the kernel, else bf16 weights.
 hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const int32_t* offsets,

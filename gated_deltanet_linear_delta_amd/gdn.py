@@ -21,7 +21,8 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_ERR_INVALID, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_scan_blockwise", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace",
-           "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_decode_step", "gdn_decode_step_fused",
+           "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_prefill_segmented_noalloc",
+           "gdn_decode_step", "gdn_decode_step_fused",
            "gdn_moe_gemm_q4", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_attention_decode",
            "gdn_attention_decode_workspace", "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string",
            "gdn_last_error")
@@ -83,6 +84,8 @@ def load_library(path: str | None = None):
     lib.gdn_prefill_scan_blockwise.restype = ctypes.c_int
     lib.gdn_prefill_segmented.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, i32, vp, ctypes.c_size_t, vp]
     lib.gdn_prefill_segmented.restype = ctypes.c_int
+    lib.gdn_prefill_segmented_noalloc.argtypes = [shp, vp, vp, vp, f, f, vp, f, vp, f, i32, i32, vp]
+    lib.gdn_prefill_segmented_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_segmented_workspace.argtypes = [shp, i32, i32]
     lib.gdn_prefill_segmented_workspace.restype = ctypes.c_size_t
     lib.gdn_prefill_chunked_workspace.argtypes = [shp, i32]
@@ -281,6 +284,25 @@ def prefill_segmented(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, sta
                                          _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out), int(chunk_size),
                                          int(segment_tokens), ctypes.c_void_p(wp), ctypes.c_size_t(max(wn, 0)),
                                          _stream(stream)))
+        return out, state_out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # GDN_STATIC_SCRATCH_BYTES in include/gdn.h
+
+
+def prefill_segmented_noalloc(q, k, v, g, beta, cu_seqlens, state_in=None, out=None, state_out=None, chunk_size=64,
+                              segment_tokens=2048, stream=None):
+    """gdn_prefill_segmented with the workspace in the library's static
+    device scratch (gdn_prefill_segmented_noalloc): the library allocates
+    nothing; out and state_out are allocated here only when not given.
+    Returns (out, state_out)."""
+    lib = load_library()
+    with _on(stream):
+        shape = _prefill_shape(q, k, v, g, beta, cu_seqlens, state_in)
+        out, state_out = _outputs(shape, q, out, state_out)
+        _check(lib.gdn_prefill_segmented_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                                 _ptr(cu_seqlens), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                                 int(chunk_size), int(segment_tokens), _stream(stream)))
         return out, state_out
 
 

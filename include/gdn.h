@@ -23,7 +23,9 @@
  * Conventions shared by every entry point.
  *  - All tensor pointers are DEVICE pointers allocated and owned by the
  *    caller; the library never allocates or frees device memory and keeps no
- *    pointer after returning.  Layouts are dense row-major, last index
+ *    pointer after returning.  (The one device buffer of its own is the
+ *    static scratch array of gdn_prefill_segmented_noalloc, which comes with
+ *    the library's code on each device.)  Layouts are dense row-major, last index
  *    fastest:
  *        q, k        [T, h_qk, d_k]        io_dtype
  *        v, out      [T, h_v,  d_v]        io_dtype
@@ -172,6 +174,32 @@ gdn_status_t gdn_prefill_segmented(const gdn_shape_t* shape,
                                    void* out, float* state_out,
                                    int32_t chunk_size, int32_t segment_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gdn_prefill_segmented with its workspace taken from a static device array
+ * of GDN_STATIC_SCRATCH_BYTES bytes instead of a caller buffer.  The library
+ * holds that array on every device it runs on until the process ends; the
+ * call allocates nothing.  Arguments, results and errors are those of
+ * gdn_prefill_segmented (the same kernels, so out and state_out are equal to
+ * its results bit for bit), except that a call whose
+ * gdn_prefill_segmented_workspace(shape, chunk_size, segment_tokens) exceeds
+ * GDN_STATIC_SCRATCH_BYTES returns GDN_ERR_INVALID and enqueues nothing (use
+ * fewer segment_tokens: at 32 value heads of 128 x 128, chunk 64, a
+ * 2048-token segment needs about 45 MiB).  All calls on one device share the
+ * array, which keeps whatever the last call left in it: calls that may
+ * overlap on one device (other streams, other threads) race and must be
+ * ordered by the caller.
+ */
+#define GDN_STATIC_SCRATCH_BYTES (64u << 20)
+
+gdn_status_t gdn_prefill_segmented_noalloc(const gdn_shape_t* shape,
+                                           const void* q, const void* k, const void* v,
+                                           const float* g, const float* beta,
+                                           const int32_t* cu_seqlens, const float* state_in,
+                                           void* out, float* state_out,
+                                           int32_t chunk_size, int32_t segment_tokens, void* stream);
 
 /*
  * One recurrent step for each of `batch` sequences (section "Decode: minimize
