@@ -47,6 +47,14 @@ def check_prefill_item(item: dict) -> dict:
     o_ref, s_ref = gated_delta_recurrence(item["q"], item["k"], item["v"], item["g"], item["beta"],
                                           state_in=item.get("state_in"))
     res = {"out": seq_errors(item["o"], o_ref), "state": state_errors(item["s"], s_ref)}
+    if res["out"].tok > 0.1:  # name the wrong tokens and heads, for the failure message
+        o = np.asarray(item["o"], dtype=np.float64)
+        d = np.sqrt(np.sum((o - o_ref) ** 2, axis=2))
+        rn = np.sqrt(np.sum(o_ref ** 2, axis=2))
+        rms = np.sqrt(np.mean(rn ** 2, axis=0))
+        bad = np.argwhere(d > 0.1 * np.maximum(rn, rms[None, :]))
+        res["bad_tokens"] = f"{len(bad)} (token, head) rows, first {bad[:8].tolist()}, tokens {bad[:, 0].min()}..{bad[:, 0].max()}"
+
     dec = item.get("dec")
     if dec is not None:
         S = s_ref

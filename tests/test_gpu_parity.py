@@ -195,7 +195,8 @@ def test_ragged_32_then_decode(kind):
     worst = {key: Errors() for key in ("out", "state", "dec_out", "dec_state")}
     for res in pool_map(check_prefill_item, items()):
         print(f"{kind} {res['tag']}: prefill out {res['out']}; state {res['state']}; "
-              f"decode out {res['dec_out']}; state {res['dec_state']}", flush=True)
+              f"decode out {res['dec_out']}; state {res['dec_state']}"
+              + (f"; wrong: {res['bad_tokens']}" if "bad_tokens" in res else ""), flush=True)
         for key in worst:
             worst[key] = worst[key].merge(res[key])
     print(f"{kind} all 32 sequences: " + "; ".join(f"{key} {e}" for key, e in worst.items()), flush=True)
