@@ -80,6 +80,9 @@ T, HQK, HV, DK, DV, CHUNK = 4096, 16, 32, 128, 128, 64
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_sweep_T4096_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "gated_deltanet_linear_delta_amd", "csrc", "gdn_chunked.hip")
+MFMA_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_T4096_mfma.md")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.md")
+DECODE_SOURCE = os.path.join(ROOT, "gated_deltanet_linear_delta_amd", "csrc", "gdn_decode.hip")
 
 
 def log(msg):
@@ -126,17 +129,45 @@ def source_digest(path):
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the sweep kernel from the committed counter
-    summary, if it was taken on the current kernel source; else None."""
+def profile_fields(path, source):
+    """The machine-readable `- key: value` lines of a committed counter
+    summary, if it was taken on the current source of its kernel; else None."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             fields = dict(line.strip("- \n").split(": ", 1) for line in fh if line.startswith("- ") and ": " in line)
-        if fields.get("source_sha256") != source_digest(KERNEL_SOURCE):
-            return None
-        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return fields if fields.get("source_sha256") == source_digest(source) else None
+    except OSError:
         return None
+
+
+def measured_traffic():
+    """HBM bytes of one chunked-prefill call (prep and sweep launches) from the
+    committed counter summary, if it was taken on the current kernel source;
+    else None."""
+    f = profile_fields(TRAFFIC_FILE, KERNEL_SOURCE)
+    try:
+        return sum(int(f[k]) for k in ("prep_fetch_bytes_per_launch", "prep_write_bytes_per_launch",
+                                       "fetch_bytes_per_launch", "write_bytes_per_launch")) if f else None
+    except (KeyError, ValueError):
+        return None
+
+
+def counter_figures():
+    """Counter-derived figures from the committed rocprofv3 summaries (each
+    None unless taken on the current kernel source): the prefill kernels'
+    MFMA busy fractions and executed bf16 MFMA flops, and the decode step's
+    HBM bytes at B = 1 and B = 32 (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."""
+    out = {}
+    m = profile_fields(MFMA_FILE, KERNEL_SOURCE)
+    for key in ("prep_mfma_busy", "sweep_mfma_busy", "call_mfma_busy"):
+        out[key] = float(m[key]) if m and key in m else None
+    for key in ("prep_bf16_mfma_flops", "sweep_bf16_mfma_flops"):
+        out[key] = int(m[key]) if m and key in m else None
+    d = profile_fields(DECODE_TRAFFIC_FILE, DECODE_SOURCE)
+    for key in ("b1_bytes_per_step", "b32_bytes_per_step"):
+        out["decode_" + key] = int(d[key]) if d and key in d else None
+    out["source"] = "profiles/chunk_prefill_T4096_mfma.md, profiles/decode_step_traffic.md"
+    return out
 
 
 def cpu_model():
@@ -426,9 +457,14 @@ def main():
     per_kernel = mean_by_name(gdn.profile_collect())
     call_ms = sum(m for m, _ in per_kernel.values())
     log("chunked kernels (HIP events): " + ", ".join(f"{n} {m * 1e3:.1f} us" for n, (m, _) in per_kernel.items()))
-    dom = max(per_kernel, key=lambda n: per_kernel[n][0])
-    dom_ms = per_kernel[dom][0]
-    dom_bytes = kernel_bytes(dom, T, 1, False)
+    # The roofline unit is the whole call (prep + sweep, the two launches of one
+    # gdn_prefill_chunked): HIP events around each call leave the launches
+    # back to back, while events between the two kernels add a barrier that
+    # costs the sweep about 5 us (rocprofv3 reads it 10 % below the per-kernel
+    # events above).
+    dom = "chunk_prep+chunk_sweep"
+    dom_ms = call_stats["median_us"] * 1e-3
+    dom_bytes = kernel_bytes("chunk_prep", T, 1, False) + kernel_bytes("chunk_sweep", T, 1, False)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     flops = prefill_flops(T)
     mfma_util = flops / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
@@ -570,8 +606,10 @@ def main():
     log(f"decode B=1 cold: {dec_b1_cold}")
     log(f"decode B=32 cold: {dec_b32}")
     fused_b1 = fused_leg(1, 1, 200, 2001)
+    fused_b1_cold = fused_leg(1, 256, 256, 2001)
     fused_b32 = fused_leg(32, 8, 64, 2004)
     log(f"fused decode B=1: {fused_b1}")
+    log(f"fused decode B=1 cold: {fused_b1_cold}")
     log(f"fused decode B=32 cold: {fused_b32}")
 
     # ------------------------------------------------------------ direct scan
@@ -942,9 +980,12 @@ def main():
         "call_us_events": call_stats,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2)},
+                     "algorithmic_bytes": dom_bytes, "kernel_us": round(dom_ms * 1e3, 2),
+                     "mfma_busy": counter_figures()["call_mfma_busy"]},
+        # from the committed rocprofv3 counter summaries (None when taken on another kernel source)
+        "counters": counter_figures(),
         "decode": {"b1_warm": dec_b1, "b1_cold": dec_b1_cold, "b32_cold": dec_b32},
-        "decode_fused": {"b1_warm": fused_b1, "b32_cold": fused_b32},
+        "decode_fused": {"b1_warm": fused_b1, "b1_cold": fused_b1_cold, "b32_cold": fused_b32},
         "state_residency_ablation": ablation,
         "segmented_prefill": segmented,
         "ragged_prefill": ragged,

@@ -369,12 +369,13 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int C, i
   for (int sl = max(first_slot(eN, N, C), 0) + int(threadIdx.x); sl < max_chunks; sl += 256) tab[sl] = make_int2(0, 0);
 }
 
+// One prep item p = chunk slot * h_v + value head, by the 512 lanes of a
+// workgroup whose LDS is `smem`.
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
-                                                         const IO* __restrict__ k, const float* __restrict__ g,
-                                                         const float* __restrict__ beta, int num_seqs, int T, int num_items,
-                                                         const int2* __restrict__ tab, uint8_t* __restrict__ ws,
-                                                         uint8_t* __restrict__ qf) {
+__device__ __forceinline__ void prep_item(int h_qk, int h_v, const IO* __restrict__ q, const IO* __restrict__ k,
+                                          const float* __restrict__ g, const float* __restrict__ beta, int num_seqs,
+                                          int T, int num_items, const int2* __restrict__ tab, uint8_t* __restrict__ ws,
+                                          uint8_t* __restrict__ qf, const int p, uint8_t* smem) {
   constexpr bool BF = sizeof(IO) == 2;
   using Geo = Geom<BF, DK, C>;
   using Lds = PrepLds<IO, DK, C>;
@@ -388,7 +389,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   constexpr int NGP = (NBLK + GW - 1) / GW;  // Gram blocks per wave
   constexpr int WPK = NW / KB;               // waves per 16-key block of P
   constexpr int NRW = (NB + WPK - 1) / WPK;  // token blocks of P per wave
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   IO* sK = reinterpret_cast<IO*>(smem);
   IO* sQ = sK + Lds::CP * KP;
   float* sA = reinterpret_cast<float*>(smem + Lds::A_OFF);  // after the Gram products
@@ -402,11 +402,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   float* sBeta = reinterpret_cast<float*>(smem + Lds::B_OFF);
   float* sDec = reinterpret_cast<float*>(smem + Lds::D_OFF);
 
-  // items p = chunk * h_v + value head, the items of XCD x (workgroups i
-  // with i % 8 == x) contiguous: value heads of one query/key head run on one
-  // XCD back to back and share its L2 for their K and Q tiles
-  const int per = int(gridDim.x) >> 3;
-  const int p = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
   if (p >= num_items) return;
   const int gc = p / h_v, h = p % h_v;
   const int2 ch = num_seqs == 1 ? make_int2(gc * C, min(C, T - gc * C)) : tab[gc];
@@ -762,11 +757,27 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   }
 }
 
+// items p = chunk * h_v + value head, the items of XCD x (workgroups i with
+// i % 8 == x) contiguous: value heads of one query/key head run on one XCD
+// back to back and share its L2 for their K and Q tiles
+template <typename IO, int DK, int C>
+__global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, const IO* __restrict__ q,
+                                                         const IO* __restrict__ k, const float* __restrict__ g,
+                                                         const float* __restrict__ beta, int num_seqs, int T,
+                                                         int num_items, const int2* __restrict__ tab,
+                                                         uint8_t* __restrict__ ws, uint8_t* __restrict__ qf) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int per = int(gridDim.x) >> 3;
+  const int p = int(blockIdx.x & 7) * per + int(blockIdx.x >> 3);
+  prep_item<IO, DK, C>(h_qk, h_v, q, k, g, beta, num_seqs, T, num_items, tab, ws, qf, p, smem);
+}
+
 template <typename IO, int DK, int C>
 __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
                                                           const uint8_t* __restrict__ ws, const uint8_t* __restrict__ qf,
-                                                          const float* s_in, IO* __restrict__ out, float* s_out) {
+                                                          const float* s_in, IO* __restrict__ out, float* s_out,
+                                                          int pfd) {
   constexpr bool BF = sizeof(IO) == 2;
   using Geo = Geom<BF, DK, C>;
   using Lds = SweepLds<IO, DK, C>;
@@ -794,7 +805,8 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
   const int i_x = int(blockIdx.x >> 3);
   const int unit = int(blockIdx.x & 7) + 8 * (i_x / U);
   if (unit >= N * h_qk) return;
-  const int L = unit * U + i_x % U;
+  const int uidx = i_x % U;  // chain index within the unit
+  const int L = unit * U + uidx;
   const int tl = L % ntile, nh = L / ntile, h = nh % h_v, n = nh / h_v;
   const int j = h / (h_v / h_qk);
   const int dv0 = 16 * tl;
@@ -966,6 +978,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     // of one output row and stores them at once.  Q and R fragments are
     // loaded two chunks ahead into registers.
     const int ht = tid - 256;  // 0..255
+    float pf_sink = 0.f;        // keeps the prefetch loads alive
     constexpr int NVP = int(Lds::VBUF / 16);      // 16-byte pieces of a chunk's V slice
     constexpr int NSP = int(Lds::SCBUF / 16);      // and of its scalars
     constexpr int NST = (NVP + NSP + 255) / 256;   // pieces per helper lane
@@ -1032,10 +1045,39 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       // aq, rf: fragments of chunk cc; stg: staged chunk cc+2.  rn and sn,
       // the other sets, are loaded here with R of chunk cc+1 and the staged
       // pieces of chunk cc+3, in the first window, where these waves wait.
+      // L2 prefetch of chunk cc, pfd chunks ahead (pfd past the last chunk: no
+      // prefetch, for operands and V small enough to stay in the memory-side
+      // cache between the prep and this launch): each chain touches one dword of its share of the 128-byte
+      // lines (the unit's chains share the K and Q sets, a value head's slices
+      // its per-chunk block and V rows), so the loads of a few steps later
+      // find them in the XCD's L2 instead of waiting for HBM.
+      auto prefetch = [&](int cc) __attribute__((always_inline)) -> float {
+        constexpr int LN = 128;
+        constexpr int NQK = int(QKF / LN), NWS = int(Geo::BYTES / LN);
+        const int vrow_lines = (d_v * ESZ + LN - 1) / LN;
+        const int nv = (chunk_nc(cc) * vrow_lines - tl + ntile - 1) / ntile;
+        const int nqk = (NQK - uidx + U - 1) / U, nws = (NWS - tl + ntile - 1) / ntile;
+        int m = ht;
+        const uint8_t* a = nullptr;
+        if (m < nv) {
+          const int ln = tl + ntile * m;
+          a = reinterpret_cast<const uint8_t*>(v + (size_t(chunk_t0(cc) + ln / vrow_lines) * h_v + h) * d_v) +
+              size_t(ln % vrow_lines) * LN;
+        } else if ((m -= nv) < nqk) {
+          a = qfb(cc) + size_t(uidx + U * m) * LN;
+        } else if ((m -= nqk) < nws) {
+          a = wsb(cc) + size_t(tl + ntile * m) * LN;
+        }
+        return a ? *reinterpret_cast<const float*>(a) : 0.f;
+      };
+      float pf_prev = 0.f;
+
       auto step = [&](int cc, E (&aq)[NKS], Sp (&rf)[NRA], Sp (&rn)[NRA], u32x4 (&stg)[NST],
                       u32x4 (&sn)[NST]) __attribute__((always_inline)) {
         const int nc = chunk_nc(cc);
         const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF);
+        pf_sink += pf_prev;  // consume the previous step's prefetch (issued a whole step ago)
+        pf_prev = cc + pfd < nchunk ? prefetch(cc + pfd) : 0.f;
 
         // (1) Z^T = S Q^T for token block r (S is the chunk's initial state)
         E bs[NKS];
@@ -1089,6 +1131,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
     if (!rowblk) run(std::integral_constant<int, 0>());
     else if (NTF == 1 || r < 2) run(std::integral_constant<int, 1>());
     else run(std::integral_constant<int, NTF>());
+    if (T < 0) s_out[tid] = pf_sink;  // never true (T >= 0): the sink only has to look used
   }
 }
 
@@ -1111,10 +1154,13 @@ static size_t blocks_bytes(const Dims& d, int chunk) {
   return chunked_max_chunks(d, chunk) * size_t(d.h_v) * chunk_bytes(d, chunk);
 }
 
+static size_t qf_bytes(const Dims& d, int chunk) {
+  return chunked_max_chunks(d, chunk) * size_t(d.h_qk) * qk_frag_bytes(d.d_k, chunk, d.bf16);
+}
+
 size_t chunked_workspace_bytes(const Dims& d, int chunk) {
   if (chunk_bytes(d, chunk) == 0) return 0;
-  return table_bytes(d, chunk) + blocks_bytes(d, chunk) +
-         chunked_max_chunks(d, chunk) * size_t(d.h_qk) * qk_frag_bytes(d.d_k, chunk, d.bf16);
+  return table_bytes(d, chunk) + blocks_bytes(d, chunk) + qf_bytes(d, chunk);
 }
 
 template <typename IO, int DK, int C>
@@ -1159,10 +1205,14 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
+  // Prefetch six chunks ahead when the operands and V (per launch) exceed
+  // what the 256 MiB memory-side cache keeps between the two launches.
+  const size_t v_bytes = size_t(d.total_tokens) * d.h_v * d.d_v * (d.bf16 ? 2 : 4);
+  const int pfd = blocks_bytes(d, C) + qf_bytes(d, C) + v_bytes > (size_t(192) << 20) ? 6 : (1 << 30);
   Prof prof("chunk_sweep", st);
   hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
                      d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(v), cu, ws, qf,
-                     s_in, static_cast<IO*>(out), s_out);
+                     s_in, static_cast<IO*>(out), s_out, pfd);
   return hipGetLastError();
 }
 

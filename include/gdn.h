@@ -120,7 +120,7 @@ gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape,
 /*
  * Bytes of device workspace gdn_prefill_chunked needs for this shape and
  * chunk size (0 if the shape or chunk size is invalid).  The bound depends
- * only on num_seqs, total_tokens, h_v and chunk_size.
+ * on num_seqs, total_tokens, h_qk, h_v, d_k, io_dtype and chunk_size.
  */
 size_t gdn_prefill_chunked_workspace(const gdn_shape_t* shape, int32_t chunk_size);
 
