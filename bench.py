@@ -252,13 +252,13 @@ def cpu_baseline_leg(log_fn):
         "prefill_4096": ("prefill", make_prefill([4096], HQK, HV, DK, DV, "bf16", 2.0, None,
                                                  rng=np.random.default_rng(1002)), [0],
                          "all 4096 tokens, 32 value heads"),
-        "prefill_131072": ("prefill", make_prefill([8192], HQK, HV, DK, DV, "bf16", 2.0, None,
+        "prefill_131072": ("prefill", make_prefill([32768], HQK, HV, DK, DV, "bf16", 2.0, None,
                                                    rng=np.random.default_rng(1003)), [0],
-                           "the first 8192 tokens (same distributions), 32 value heads"),
-        "ragged_32_then_decode": ("prefill", make_prefill(lens4[:4], HQK, HV, DK, DV, "bf16", 2.0, 0.02,
-                                                          rng=np.random.default_rng(1004)), [0, 1, 2, 3],
-                                  f"prefill of 4 of the 32 sequences ({int(sum(lens4[:4]))} tokens, "
-                                  "the workload's first four lengths), 32 value heads"),
+                           "the first 32768 tokens (same distributions), 32 value heads"),
+        "ragged_32_then_decode": ("prefill", make_prefill(lens4[:16], HQK, HV, DK, DV, "bf16", 2.0, 0.02,
+                                                          rng=np.random.default_rng(1004)), list(range(16)),
+                                  f"prefill of 16 of the 32 sequences ({int(sum(lens4[:16]))} tokens, "
+                                  "the workload's first sixteen lengths), 32 value heads"),
     }
     per = {}
     ctx = mp.get_context("spawn")
