@@ -772,7 +772,15 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(int h_qk, int h_v, cons
   prep_item<IO, DK, C>(h_qk, h_v, q, k, g, beta, num_seqs, T, num_items, tab, ws, qf, p, smem);
 }
 
-template <typename IO, int DK, int C>
+// LATE_P: the chain waves load the next chunk's P after their products with
+// Y (second window) instead of with their LDS reads (first window).  That
+// evens out the vector-memory instructions issued per window (32 and 32 per
+// compute unit instead of 48 and 16), which shortens the first window, whose
+// loads queue behind each other, when the operands come from the memory-side
+// cache (about 4 % faster sweep at 4096 tokens); with operands from HBM the later
+// issue leaves too little time to cover the latency, so large working sets
+// keep the early issue.
+template <typename IO, int DK, int C, bool LATE_P>
 __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk, int h_v, int d_v, int max_chunks,
                                                           const IO* __restrict__ v, const int32_t* __restrict__ cu,
                                                           const uint8_t* __restrict__ ws, const uint8_t* __restrict__ qf,
@@ -893,8 +901,8 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
           vt = lds_tr16(sV + (16 * r + 4 * grp + col / 4) * 16 + 4 * (col % 4));
         }
       }
-      fetch_p(pn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
-      __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the products
+      if constexpr (!LATE_P) fetch_p(pn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
       if (rowblk) {
         f4 x = zero4(), x1 = zero4();
 #pragma unroll
@@ -939,6 +947,11 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
 #pragma unroll
         for (int bi = 0; bi < SB; ++bi)
           if (r + 4 * bi < KB) mm_es(pf[bi][s], yb[s], ah[bi], al[bi]);
+      if constexpr (LATE_P) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_p(pn, min(cc + 1, nchunk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int bi = 0; bi < SB; ++bi) {
         const int b = r + 4 * bi;
@@ -1201,18 +1214,26 @@ static hipError_t launch_chunked_t(const Dims& d, const void* q, const void* k, 
   const int per = (units + 7) / 8 * U;
   constexpr size_t lds = SweepLds<IO, DK, C>::BYTES;
   if (lds > 65536) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_sweep_kernel<IO, DK, C>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
+    for (const void* f : {reinterpret_cast<const void*>(&chunk_sweep_kernel<IO, DK, C, false>),
+                          reinterpret_cast<const void*>(&chunk_sweep_kernel<IO, DK, C, true>)}) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      if (e != hipSuccess) return e;
+    }
   }
   // Prefetch six chunks ahead when the operands and V (per launch) exceed
   // what the 256 MiB memory-side cache keeps between the two launches.
   const size_t v_bytes = size_t(d.total_tokens) * d.h_v * d.d_v * (d.bf16 ? 2 : 4);
-  const int pfd = blocks_bytes(d, C) + qf_bytes(d, C) + v_bytes > (size_t(192) << 20) ? 6 : (1 << 30);
+  const bool large = blocks_bytes(d, C) + qf_bytes(d, C) + v_bytes > (size_t(192) << 20);
+  const int pfd = large ? 6 : (1 << 30);
   Prof prof("chunk_sweep", st);
-  hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
-                     d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(v), cu, ws, qf,
-                     s_in, static_cast<IO*>(out), s_out, pfd);
+  if (large)
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C, false>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
+                       d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(v), cu, ws, qf,
+                       s_in, static_cast<IO*>(out), s_out, pfd);
+  else
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, DK, C, true>), dim3(8 * per), dim3(512), lds, st, d.num_seqs,
+                       d.total_tokens, d.h_qk, d.h_v, d.d_v, int(max_chunks), static_cast<const IO*>(v), cu, ws, qf,
+                       s_in, static_cast<IO*>(out), s_out, pfd);
   return hipGetLastError();
 }
 
