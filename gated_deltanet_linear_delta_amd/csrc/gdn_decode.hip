@@ -166,9 +166,14 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus; log1p(e^x) = x to fp32 precision past 20
   const float alpha = expf(-(fa.gate_scale ? fa.gate_scale[h] : 1.f) * sp);
   const float bt = 1.f / (1.f + expf(-b_raw[bh]));
-  float vi[RPL];
+  // v and the norm weight of the lane's rows with the other inputs, so that
+  // no load waits at the end of the step
+  float vi[RPL], nw[RPL];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) vi[r] = io_traits<IO>::load(v + size_t(bh) * d_v + row[r]);
+  for (int r = 0; r < RPL; ++r) {
+    vi[r] = io_traits<IO>::load(v + size_t(bh) * d_v + row[r]);
+    nw[r] = fa.norm_w ? fa.norm_w[row[r]] : 1.f;
+  }
 
   float kk0 = 0.f, kk1 = 0.f, qq0 = 0.f, qq1 = 0.f, kq0 = 0.f, kq1 = 0.f;
 #pragma unroll
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   if (act && l == 0) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      io_traits<IO>::store(out + size_t(bh) * d_v + row[r], o[r] * scale * (fa.norm_w ? fa.norm_w[row[r]] : 1.f));
+      io_traits<IO>::store(out + size_t(bh) * d_v + row[r], o[r] * scale * nw[r]);
   }
 }
 
