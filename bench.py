@@ -952,6 +952,45 @@ def main():
         torch.cuda.empty_cache()
         log(f"segmented long prompt: {segmented}")
 
+    # ------------------------------------------------------------ measured roofs
+    # The box's practical roofs beside the data-sheet peaks: a 1 GiB device
+    # copy (read and written once) and a bf16 8192^3 GEMM through torch.mm
+    # (the vendor library), each the median of 20 event-timed runs after 5
+    # untimed ones.
+    def measured_roofs():
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+
+        def median_s(fn):
+            for _ in range(5):
+                fn()
+            for e0, e1 in ev:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        copy_gbs = 2 * src.numel() * 4 / median_s(lambda: dst.copy_(src)) / 1e9
+        del src, dst
+        n = 8192
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        gemm_tflops = 2 * n ** 3 / median_s(lambda: torch.mm(a, b, out=c)) / 1e12
+        del a, b, c
+        torch.cuda.empty_cache()
+        return {"copy_gbs": round(copy_gbs, 1), "gemm_bf16_tflops": round(gemm_tflops, 1),
+                "prefill_hbm_frac_of_copy": round(achieved / copy_gbs, 4),
+                "prefill_mfma_frac_of_gemm": round(flops / (ms_step * 1e-3) / (gemm_tflops * 1e12), 4),
+                "decode_b32_frac_of_copy": round(dec_b32["hbm_gbs"] / copy_gbs, 4),
+                "method": "1 GiB fp32 device-to-device copy (torch copy_, the runtime's copy kernel) and bf16 "
+                          "8192^3 torch.mm, medians of 20 HIP-event-timed runs"}
+
+    roofs = measured_roofs()
+    log(f"measured roofs: {roofs}")
+
     # ------------------------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -984,6 +1023,7 @@ def main():
                      "mfma_busy": counter_figures()["call_mfma_busy"]},
         # from the committed rocprofv3 counter summaries (None when taken on another kernel source)
         "counters": counter_figures(),
+        "measured_roofs": roofs,
         "decode": {"b1_warm": dec_b1, "b1_cold": dec_b1_cold, "b32_cold": dec_b32},
         "decode_fused": {"b1_warm": fused_b1, "b1_cold": fused_b1_cold, "b32_cold": fused_b32},
         "state_residency_ablation": ablation,
