@@ -602,9 +602,11 @@ def main():
     dec_b1 = decode_leg(1, 1, 200, 1001)
     dec_b1_cold = decode_leg(1, 256, 256, 1001)
     dec_b32 = decode_leg(32, 8, 64, 1004)
+    dec_b32_warm = decode_leg(32, 1, 64, 1004)  # one 64 MiB state set: it stays in the Infinity Cache
     log(f"decode B=1: {dec_b1}")
     log(f"decode B=1 cold: {dec_b1_cold}")
     log(f"decode B=32 cold: {dec_b32}")
+    log(f"decode B=32 warm: {dec_b32_warm}")
     fused_b1 = fused_leg(1, 1, 200, 2001)
     fused_b1_cold = fused_leg(1, 256, 256, 2001)
     fused_b32 = fused_leg(32, 8, 64, 2004)
@@ -1024,7 +1026,7 @@ def main():
         # from the committed rocprofv3 counter summaries (None when taken on another kernel source)
         "counters": counter_figures(),
         "measured_roofs": roofs,
-        "decode": {"b1_warm": dec_b1, "b1_cold": dec_b1_cold, "b32_cold": dec_b32},
+        "decode": {"b1_warm": dec_b1, "b1_cold": dec_b1_cold, "b32_cold": dec_b32, "b32_warm": dec_b32_warm},
         "decode_fused": {"b1_warm": fused_b1, "b1_cold": fused_b1_cold, "b32_cold": fused_b32},
         "state_residency_ablation": ablation,
         "segmented_prefill": segmented,
