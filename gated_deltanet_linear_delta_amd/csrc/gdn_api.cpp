@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -37,12 +38,23 @@ gdn_status_t ok() {
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// The int32 an enum object of the ABI holds.  A C caller may store any int
+// there, and reading a value outside the enumerators through the C++ enum
+// type is undefined, so the bytes are copied instead.
+template <typename E>
+int32_t enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "the ABI's enums are int-sized");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape checks shared by all entry points.  Sizes are bounded so that every
 // element index of the largest tensor fits in int32 arithmetic on the
 // (sequence, head, row) granularity the kernels use.
-gdn_status_t check_dims(int n, int t, int h_qk, int h_v, int d_k, int d_v, gdn_dtype_t io, const char* what) {
+gdn_status_t check_dims(int n, int t, int h_qk, int h_v, int d_k, int d_v, int32_t io, const char* what) {
   if (n < 1) return fail(GDN_ERR_INVALID, "%s: num_seqs/batch must be >= 1 (got %d)", what, n);
   if (t < 0) return fail(GDN_ERR_INVALID, "%s: total_tokens must be >= 0 (got %d)", what, t);
   if (h_qk < 1 || h_v < 1 || h_v % h_qk != 0)
@@ -72,14 +84,16 @@ gdn_status_t launched(hipError_t e, const char* what) {
 }
 
 gdn::Dims dims_of(const gdn_shape_t* s) {
-  return gdn::Dims{s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, s->io_dtype == GDN_DTYPE_BF16};
+  return gdn::Dims{s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v,
+                   enum_bits(s->io_dtype) == GDN_DTYPE_BF16};
 }
 
 gdn_status_t check_prefill(const gdn_shape_t* s, const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const int32_t* cu, const float* state_in, const void* out,
                            const float* state_out, const char* what) {
   if (!s) return fail(GDN_ERR_INVALID, "%s: shape is NULL", what);
-  gdn_status_t st = check_dims(s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, s->io_dtype, what);
+  gdn_status_t st =
+      check_dims(s->num_seqs, s->total_tokens, s->h_qk, s->h_v, s->d_k, s->d_v, enum_bits(s->io_dtype), what);
   if (st != GDN_OK) return st;
   // with no tokens the per-token tensors are never read or written and may be NULL
   if (s->total_tokens > 0) {
@@ -165,7 +179,7 @@ int gdn_profile_collect(const char** names, float* ms, int cap) {
 
 
 const char* gdn_status_string(gdn_status_t status) {
-  switch (status) {
+  switch (enum_bits(status)) {
     case GDN_OK: return "GDN_OK";
     case GDN_ERR_INVALID: return "GDN_ERR_INVALID";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
@@ -204,7 +218,7 @@ gdn_status_t gdn_prefill_scan_blockwise(const gdn_shape_t* shape, const void* q,
 size_t gdn_prefill_chunked_workspace(const gdn_shape_t* shape, int32_t chunk_size) {
   if (!shape || (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)) return 0;
   if (check_dims(shape->num_seqs, shape->total_tokens, shape->h_qk, shape->h_v, shape->d_k, shape->d_v,
-                 shape->io_dtype, "gdn_prefill_chunked_workspace") != GDN_OK)
+                 enum_bits(shape->io_dtype), "gdn_prefill_chunked_workspace") != GDN_OK)
     return 0;
   return gdn::chunked_workspace_bytes(dims_of(shape), chunk_size);
 }
@@ -237,7 +251,7 @@ size_t gdn_prefill_segmented_workspace(const gdn_shape_t* shape, int32_t chunk_s
   if (!shape || (chunk_size != 0 && chunk_size != 16 && chunk_size != 32 && chunk_size != 64)) return 0;
   if (segment_tokens < 1 || (chunk_size > 0 && segment_tokens % chunk_size != 0)) return 0;
   if (check_dims(shape->num_seqs, shape->total_tokens, shape->h_qk, shape->h_v, shape->d_k, shape->d_v,
-                 shape->io_dtype, "gdn_prefill_segmented_workspace") != GDN_OK)
+                 enum_bits(shape->io_dtype), "gdn_prefill_segmented_workspace") != GDN_OK)
     return 0;
   return gdn::segmented_workspace_bytes(dims_of(shape), chunk_size, segment_tokens);
 }
@@ -317,14 +331,14 @@ gdn_status_t gdn_decode_step(int32_t batch, int32_t h_qk, int32_t h_v, int32_t d
                              const float* beta, const float* state_in, void* out, float* state_out,
                              void* stream) {
   const char* what = "gdn_decode_step";
-  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, io_dtype, what);
+  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, enum_bits(io_dtype), what);
   if (st != GDN_OK) return st;
   st = check_ptrs(what, {{"q", q}, {"k", k}, {"v", v}, {"g", g}, {"beta", beta}, {"state_in", state_in},
                          {"out", out}, {"state_out", state_out}});
   if (st != GDN_OK) return st;
   if (out == q || out == k || out == v || out == state_in || out == state_out)
     return fail(GDN_ERR_INVALID, "%s: out aliases another tensor", what);
-  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, io_dtype == GDN_DTYPE_BF16};
+  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, enum_bits(io_dtype) == GDN_DTYPE_BF16};
   return launched(gdn::launch_decode(d, q, k, v, g, beta, state_in, out, state_out,
                                      static_cast<hipStream_t>(stream)),
                   what);
@@ -336,7 +350,7 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
                                    const gdn_decode_fused_params_t* params, const float* state_in, void* out,
                                    float* state_out, void* stream) {
   const char* what = "gdn_decode_step_fused";
-  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, io_dtype, what);
+  gdn_status_t st = check_dims(batch, batch, h_qk, h_v, d_k, d_v, enum_bits(io_dtype), what);
   if (st != GDN_OK) return st;
   st = check_ptrs(what, {{"q_raw", q_raw}, {"k_raw", k_raw}, {"v", v}, {"g_raw", g_raw}, {"beta_raw", beta_raw},
                          {"state_in", state_in}, {"out", out}, {"state_out", state_out}});
@@ -351,7 +365,7 @@ gdn_status_t gdn_decode_step_fused(int32_t batch, int32_t h_qk, int32_t h_v, int
       return fail(GDN_ERR_INVALID, "%s: gate_bias, gate_scale and norm_weight must be 4-byte aligned", what);
   if (!(p.qk_eps >= 0.f && p.qk_eps <= 3.0e38f) || !(p.norm_eps >= 0.f && p.norm_eps <= 3.0e38f))
     return fail(GDN_ERR_INVALID, "%s: qk_eps and norm_eps must be finite and >= 0", what);
-  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, io_dtype == GDN_DTYPE_BF16};
+  const gdn::Dims d{batch, batch, h_qk, h_v, d_k, d_v, enum_bits(io_dtype) == GDN_DTYPE_BF16};
   return launched(gdn::launch_decode_fused(d, q_raw, k_raw, v, g_raw, beta_raw, p.gate_bias, p.gate_scale,
                                            p.norm_weight, p.qk_eps, p.norm_eps, state_in, out, state_out,
                                            static_cast<hipStream_t>(stream)),
