@@ -74,6 +74,11 @@ __device__ __forceinline__ void mm_es(uint4 a, const sp8& b, f4& ch, f4& cl) {
   cl = mma32(a, b.lo, cl);
 }
 __device__ __forceinline__ void mm_es(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
+__device__ __forceinline__ void mm_se(const sp8& a, uint4 b, f4& ch, f4& cl) {
+  ch = mma32(a.hi, b, ch);
+  cl = mma32(a.lo, b, cl);
+}
+__device__ __forceinline__ void mm_se(const f8& a, const f8& b, f4& ch, f4&) { ch = mma32(a, b, ch); }
 __device__ __forceinline__ void mm_ss(const sp8& a, const sp8& b, f4& ch, f4& cl) {
   ch = mma32(a.hi, b.hi, ch);
   cl = mma32(a.hi, b.lo, cl);
@@ -127,8 +132,8 @@ constexpr int frag_row_stride(int row_bytes) { return (row_bytes + 95) / 128 * 1
 
 // Exchange buffers: [16 rows][K + pad] arrays with K contiguous, written from
 // D blocks (4 consecutive k per lane) and read as B fragments (8 consecutive
-// k per lane).  bf16 buffers hold either the rounded value (single) or the
-// hi and lo halves in two planes; fp32 buffers hold the value.
+// k per lane).  bf16 buffers hold the hi and lo halves in two planes; fp32
+// buffers hold the value.
 template <bool BF, int K>
 struct XBuf {
   using El = std::conditional_t<BF, uint16_t, float>;
@@ -136,12 +141,6 @@ struct XBuf {
   static constexpr size_t PLANE = 16 * LD * sizeof(El);
 };
 
-template <bool BF, int K>
-__device__ __forceinline__ void xb_write_single(uint8_t* buf, int n, int k0, f4 v) {
-  using X = XBuf<BF, K>;
-  if constexpr (BF) *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(buf) + n * X::LD + k0) = bf16x4(v);
-  else *reinterpret_cast<f4*>(reinterpret_cast<float*>(buf) + n * X::LD + k0) = v;
-}
 template <bool BF, int K>
 __device__ __forceinline__ void xb_write_split(uint8_t* buf, int n, int k0, f4 v) {
   using X = XBuf<BF, K>;
@@ -153,11 +152,6 @@ __device__ __forceinline__ void xb_write_split(uint8_t* buf, int n, int k0, f4 v
   } else {
     *reinterpret_cast<f4*>(reinterpret_cast<float*>(buf) + n * X::LD + k0) = v;
   }
-}
-template <bool BF, int K>
-__device__ __forceinline__ void xb_read_single(typename Types<BF>::E& d, const uint8_t* buf, int n, int k0) {
-  using X = XBuf<BF, K>;
-  ld8(d, reinterpret_cast<const typename X::El*>(buf) + n * X::LD + k0);
 }
 template <bool BF, int K>
 __device__ __forceinline__ void xb_read_split(typename Types<BF>::S& d, const uint8_t* buf, int n, int k0) {
@@ -297,11 +291,11 @@ struct SweepLds {
   static constexpr int DKP = dk_pad(DK);  // key columns of the state buffer
   static constexpr size_t VBUF = size_t(C) * 16 * ESZ;    // V slice: C tokens x 16 values
   static constexpr size_t SCBUF = 3 * C * sizeof(float);  // beta, beta gamma, gamma
-  // S (B fragments of S^T) and Y have one buffer each.  The V slice and the
+  // S (B fragments of S^T, split: hi and lo planes) and Y have one buffer each.  The V slice and the
   // scalars are written two chunks ahead: V has two buffers (chunk parity),
   // the scalars, read until the end of a step, four.
   static constexpr size_t S_OFF = 0;
-  static constexpr size_t Y_OFF = S_OFF + XBuf<BF, DKP>::PLANE;
+  static constexpr size_t Y_OFF = S_OFF + xb_bytes_split<BF, DKP>();
   static constexpr size_t V_OFF = Y_OFF + xb_bytes_split<BF, CP>();
   static constexpr size_t SC_OFF = V_OFF + 2 * VBUF;
   static constexpr size_t BYTES = SC_OFF + 4 * SCBUF;
@@ -858,7 +852,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       st[bi] = zero4();
       if (b < KB) {
         if (s_in) st[bi] = *reinterpret_cast<const f4*>(s_in + (size_t(nh) * d_v + dv0 + col) * DK + 16 * b + 4 * grp);
-        xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
+        xb_write_split<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
       }
     }
     auto fetch_p = [&](E (&pf)[SB][NTS], int cc) __attribute__((always_inline)) {
@@ -886,13 +880,14 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       const int nc = chunk_nc(cc);
       const float* sSc = reinterpret_cast<const float*>(smem + Lds::SC_OFF + (cc & 3) * Lds::SCBUF);
 
-      // (1) X = K S^T for token block r; Y = beta V - beta gamma X
-      E bs[NKS];
+      // (1) X = K S^T for token block r (S split: the rounding of the state
+      // would otherwise enter every later chunk); Y = beta V - beta gamma X
+      Sp bs[NKS];
       uint2 vt;
       f4 bt, bg;
       if (rowblk) {
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) xb_read_single<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
+        for (int s = 0; s < NKS; ++s) xb_read_split<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
         bt = *reinterpret_cast<const f4*>(sSc + 16 * r + 4 * grp);
         bg = *reinterpret_cast<const f4*>(sSc + C + 16 * r + 4 * grp);
         if constexpr (BF) {
@@ -904,13 +899,13 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
       if constexpr (!LATE_P) fetch_p(pn, min(cc + 1, nchunk - 1));  // past the end: harmless refetch
       __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
       if (rowblk) {
-        f4 x = zero4(), x1 = zero4();
+        f4 x = zero4(), x1 = zero4(), xl = zero4(), xl1 = zero4();
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-          if (s & 1) x1 = mma32(kf[s], bs[s], x1);
-          else x = mma32(kf[s], bs[s], x);
+          if (s & 1) mm_es(kf[s], bs[s], x1, xl1);
+          else mm_es(kf[s], bs[s], x, xl);
         }
-        x = x + x1;
+        x = (x + x1) + (xl + xl1);
         float vv[4];
         if constexpr (BF) {
           vv[0] = __uint_as_float(vt.x << 16), vv[1] = __uint_as_float(vt.x & 0xffff0000u);
@@ -957,7 +952,7 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         const int b = r + 4 * bi;
         if (b < KB) {
           st[bi] = ah[bi] + al[bi];
-          xb_write_single<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
+          xb_write_split<BF, DKP>(sS, col, 16 * b + 4 * grp, st[bi]);
         }
       }
       lds_barrier();
@@ -1092,24 +1087,25 @@ __global__ __launch_bounds__(512) void chunk_sweep_kernel(int N, int T, int h_qk
         pf_sink += pf_prev;  // consume the previous step's prefetch (issued a whole step ago)
         pf_prev = cc + pfd < nchunk ? prefetch(cc + pfd) : 0.f;
 
-        // (1) Z^T = S Q^T for token block r (S is the chunk's initial state)
-        E bs[NKS];
+        // (1) Z^T = S Q^T for token block r (S is the chunk's initial state,
+        // split: with slow decay S Q^T carries most of the output)
+        Sp bs[NKS];
         if constexpr (NR > 0) {
 #pragma unroll
-          for (int s = 0; s < NKS; ++s) xb_read_single<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
+          for (int s = 0; s < NKS; ++s) xb_read_split<BF, DKP>(bs[s], sS, col, 32 * s + 8 * grp);
           fetch_r(rn, min(cc + 1, nchunk - 1));
         }
         fetch_stg(sn, min(cc + 3, nchunk - 1));
         __builtin_amdgcn_sched_barrier(0);
         f4 z = zero4();
         if constexpr (NR > 0) {
-          f4 z1 = zero4();
+          f4 z1 = zero4(), zl = zero4(), zl1 = zero4();
 #pragma unroll
           for (int s = 0; s < NKS; ++s) {
-            if (s & 1) z1 = mma32(bs[s], aq[s], z1);
-            else z = mma32(bs[s], aq[s], z);
+            if (s & 1) mm_se(bs[s], aq[s], z1, zl1);
+            else mm_se(bs[s], aq[s], z, zl);
           }
-          z = z + z1;
+          z = (z + z1) + (zl + zl1);
           fetch_rows(aq, qfb(min(cc + 2, nchunk - 1)));
         }
         lds_barrier();

@@ -1,0 +1,88 @@
+"""GPU parity of the prefill kernels on harder input distributions than the
+configurations', at 4096 tokens (one sequence, 16 query/key and 32 value
+heads, d = 128, bf16), against the fp64 oracle on every head:
+
+* slow decay: g = -softplus(N - 8), about -3e-4 per token, so the state
+  keeps almost everything over the whole prompt;
+* fast decay: g = -softplus(N + 3), about -3 per token;
+* beta at its extremes: 0.001 or 0.999 per (token, head);
+* correlated keys: each head's keys are one direction plus 5 % noise, so
+  k_i . k_j is near 1 and the chunk form's triangular inverse is far from
+  the identity (with beta 0.999 and slow decay in the harshest case);
+* a large initial state (standard deviation 1).
+
+The inputs are the generator's, transformed here before rounding to bf16;
+the oracle sees the same rounded values.  The bars are the suite's (relative
+Frobenius 3e-3 per slice, max norm and per token 1e-2, final state alike).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_delta_amd import gdn
+from gated_deltanet_linear_delta_amd.workloads import make_prefill
+
+from helpers import Errors, dev_prefill
+from oracle_pool import check_prefill_item, pool_map
+
+pytestmark = pytest.mark.gpu
+
+T, HQK, HV, D = 4096, 16, 32, 128
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def inputs(case):
+    seed = {"slow_decay": 71, "fast_decay": 72, "beta_extremes": 73, "correlated_keys": 74,
+            "correlated_keys_beta1": 75, "large_state": 76}[case]
+    shift = {"slow_decay": -8.0, "fast_decay": 3.0, "correlated_keys_beta1": -8.0}.get(case, 2.0)
+    inp = make_prefill([T], HQK, HV, D, D, "bf16", shift, 1.0 if case == "large_state" else None, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    if case == "beta_extremes":
+        inp.beta[...] = np.where(rng.random(inp.beta.shape) < 0.5, 0.001, 0.999).astype(np.float32)
+    if case.startswith("correlated_keys"):
+        base = rng.standard_normal((1, HQK, D))
+        inp.k[...] = _bf16(_unit(_unit(base) + 0.05 * rng.standard_normal((T, HQK, D)) / np.sqrt(D)))
+        if case == "correlated_keys_beta1":
+            inp.beta[...] = np.float32(0.999)
+    return inp
+
+
+CASES = ["slow_decay", "fast_decay", "beta_extremes", "correlated_keys", "correlated_keys_beta1", "large_state"]
+
+
+@pytest.mark.parametrize("kind", ["chunked", "scan"])
+@pytest.mark.parametrize("case", CASES)
+def test_prefill_harder_inputs(case, kind):
+    inp = inputs(case)
+    d = dev_prefill(inp)
+    if kind == "chunked":
+        o, s = gdn.prefill_chunked(**d, chunk_size=64)
+    else:
+        o, s = gdn.prefill_scan(**d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    o_h, s_h = o.float().cpu().numpy(), s.cpu().numpy()
+    G = HV // HQK
+    f = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+
+    def items():
+        for j in range(HQK):
+            hs = slice(G * j, G * j + G)
+            yield {"q": f(inp.q[:, j:j + 1]), "k": f(inp.k[:, j:j + 1]), "v": f(inp.v[:, hs]),
+                   "g": f(inp.g[:, hs]), "beta": f(inp.beta[:, hs]), "o": f(o_h[:, hs]), "s": f(s_h[:, hs]),
+                   "state_in": None if inp.state_in is None else f(inp.state_in[:, hs]), "tag": f"heads {hs}"}
+
+    eo, es = Errors(), Errors()
+    for res in pool_map(check_prefill_item, items()):
+        eo, es = eo.merge(res["out"]), es.merge(res["state"])
+        if "bad_tokens" in res:
+            print(f"{case} {kind} {res['tag']}: {res['bad_tokens']}", flush=True)
+    print(f"{case} {kind}: out {eo}; state {es}", flush=True)
+    assert eo.ok("bf16") and es.ok("bf16"), (eo, es)
