@@ -14,6 +14,8 @@ heads, d = 128, bf16), against the fp64 oracle on every head:
 The inputs are the generator's, transformed here before rounding to bf16;
 the oracle sees the same rounded values.  The bars are the suite's (relative
 Frobenius 3e-3 per slice, max norm and per token 1e-2, final state alike).
+The two hardest cases also run with fp32 q, k and v against the fp32 bar
+(1e-5 on every measure).
 """
 import numpy as np
 import pytest
@@ -38,29 +40,32 @@ def _unit(x):
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def inputs(case):
+def inputs(case, io="bf16"):
     seed = {"slow_decay": 71, "fast_decay": 72, "beta_extremes": 73, "correlated_keys": 74,
             "correlated_keys_beta1": 75, "large_state": 76}[case]
     shift = {"slow_decay": -8.0, "fast_decay": 3.0, "correlated_keys_beta1": -8.0}.get(case, 2.0)
-    inp = make_prefill([T], HQK, HV, D, D, "bf16", shift, 1.0 if case == "large_state" else None, seed=seed)
+    inp = make_prefill([T], HQK, HV, D, D, io, shift, 1.0 if case == "large_state" else None, seed=seed)
     rng = np.random.default_rng(seed + 1000)
     if case == "beta_extremes":
         inp.beta[...] = np.where(rng.random(inp.beta.shape) < 0.5, 0.001, 0.999).astype(np.float32)
     if case.startswith("correlated_keys"):
         base = rng.standard_normal((1, HQK, D))
-        inp.k[...] = _bf16(_unit(_unit(base) + 0.05 * rng.standard_normal((T, HQK, D)) / np.sqrt(D)))
+        k = _unit(_unit(base) + 0.05 * rng.standard_normal((T, HQK, D)) / np.sqrt(D))
+        inp.k[...] = _bf16(k) if io == "bf16" else k.astype(np.float32)
         if case == "correlated_keys_beta1":
             inp.beta[...] = np.float32(0.999)
     return inp
 
 
-CASES = ["slow_decay", "fast_decay", "beta_extremes", "correlated_keys", "correlated_keys_beta1", "large_state"]
+CASES = [(c, "bf16") for c in ["slow_decay", "fast_decay", "beta_extremes", "correlated_keys",
+                                "correlated_keys_beta1", "large_state"]]
+CASES += [("slow_decay", "f32"), ("correlated_keys_beta1", "f32")]
 
 
 @pytest.mark.parametrize("kind", ["chunked", "scan"])
-@pytest.mark.parametrize("case", CASES)
-def test_prefill_harder_inputs(case, kind):
-    inp = inputs(case)
+@pytest.mark.parametrize("case,io", CASES)
+def test_prefill_harder_inputs(case, io, kind):
+    inp = inputs(case, io)
     d = dev_prefill(inp)
     if kind == "chunked":
         o, s = gdn.prefill_chunked(**d, chunk_size=64)
@@ -84,5 +89,5 @@ def test_prefill_harder_inputs(case, kind):
         eo, es = eo.merge(res["out"]), es.merge(res["state"])
         if "bad_tokens" in res:
             print(f"{case} {kind} {res['tag']}: {res['bad_tokens']}", flush=True)
-    print(f"{case} {kind}: out {eo}; state {es}", flush=True)
-    assert eo.ok("bf16") and es.ok("bf16"), (eo, es)
+    print(f"{case} {io} {kind}: out {eo}; state {es}", flush=True)
+    assert eo.ok(io) and es.ok(io), (eo, es)
