@@ -47,12 +47,13 @@
 //      the output and stage inputs ahead.
 //
 // All block products use 16x16x32 fragments (see gdn_common.hpp).  Precision:
-// bf16 inputs (K, Q, V) enter MFMA exactly.  Y and R are split into hi + lo
-// bf16 halves (as is diag(dec) T when P is formed); P and the state (in
-// K S^T, Q S^T) enter rounded once to bf16: their error reaches the outputs
-// damped by the block decay and stays well below the output's own bf16
-// rounding.  Every product accumulates in
-// fp32.  fp32 inputs use fp32 MFMA throughout.
+// bf16 inputs (K, Q, V) enter MFMA exactly.  Y, R and the state (in K S^T and
+// Q S^T) are split into hi + lo bf16 halves, as is diag(dec) T when P is
+// formed; with gates near 1, Q S^T carries most of an output, so the state
+// rounded once would put its bf16 error there undamped.  P enters rounded once:
+// its error enters each chunk's state update (about 1e-3 relative on the final
+// state).  Every product accumulates in fp32.  fp32 inputs use fp32 MFMA
+// throughout.
 #include <type_traits>
 
 #include "gdn_common.hpp"
