@@ -116,6 +116,11 @@ __global__ __launch_bounds__(16 * (DK / 8)) void decode_kernel(
 // rg + d_v / RPL, ...), at least one full wave.  The unnormalised o
 // goes through LDS; every wave then sums the squares in the same order, so
 // all of them derive the same scale without a second barrier.
+// The products with the state are formed from the raw q and k and scaled by
+// 1/|q|, 1/|k| afterwards (S k_raw / |k| = S k), so they run beside the norm
+// reductions instead of after them; the scalar activations and inverse
+// square roots use the hardware exp2, log2, rcp and rsq (about 1e-6
+// relative error, far below the fp32 tolerance).
 struct FusedArgs {
   const float* gate_bias;   // [h_v] or null
   const float* gate_scale;  // [h_v] or null
@@ -124,9 +129,9 @@ struct FusedArgs {
 };
 
 __device__ __forceinline__ float wave_sum64(float x) {
-  x = sum_lanes16(x);
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  x = sum_lanes16(x);  // each row's sum in all its lanes; the four rows read out as scalars
+  auto rd = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  return (rd(0) + rd(16)) + (rd(32) + rd(48));
 }
 
 template <typename IO, int DK, int RPL>
@@ -163,9 +168,11 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   load4(qp + c0, qv);
   load4(qp + c1, qv + 4);
   const float x = g_raw[bh] + (fa.gate_bias ? fa.gate_bias[h] : 0.f);
-  const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus; log1p(e^x) = x to fp32 precision past 20
-  const float alpha = expf(-(fa.gate_scale ? fa.gate_scale[h] : 1.f) * sp);
-  const float bt = 1.f / (1.f + expf(-b_raw[bh]));
+  constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+  // softplus ln(1 + e^x) through the hardware exp2 and log2 (x past 20: ln(1 + e^x) = x in fp32)
+  const float sp = x > 20.f ? x : __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * LOG2E)) * LN2;
+  const float alpha = __builtin_amdgcn_exp2f(-(fa.gate_scale ? fa.gate_scale[h] : 1.f) * sp * LOG2E);
+  const float bt = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b_raw[bh] * LOG2E));
   // v and the norm weight of the lane's rows with the other inputs, so that
   // no load waits at the end of the step
   float vi[RPL], nw[RPL];
@@ -185,11 +192,9 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
     kq0 = fmaf(kv[e], qv[e], kq0);
     kq1 = fmaf(kv[e + 4], qv[e + 4], kq1);
   }
-  const float rk = 1.f / sqrtf(sum_lanes<LPR>(kk0 + kk1) + fa.qk_eps);
-  const float rq = 1.f / sqrtf(sum_lanes<LPR>(qq0 + qq1) + fa.qk_eps);
+  const float rk = __builtin_amdgcn_rsqf(sum_lanes<LPR>(kk0 + kk1) + fa.qk_eps);
+  const float rq = __builtin_amdgcn_rsqf(sum_lanes<LPR>(qq0 + qq1) + fa.qk_eps);
   const float kq = sum_lanes<LPR>(kq0 + kq1) * rk * rq;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) kv[e] *= rk, qv[e] *= rq;
 
   float o[RPL];
 #pragma unroll
@@ -203,11 +208,12 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
       r0 = fmaf(s[e], qv[e], r0);
       r1 = fmaf(s[e + 4], qv[e + 4], r1);
     }
-    const float p = sum_lanes<LPR>(p0 + p1);
-    const float sq = sum_lanes<LPR>(r0 + r1);
+    const float p = sum_lanes<LPR>(p0 + p1) * rk;
+    const float sq = sum_lanes<LPR>(r0 + r1) * rq;
     const float u = bt * (vi[r] - alpha * p);
+    const float uk = u * rk;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], u * kv[e]);
+    for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], uk * kv[e]);
     if (act) {
       float* so_row = s_out + (size_t(bh) * d_v + row[r]) * DK;
       __builtin_nontemporal_store(f4{s[0], s[1], s[2], s[3]}, reinterpret_cast<f4*>(so_row + c0));
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   const int lane = threadIdx.x & 63;
   float ss = 0.f;
   for (int i = lane; i < d_v; i += 64) ss = fmaf(so[i], so[i], ss);
-  const float scale = 1.f / sqrtf(wave_sum64(ss) / float(d_v) + fa.norm_eps);
+  const float scale = __builtin_amdgcn_rsqf(wave_sum64(ss) / float(d_v) + fa.norm_eps);
   if (act && l == 0) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
