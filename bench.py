@@ -155,8 +155,9 @@ def measured_traffic():
 def counter_figures():
     """Counter-derived figures from the committed rocprofv3 summaries (each
     None unless taken on the current kernel source): the prefill kernels'
-    MFMA busy fractions and executed bf16 MFMA flops, and the decode step's
-    HBM bytes at B = 1 and B = 32 (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."""
+    MFMA busy fractions and executed bf16 MFMA flops, and the HBM bytes of
+    the plain and the fused decode step at B = 1 and B = 32 (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated)."""
     out = {}
     m = profile_fields(MFMA_FILE, KERNEL_SOURCE)
     for key in ("prep_mfma_busy", "sweep_mfma_busy", "call_mfma_busy"):
@@ -164,7 +165,7 @@ def counter_figures():
     for key in ("prep_bf16_mfma_flops", "sweep_bf16_mfma_flops"):
         out[key] = int(m[key]) if m and key in m else None
     d = profile_fields(DECODE_TRAFFIC_FILE, DECODE_SOURCE)
-    for key in ("b1_bytes_per_step", "b32_bytes_per_step"):
+    for key in ("b1_bytes_per_step", "b32_bytes_per_step", "fused_b1_bytes_per_step", "fused_b32_bytes_per_step"):
         out["decode_" + key] = int(d[key]) if d and key in d else None
     out["source"] = "profiles/chunk_prefill_T4096_mfma.md, profiles/decode_step_traffic.md"
     return out
@@ -372,6 +373,30 @@ def main():
             torch.cuda.synchronize()
             log(f"decode B={B}: {2 * n_sets} eager steps over {n_sets} state sets")
             del states, dq, dk_, dv_, dg, db, dout
+            torch.cuda.empty_cache()
+        # the fused step over the same rotation (raw q/k/g/beta, per-head
+        # gate parameters and norm weight)
+        from gated_deltanet_linear_delta_amd.workloads import make_decode_raw
+        for B, n_sets in ((1, 256), (32, 8)):
+            rng = np.random.default_rng(2001 + B)
+            sets = [make_decode_raw(B, HQK, HV, DK, DV, "bf16", 0.02, rng=rng) for _ in range(n_sets)]
+            bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(dev)
+            f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+            dq = [bf(r.q_raw) for r in sets]
+            dk_ = [bf(r.k_raw) for r in sets]
+            dv_ = [bf(r.v) for r in sets]
+            dg = [f32(r.g_raw) for r in sets]
+            db = [f32(r.beta_raw) for r in sets]
+            states = [f32(r.state) for r in sets]
+            bias, scale, w = f32(sets[0].gate_bias), f32(sets[0].gate_scale), f32(sets[0].norm_weight)
+            dout = torch.empty((B, HV, DV), dtype=torch.bfloat16, device=dev)
+            for i in range(2 * n_sets):
+                s_ = i % n_sets
+                gdn.decode_step_fused(dq[s_], dk_[s_], dv_[s_], dg[s_], db[s_], states[s_], gate_bias=bias,
+                                      gate_scale=scale, norm_weight=w, out=dout, state_out=states[s_])
+            torch.cuda.synchronize()
+            log(f"fused decode B={B}: {2 * n_sets} eager steps over {n_sets} state sets")
+            del sets, states, dq, dk_, dv_, dg, db, dout
             torch.cuda.empty_cache()
         copy_calibration()
         print(json.dumps({"decode_counters": True}), flush=True)

@@ -134,12 +134,13 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return (rd(0) + rd(16)) + (rd(32) + rd(48));
 }
 
-template <typename IO, int DK, int RPL>
+template <typename IO, int DK, int NQ, int RPL>
 __global__ __launch_bounds__(1024) void decode_fused_kernel(
     int h_qk, int h_v, int d_v, const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g_raw, const float* __restrict__ b_raw, FusedArgs fa, const float* s_in,
     IO* __restrict__ out, float* s_out) {
-  constexpr int LPR = DK / 8;
+  constexpr int LPR = DK / (4 * NQ);  // lanes per row
+  constexpr int NV = 4 * NQ;          // state values per lane and row
   __shared__ float so[128];
   const int bh = blockIdx.x;  // b * h_v + h
   const int h = bh % h_v;
@@ -149,24 +150,22 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   const int rg = threadIdx.x / LPR;
   const int ngrp = d_v / RPL;
   const bool act = rg < ngrp;  // lane groups past the rows (blocks padded to a wave) only join the sum
-  const int c0 = 4 * l, c1 = DK / 2 + 4 * l;
+  auto cof = [&](int m) { return 4 * l + m * (DK / NQ); };  // column of the lane's m-th float4
 
-  f4 sa[RPL], sb[RPL];
+  f4 sv[RPL][NQ];
   int row[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     row[r] = min(rg, ngrp - 1) + r * ngrp;
     const float* sr = s_in + (size_t(bh) * d_v + row[r]) * DK;
-    sa[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c0));
-    sb[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + c1));
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) sv[r][m] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(sr + cof(m)));
   }
   const IO* kp = k + (size_t(b) * h_qk + j) * DK;
   const IO* qp = q + (size_t(b) * h_qk + j) * DK;
-  float kv[8], qv[8];
-  load4(kp + c0, kv);
-  load4(kp + c1, kv + 4);
-  load4(qp + c0, qv);
-  load4(qp + c1, qv + 4);
+  float kv[NV], qv[NV];
+#pragma unroll
+  for (int m = 0; m < NQ; ++m) load4(kp + cof(m), kv + 4 * m), load4(qp + cof(m), qv + 4 * m);
   const float x = g_raw[bh] + (fa.gate_bias ? fa.gate_bias[h] : 0.f);
   constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
   // softplus ln(1 + e^x) through the hardware exp2 and log2 (x past 20: ln(1 + e^x) = x in fp32)
@@ -184,13 +183,13 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
 
   float kk0 = 0.f, kk1 = 0.f, qq0 = 0.f, qq1 = 0.f, kq0 = 0.f, kq1 = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < NV / 2; ++e) {
     kk0 = fmaf(kv[e], kv[e], kk0);
-    kk1 = fmaf(kv[e + 4], kv[e + 4], kk1);
+    kk1 = fmaf(kv[e + NV / 2], kv[e + NV / 2], kk1);
     qq0 = fmaf(qv[e], qv[e], qq0);
-    qq1 = fmaf(qv[e + 4], qv[e + 4], qq1);
+    qq1 = fmaf(qv[e + NV / 2], qv[e + NV / 2], qq1);
     kq0 = fmaf(kv[e], qv[e], kq0);
-    kq1 = fmaf(kv[e + 4], qv[e + 4], kq1);
+    kq1 = fmaf(kv[e + NV / 2], qv[e + NV / 2], kq1);
   }
   const float rk = __builtin_amdgcn_rsqf(sum_lanes<LPR>(kk0 + kk1) + fa.qk_eps);
   const float rq = __builtin_amdgcn_rsqf(sum_lanes<LPR>(qq0 + qq1) + fa.qk_eps);
@@ -199,25 +198,29 @@ __global__ __launch_bounds__(1024) void decode_fused_kernel(
   float o[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    float s[8] = {sa[r][0], sa[r][1], sa[r][2], sa[r][3], sb[r][0], sb[r][1], sb[r][2], sb[r][3]};
+    float s[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) s[e] = sv[r][e / 4][e % 4];
     float p0 = 0.f, p1 = 0.f, r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < NV / 2; ++e) {
       p0 = fmaf(s[e], kv[e], p0);
-      p1 = fmaf(s[e + 4], kv[e + 4], p1);
+      p1 = fmaf(s[e + NV / 2], kv[e + NV / 2], p1);
       r0 = fmaf(s[e], qv[e], r0);
-      r1 = fmaf(s[e + 4], qv[e + 4], r1);
+      r1 = fmaf(s[e + NV / 2], qv[e + NV / 2], r1);
     }
     const float p = sum_lanes<LPR>(p0 + p1) * rk;
     const float sq = sum_lanes<LPR>(r0 + r1) * rq;
     const float u = bt * (vi[r] - alpha * p);
     const float uk = u * rk;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = fmaf(alpha, s[e], uk * kv[e]);
+    for (int e = 0; e < NV; ++e) s[e] = fmaf(alpha, s[e], uk * kv[e]);
     if (act) {
       float* so_row = s_out + (size_t(bh) * d_v + row[r]) * DK;
-      __builtin_nontemporal_store(f4{s[0], s[1], s[2], s[3]}, reinterpret_cast<f4*>(so_row + c0));
-      __builtin_nontemporal_store(f4{s[4], s[5], s[6], s[7]}, reinterpret_cast<f4*>(so_row + c1));
+#pragma unroll
+      for (int m = 0; m < NQ; ++m)
+        __builtin_nontemporal_store(f4{s[4 * m], s[4 * m + 1], s[4 * m + 2], s[4 * m + 3]},
+                                    reinterpret_cast<f4*>(so_row + cof(m)));
     }
     o[r] = fmaf(alpha, sq, u * kq);
     if (act && l == 0) so[row[r]] = o[r];
@@ -240,25 +243,39 @@ static hipError_t launch_decode_fused_t(const Dims& d, const void* q, const void
                                         const float* s_in, void* out, float* s_out, hipStream_t st) {
   const int blocks = d.num_seqs * d.h_v;
   if (blocks == 0) return hipSuccess;
-  constexpr int LPR = DK / 8;
-  const int lanes = d.d_v * LPR;  // <= 16 d_k
   Prof prof("decode_fused", st);
-  // At most MAXL lanes per workgroup (RPL = 1, 2, 4 or 8 rows per lane
-  // group), so that each lane keeps 2 RPL state loads in flight.
-  constexpr int MAXL = 512;
-  const int rpl = lanes <= MAXL ? 1 : lanes / MAXL;
-  auto go = [&](auto rc) {
-    constexpr int RPL = decltype(rc)::value;
-    hipLaunchKernelGGL((decode_fused_kernel<IO, DK, RPL>), dim3(blocks), dim3(lanes / RPL < 64 ? 64 : lanes / RPL),
-                       0, st, d.h_qk, d.h_v, d.d_v, static_cast<const IO*>(q), static_cast<const IO*>(k),
-                       static_cast<const IO*>(v), g_raw, b_raw, fa, s_in, static_cast<IO*>(out), s_out);
-    return hipGetLastError();
+  // Two shapes, chosen by the number of (sequence, head) workgroups.  With
+  // few heads (below 512 workgroups, e.g. B = 1) the step is the latency of
+  // one workgroup: each lane holds 16 values of a state row (NQ = 4 float4),
+  // so a row needs d_k / 16 lanes and every reduction one DPP step less, and
+  // a workgroup has at most 512 lanes.  With enough heads to fill the GPU
+  // (B = 32) the step is the stream of all heads: each lane holds 8 values
+  // (NQ = 2) and a workgroup up to 1024 lanes, so each lane's serial work per
+  // row is short.  Measured at d = 128: B = 1 3.77 -> 3.59 us against one
+  // shape for both, B = 32 26.1 -> 24.3 us against 512-lane workgroups.
+  // RPL = 1, 2, 4 or 8 rows per lane group keep the workgroup within its cap
+  // (each lane then has NQ RPL state loads in flight).
+  auto launch = [&](auto nq_c, auto maxl_c) {
+    constexpr int NQ = decltype(nq_c)::value, MAXL = decltype(maxl_c)::value;
+    constexpr int LPR = DK / (4 * NQ);
+    const int lanes = d.d_v * LPR;
+    const int rpl = lanes <= MAXL ? 1 : lanes / MAXL;
+    auto go = [&](auto rc) {
+      constexpr int RPL = decltype(rc)::value;
+      hipLaunchKernelGGL((decode_fused_kernel<IO, DK, NQ, RPL>), dim3(blocks),
+                         dim3(lanes / RPL < 64 ? 64 : lanes / RPL), 0, st, d.h_qk, d.h_v, d.d_v,
+                         static_cast<const IO*>(q), static_cast<const IO*>(k), static_cast<const IO*>(v), g_raw,
+                         b_raw, fa, s_in, static_cast<IO*>(out), s_out);
+      return hipGetLastError();
+    };
+    constexpr int RMAX = 128 * LPR / MAXL;  // rows per lane group at d_v = 128
+    if constexpr (RMAX >= 8) if (rpl == 8) return go(std::integral_constant<int, 8>());
+    if constexpr (RMAX >= 4) if (rpl == 4) return go(std::integral_constant<int, 4>());
+    if constexpr (RMAX >= 2) if (rpl == 2) return go(std::integral_constant<int, 2>());
+    return go(std::integral_constant<int, 1>());
   };
-  constexpr int RMAX = 16 * DK / MAXL;  // rows per lane group at d_v = 128
-  if constexpr (RMAX >= 8) if (rpl == 8) return go(std::integral_constant<int, 8>());
-  if constexpr (RMAX >= 4) if (rpl == 4) return go(std::integral_constant<int, 4>());
-  if constexpr (RMAX >= 2) if (rpl == 2) return go(std::integral_constant<int, 2>());
-  return go(std::integral_constant<int, 1>());
+  if (blocks >= 512) return launch(std::integral_constant<int, 2>(), std::integral_constant<int, 1024>());
+  return launch(std::integral_constant<int, 4>(), std::integral_constant<int, 512>());
 }
 
 hipError_t launch_decode_fused(const Dims& d, const void* q, const void* k, const void* v, const float* g_raw,

@@ -6,8 +6,9 @@ per-head RMS norm of the output into the recurrent update, the fusion that
 Perplexity's "Optimizing on-device inference for Apple Silicon" describes in
 section "Reduce state and intermediate traffic".  Errors are per (sequence,
 value head) slice, relative Frobenius: 1e-5 for fp32 inputs, 3e-3 for bf16.
-Shapes cover the 16/32-head d = 128 layer at batch 1 and 32 (one workgroup of
-1024 lanes per head), the small sizes (workgroups padded to a full wave) and
+Shapes cover the 16/32-head d = 128 layer at batch 1 and 32 (one workgroup
+per head; the step has one shape below 512 workgroups and another from 512
+on, both covered), the small sizes (workgroups padded to a full wave) and
 every d_k.
 """
 import numpy as np
@@ -49,6 +50,8 @@ def errors(o, s, o_ref, s_ref):
     (4, 1, 2, 64, 128, "f32"),
     (2, 4, 4, 128, 32, "f32"),
     (5, 2, 4, 128, 128, "f32"),
+    (128, 2, 4, 64, 64, "f32"),   # 512 workgroups and more: the large-batch shape at smaller d_k
+    (256, 1, 2, 32, 128, "f32"),
 ])
 def test_fused_decode_parity(B, h_qk, h_v, d_k, d_v, io):
     r = make_decode_raw(B, h_qk, h_v, d_k, d_v, io, state_std=0.1, seed=300 + B + d_k + d_v)
