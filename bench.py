@@ -1042,6 +1042,10 @@ def main():
                    "batch": 1, "seq_len": T, "h_qk": HQK, "h_v": HV, "d_k": DK, "d_v": DV, "chunk": CHUNK},
         "mfma_util": round(mfma_util, 4),
         "algorithmic_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        # the same count with the Gram products formed per value head instead of
+        # once per query/key head (140,629 instead of 132,437 flop per token and
+        # value head at this shape)
+        "mfma_util_dense": round(prefill_flops(T, hqk=HV) / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
         "kernels_us": {n: round(m * 1e3, 2) for n, (m, _) in per_kernel.items()},
         "call_us_events": call_stats,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
