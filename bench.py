@@ -30,8 +30,9 @@ same JSON line also carries:
               the scan: tokens/s, MFMA and HBM fractions;
   moe_gemm_q4  the expert GEMM on 4-bit group-affine weights (256 experts,
               top 8, K = 2048, N = 1024) at 512- and 2048-token prompts:
-              rebuilt in the GEMM against the two-pass ablation, with the
-              HBM and MFMA fractions of the fused kernel;
+              rebuilt in the GEMM (codes as given, and repacked into 1 KiB
+              tiles) against the two-pass ablation, with the HBM and MFMA
+              fractions of the fused kernel;
   attention_decode  one decode step of grouped-query attention (16 query
               heads on 2 KV heads, 256 values per head, bf16 cache drawn on
               the device) at contexts of 32K, 64K and 128K positions: the
@@ -338,7 +339,8 @@ def main():
 
     if args.moe_counters:
         # counter runs: three eager calls of the fused expert GEMM per prompt
-        # size (the bench leg's inputs), then the calibration copy
+        # size (the bench leg's inputs), three more on the packed codes, then
+        # the calibration copy
         from gated_deltanet_linear_delta_amd.workloads import make_moe
         for tok in (512, 2048):
             mi = make_moe(tok, num_experts=256, top_k=8, k=2048, n=1024, seed=5000 + tok)
@@ -348,9 +350,12 @@ def main():
             ym = torch.empty((xm.shape[0], 1024), dtype=torch.bfloat16, device=dev)
             for _ in range(3):
                 gdn.moe_gemm_q4(xm, offm, cm, sm, bm, y=ym)
+            pm = gdn.moe_pack_q4(cm)
+            for _ in range(3):
+                gdn.moe_gemm_q4_packed(xm, offm, pm, sm, bm, y=ym)
             torch.cuda.synchronize()
-            log(f"expert GEMM at {tok} tokens: three calls")
-            del xm, offm, cm, sm, bm, ym
+            log(f"expert GEMM at {tok} tokens: three calls, then three on packed codes")
+            del xm, offm, cm, pm, sm, bm, ym
             torch.cuda.empty_cache()
         copy_calibration()
         print(json.dumps({"moe_counters": True}), flush=True)
@@ -828,14 +833,16 @@ def main():
             cm, sm, bm = torch.from_numpy(mi.codes).to(dev), bfd(mi.scales), bfd(mi.biases)
             ym = torch.empty((xm.shape[0], 1024), dtype=torch.bfloat16, device=dev)
             wm = torch.empty((256, 1024, 2048), dtype=torch.bfloat16, device=dev)
+            pm = gdn.moe_pack_q4(cm)  # codes in the tiled layout (a one-time step at weight load)
             fused = lambda: gdn.moe_gemm_q4(xm, offm, cm, sm, bm, y=ym)
+            fused_packed = lambda: gdn.moe_gemm_q4_packed(xm, offm, pm, sm, bm, y=ym)
             two_pass = lambda: (gdn.dequant_q4(cm, sm, bm, weights=wm), gdn.moe_gemm_bf16(xm, offm, wm, y=ym))
-            for fn in (fused, two_pass, fused):
+            for fn in (fused, fused_packed, two_pass, fused, fused_packed):
                 for _ in range(3):
                     fn()
             torch.cuda.synchronize()
             res = {}
-            for name, fn in (("fused", fused), ("two_pass", two_pass)):
+            for name, fn in (("fused", fused), ("fused_packed", fused_packed), ("two_pass", two_pass)):
                 # wall time per call with profiling off (best of 5 runs of 20 calls), then the
                 # kernels' own durations from a separate pass with HIP events
                 best = float("inf")
@@ -856,7 +863,9 @@ def main():
             M = int(xm.shape[0])
             nbytes = cm.numel() + 2 * 2 * sm.numel() + 2 * xm.numel() + 2 * ym.numel() + 4 * offm.numel()
             kern = res["fused_kernels_us"]["moe_gemm_q4"]
-            res.update({"routed_rows": M, "rows_per_expert_max": int(np.diff(mi.expert_offsets).max()),
+            kern_p = res["fused_packed_kernels_us"]["moe_gemm_q4_packed"]
+            res.update({"packed_hbm_frac": round(nbytes / (kern_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "packed_speedup": round(res["fused_us"] / res["fused_packed_us"], 3),"routed_rows": M, "rows_per_expert_max": int(np.diff(mi.expert_offsets).max()),
                         "algorithmic_bytes": nbytes,
                         "hbm_gbs": round(nbytes / (kern * 1e-6) / 1e9, 1),
                         "hbm_frac": round(nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -864,7 +873,7 @@ def main():
                         "mfma_util": round(2.0 * M * 2048 * 1024 / (kern * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                         "fusion_speedup": round(res["two_pass_us"] / res["fused_us"], 2)})
             moe[f"tokens_{tok}"] = res
-            del xm, cm, sm, bm, ym, wm
+            del xm, cm, pm, sm, bm, ym, wm
         torch.cuda.empty_cache()
         log(f"expert GEMM on 4-bit weights: {moe}")
 

@@ -405,7 +405,40 @@ gdn_status_t gdn_moe_gemm_q4(const gdn_moe_shape_t* shape, const void* x, const 
     if (y == x) return fail(GDN_ERR_INVALID, "%s: y aliases x", what);
   }
   return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets, codes,
-                                       scales, biases, y, true, static_cast<hipStream_t>(stream)),
+                                       scales, biases, y, true, false, static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_moe_pack_q4(const gdn_moe_shape_t* shape, const uint8_t* codes, uint8_t* packed, void* stream) {
+  const char* what = "gdn_moe_pack_q4";
+  gdn_status_t st = check_moe(shape, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"codes", codes}, {"packed", packed}});  // non-NULL, 16-byte aligned
+  if (st != GDN_OK) return st;
+  const size_t bytes = size_t(shape->num_experts) * size_t(shape->n) * size_t(shape->k / 2);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(codes), b = reinterpret_cast<uintptr_t>(packed);
+  if (a < b + bytes && b < a + bytes) return fail(GDN_ERR_INVALID, "%s: packed overlaps codes", what);
+  return launched(gdn::launch_pack_q4(shape->num_experts, shape->n, shape->k, codes, packed,
+                                      static_cast<hipStream_t>(stream)),
+                  what);
+}
+
+gdn_status_t gdn_moe_gemm_q4_packed(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                                    const uint8_t* packed_codes, const void* scales, const void* biases, void* y,
+                                    void* stream) {
+  const char* what = "gdn_moe_gemm_q4_packed";
+  gdn_status_t st = check_moe(shape, what);
+  if (st != GDN_OK) return st;
+  st = check_ptrs(what, {{"expert_offsets", expert_offsets}, {"packed_codes", packed_codes}, {"scales", scales},
+                         {"biases", biases}});
+  if (st != GDN_OK) return st;
+  if (shape->rows > 0) {
+    st = check_ptrs(what, {{"x", x}, {"y", y}});
+    if (st != GDN_OK) return st;
+    if (y == x) return fail(GDN_ERR_INVALID, "%s: y aliases x", what);
+  }
+  return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets,
+                                       packed_codes, scales, biases, y, true, true, static_cast<hipStream_t>(stream)),
                   what);
 }
 
@@ -434,7 +467,7 @@ gdn_status_t gdn_moe_gemm_bf16(const gdn_moe_shape_t* shape, const void* x, cons
     if (y == x) return fail(GDN_ERR_INVALID, "%s: y aliases x", what);
   }
   return launched(gdn::launch_moe_gemm(shape->num_experts, shape->rows, shape->n, shape->k, x, expert_offsets,
-                                       weights, nullptr, nullptr, y, false, static_cast<hipStream_t>(stream)),
+                                       weights, nullptr, nullptr, y, false, false, static_cast<hipStream_t>(stream)),
                   what);
 }
 

@@ -67,10 +67,13 @@ hipError_t launch_segmented(const Dims& d, int chunk, int L, const void* q, cons
 hipError_t static_scratch(void** ptr, size_t* bytes);
 
 // Grouped expert GEMM: y[r] = W_e x[r] over expert row groups; q4 selects
-// 4-bit group-affine weights rebuilt in the kernel, else bf16 weights.
+// 4-bit group-affine weights rebuilt in the kernel, else bf16 weights;
+// packed, codes in the layout launch_pack_q4 writes.
 hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const int32_t* offsets,
                            const void* weights, const void* scales, const void* biases, void* y, bool q4,
-                           hipStream_t st);
+                           bool packed, hipStream_t st);
+// 4-bit codes [E, N, K / 2] rewritten in 1 KiB (16-row, 128-k) tiles.
+hipError_t launch_pack_q4(int n_exp, int n, int k, const void* codes, void* packed, hipStream_t st);
 // The whole bf16 weight matrix [E, N, K] from 4-bit codes.
 hipError_t launch_dequant_q4(int n_exp, int n, int k, const void* codes, const void* scales, const void* biases,
                              void* w, hipStream_t st);

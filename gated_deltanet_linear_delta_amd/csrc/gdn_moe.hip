@@ -31,6 +31,16 @@
 // super-slabs ahead, the activations one slab ahead; each weight is rebuilt
 // once per row block (two mask operations, eight byte conversions, eight fma
 // and four bf16 packs per eight weights).
+//
+// Packed codes.  In the row-major layout one 16-byte load per lane and column
+// makes an instruction touch 16 weight rows k / 2 bytes apart, 64 bytes each
+// (a power-of-two stride when k is); the compute unit's load path takes that
+// shape slowly.  gdn_moe_pack_q4 rewrites the codes once (at weight-load time)
+// so that the 16 rows x 64 bytes of one 16-row tile and super-slab that one
+// such load instruction needs are one contiguous 1 KiB block, in lane order:
+// block ((e * n / 16 + t) * k / 128 + u), lane 16 g + c at byte 16 lane holds
+// bytes 64 u + 16 g .. + 15 of row 16 t + c (the codes of k = 128 u + 32 g ..
+// + 31).  The packed GEMM reads those blocks; its arithmetic is the same.
 #include <type_traits>
 
 #include "gdn_common.hpp"
@@ -77,6 +87,19 @@ __global__ __launch_bounds__(256) void dequant_q4_kernel(size_t n_dwords, int k,
   w[i] = rebuild8(codes[i], bf16_bits_to_f32(scales[gi]), bf16_bits_to_f32(biases[gi]));
 }
 
+// One thread per 16-byte piece of the packed layout (64 pieces per block).
+__global__ __launch_bounds__(256) void pack_q4_kernel(size_t n_pieces, int n, int k, const uint4* __restrict__ codes,
+                                                      uint4* __restrict__ packed) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_pieces) return;
+  const size_t blk = i >> 6;
+  const int lane = int(i & 63), g = lane >> 4, c = lane & 15;
+  const size_t nu = size_t(k / KS), nt = size_t(n / 16);
+  const size_t u = blk % nu, t = (blk / nu) % nt, e = blk / (nu * nt);
+  const size_t row = e * size_t(n) + 16 * t + c;  // row of the [E * n, k / 2] byte matrix
+  packed[i] = codes[(row * size_t(k / 2) + 64 * u + 16 * g) / 16];
+}
+
 __device__ __forceinline__ int first_slot(int off, int e) { return (off + e * (BM - 1)) / BM; }
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
@@ -98,7 +121,7 @@ __host__ __device__ constexpr size_t moe_lds_bytes(int n_exp) {
   return (size_t(n_exp + 1) * 4 + 15) / 16 * 16 + 2 * ABUF + 2 * SBBUF;
 }
 
-template <bool Q4>
+template <bool Q4, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_gemm_kernel(
     int n_exp, int m, int n, int k, const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ wsrc, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
@@ -167,9 +190,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
 #pragma unroll
       for (int i = 0; i < NP; ++i) *reinterpret_cast<v4u*>(sa + buf * ABUF + loff[i]) = st[i];
     };
-    // codes of one super-slab for both columns: 16 bytes each (Q4)
+    // codes of one super-slab for both columns: 16 bytes each (Q4); packed,
+    // the wave's two 16-row tiles are consecutive tile rows, k / KS blocks apart
+    const size_t pblk0 = (size_t(e) * (n / 16) + size_t(n0 / 16)) * size_t(k / KS);
     auto load_w = [&](uint4 (&c)[2], int ks) __attribute__((always_inline)) {
-      if constexpr (Q4) {
+      if constexpr (Q4 && PACKED) {
+        const size_t b0 = pblk0 + size_t(ks / KS);
+        c[0] = *reinterpret_cast<const uint4*>(wsrc + (b0 << 10) + lane * 16);
+        c[1] = *reinterpret_cast<const uint4*>(wsrc + ((b0 + size_t(k / KS)) << 10) + lane * 16);
+      } else if constexpr (Q4) {
         c[0] = *reinterpret_cast<const uint4*>(wsrc + wrow0 * (k / 2) + ks / 2 + 16 * grp);
         c[1] = *reinterpret_cast<const uint4*>(wsrc + wrow1 * (k / 2) + ks / 2 + 16 * grp);
       }
@@ -277,29 +306,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
 
 hipError_t launch_moe_gemm(int n_exp, int m, int n, int k, const void* x, const int32_t* offsets,
                            const void* weights, const void* scales, const void* biases, void* y, bool q4,
-                           hipStream_t st) {
+                           bool packed, hipStream_t st) {
   // row-block slots: sum_e ceil(m_e / BM) <= (m + E (BM - 1)) / BM, rounded up
   // to a multiple of 8 for the XCD mapping (the spare slots return at once)
   const size_t slots = ((size_t(m) + size_t(n_exp) * (BM - 1)) / BM + 7) / 8 * 8;
   const unsigned blocks = unsigned(slots * size_t(n / BN));
   if (blocks == 0 || m == 0) return hipSuccess;
-  Prof prof(q4 ? "moe_gemm_q4" : "moe_gemm_bf16", st);
+  Prof prof(q4 ? (packed ? "moe_gemm_q4_packed" : "moe_gemm_q4") : "moe_gemm_bf16", st);
   const size_t lds = moe_lds_bytes(n_exp);
-  const void* fn = q4 ? reinterpret_cast<const void*>(&moe_gemm_kernel<true>)
-                      : reinterpret_cast<const void*>(&moe_gemm_kernel<false>);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
-  if (q4)
-    hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(blocks), dim3(256), lds, st, n_exp, m, n, k,
-                       static_cast<const uint16_t*>(x), offsets, static_cast<const uint8_t*>(weights),
-                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
-                       static_cast<uint16_t*>(y));
-  else
-    hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(blocks), dim3(256), lds, st, n_exp, m, n, k,
-                       static_cast<const uint16_t*>(x), offsets, static_cast<const uint8_t*>(weights), nullptr,
-                       nullptr, static_cast<uint16_t*>(y));
+  auto go = [&](auto kern, const void* sc, const void* bi) {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, st, n_exp, m, n, k, static_cast<const uint16_t*>(x),
+                       offsets, static_cast<const uint8_t*>(weights), static_cast<const uint16_t*>(sc),
+                       static_cast<const uint16_t*>(bi), static_cast<uint16_t*>(y));
+    return hipGetLastError();
+  };
+  if (!q4) return go(moe_gemm_kernel<false, false>, nullptr, nullptr);
+  if (packed) return go(moe_gemm_kernel<true, true>, scales, biases);
+  return go(moe_gemm_kernel<true, false>, scales, biases);
+}
+
+hipError_t launch_pack_q4(int n_exp, int n, int k, const void* codes, void* packed, hipStream_t st) {
+  const size_t n_pieces = size_t(n_exp) * n * (k / 32);
+  if (n_pieces == 0) return hipSuccess;
+  Prof prof("pack_q4", st);
+  hipLaunchKernelGGL(pack_q4_kernel, dim3(unsigned((n_pieces + 255) / 256)), dim3(256), 0, st, n_pieces, n, k,
+                     static_cast<const uint4*>(codes), static_cast<uint4*>(packed));
   return hipGetLastError();
 }
 

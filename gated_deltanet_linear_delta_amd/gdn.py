@@ -23,7 +23,7 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 EXPORTS = ("gdn_prefill_scan", "gdn_prefill_scan_blockwise", "gdn_prefill_chunked", "gdn_prefill_chunked_workspace",
            "gdn_prefill_segmented", "gdn_prefill_segmented_workspace", "gdn_prefill_segmented_noalloc",
            "gdn_decode_step", "gdn_decode_step_fused",
-           "gdn_moe_gemm_q4", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_attention_decode",
+           "gdn_moe_gemm_q4", "gdn_moe_pack_q4", "gdn_moe_gemm_q4_packed", "gdn_dequant_q4", "gdn_moe_gemm_bf16", "gdn_attention_decode",
            "gdn_attention_decode_workspace", "gdn_profile_enable", "gdn_profile_collect", "gdn_status_string",
            "gdn_last_error")
 GDN_ATTN_AUTO, GDN_ATTN_GENERAL, GDN_ATTN_FIXED_BLOCK = 0, 1, 2
@@ -98,6 +98,10 @@ def load_library(path: str | None = None):
     mshp = ctypes.POINTER(GdnMoeShape)
     lib.gdn_moe_gemm_q4.argtypes = [mshp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_moe_gemm_q4.restype = ctypes.c_int
+    lib.gdn_moe_pack_q4.argtypes = [mshp, vp, vp, vp]
+    lib.gdn_moe_pack_q4.restype = ctypes.c_int
+    lib.gdn_moe_gemm_q4_packed.argtypes = [mshp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_moe_gemm_q4_packed.restype = ctypes.c_int
     lib.gdn_dequant_q4.argtypes = [mshp, vp, vp, vp, vp, vp]
     lib.gdn_dequant_q4.restype = ctypes.c_int
     lib.gdn_moe_gemm_bf16.argtypes = [mshp, vp, vp, vp, vp, vp]
@@ -399,6 +403,42 @@ def moe_gemm_q4(x, expert_offsets, codes, scales, biases, y=None, stream=None):
             _need(y, "y", torch.bfloat16, (shape.rows, N))
         _check(lib.gdn_moe_gemm_q4(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(codes), _ptr(scales),
                                    _ptr(biases), _ptr(y), _stream(stream)))
+        return y
+
+
+def moe_pack_q4(codes, packed=None, stream=None):
+    """Codes [E, N, K / 2] uint8 rewritten in the tiled layout that
+    moe_gemm_q4_packed reads (gdn_moe_pack_q4); the result has the same shape
+    and size, its bytes in the packed order."""
+    lib = load_library()
+    with _on(stream):
+        E, N, K = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+        _need(codes, "codes", torch.uint8, (E, N, K // 2))
+        if packed is None:
+            packed = torch.empty_like(codes)
+        else:
+            _need(packed, "packed", torch.uint8, (E, N, K // 2))
+        shape = GdnMoeShape(E, 0, K, N)
+        _check(lib.gdn_moe_pack_q4(ctypes.byref(shape), _ptr(codes), _ptr(packed), _stream(stream)))
+        return packed
+
+
+def moe_gemm_q4_packed(x, expert_offsets, packed_codes, scales, biases, y=None, stream=None):
+    """moe_gemm_q4 on codes from moe_pack_q4 (gdn_moe_gemm_q4_packed); the
+    same y bit for bit."""
+    lib = load_library()
+    with _on(stream):
+        shape = _moe_shape(x, expert_offsets, packed_codes, True)
+        E, N, K = shape.num_experts, shape.n, shape.k
+        _need(packed_codes, "packed_codes", torch.uint8, (E, N, K // 2))
+        _need(scales, "scales", torch.bfloat16, (E, N, K // 64))
+        _need(biases, "biases", torch.bfloat16, (E, N, K // 64))
+        if y is None:
+            y = torch.empty((shape.rows, N), dtype=torch.bfloat16, device=x.device)
+        else:
+            _need(y, "y", torch.bfloat16, (shape.rows, N))
+        _check(lib.gdn_moe_gemm_q4_packed(ctypes.byref(shape), _ptr(x), _ptr(expert_offsets), _ptr(packed_codes),
+                                          _ptr(scales), _ptr(biases), _ptr(y), _stream(stream)))
         return y
 
 

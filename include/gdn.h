@@ -288,6 +288,24 @@ gdn_status_t gdn_moe_gemm_q4(const gdn_moe_shape_t* shape, const void* x, const 
                              const uint8_t* codes, const void* scales, const void* biases, void* y,
                              void* stream);
 
+/* Codes rewritten for the load path of the fused form (the same section: the
+ * GEMM reads each weight tile's codes once; here each tile's codes become one
+ * contiguous 1 KiB block, so that one load instruction covers whole cache lines
+ * instead of 16 rows k / 2 bytes apart).  A one-time step when weights are
+ * loaded.  codes [num_experts, n, k / 2] uint8 as above; packed, the same
+ * number of bytes, receives block b = (e * n / 16 + t) * k / 128 + u (16-row
+ * tile t, 128-k super-slab u) at byte 1024 b, its 16 bytes at 16 (16 g + c)
+ * (g = 0..3, c = 0..15) being bytes 64 u + 16 g .. 64 u + 16 g + 15 of row
+ * 16 t + c of expert e.  Both device pointers 16-byte aligned and not
+ * overlapping; shape as for gdn_moe_gemm_q4 (rows and x unused). */
+gdn_status_t gdn_moe_pack_q4(const gdn_moe_shape_t* shape, const uint8_t* codes, uint8_t* packed, void* stream);
+
+/* gdn_moe_gemm_q4 reading codes packed by gdn_moe_pack_q4 (16-byte aligned);
+ * y is bit-identical to gdn_moe_gemm_q4 on the same unpacked codes. */
+gdn_status_t gdn_moe_gemm_q4_packed(const gdn_moe_shape_t* shape, const void* x, const int32_t* expert_offsets,
+                                    const uint8_t* packed_codes, const void* scales, const void* biases, void* y,
+                                    void* stream);
+
 /* The pages' ablation, first half: rebuild the whole bf16 matrix
  * weights [num_experts, n, k] in memory (the same rounding as the fused form). */
 gdn_status_t gdn_dequant_q4(const gdn_moe_shape_t* shape, const uint8_t* codes, const void* scales,

@@ -38,6 +38,7 @@ void expect_zero(size_t v, const char* what) {
 
 // dummy host buffers standing in for device pointers (never read)
 alignas(256) unsigned char g_buf[4096];
+alignas(256) unsigned char g_buf2[4096];  // a second buffer where two must not overlap
 void* P = g_buf;
 const float* F = reinterpret_cast<const float*>(g_buf);
 float* FW = reinterpret_cast<float*>(g_buf);
@@ -227,7 +228,17 @@ void fuzz_moe() {
     expect_error(gdn_dequant_q4(&c.s, g_buf, P, P, P, nullptr), what);
     std::snprintf(what, sizeof what, "moe bf16: %s", c.defect);
     expect_error(gdn_moe_gemm_bf16(&c.s, P, I, P, P, nullptr), what);
+    std::snprintf(what, sizeof what, "pack q4: %s", c.defect);
+    expect_error(gdn_moe_pack_q4(&c.s, g_buf, g_buf2, nullptr), what);
+    std::snprintf(what, sizeof what, "moe q4 packed: %s", c.defect);
+    expect_error(gdn_moe_gemm_q4_packed(&c.s, P, I, g_buf, P, P, P, nullptr), what);
   }
+  expect_error(gdn_moe_pack_q4(nullptr, g_buf, g_buf2, nullptr), "pack q4: shape NULL");
+  expect_error(gdn_moe_pack_q4(&ok, nullptr, g_buf2, nullptr), "pack q4: codes NULL");
+  expect_error(gdn_moe_pack_q4(&ok, g_buf, nullptr, nullptr), "pack q4: packed NULL");
+  expect_error(gdn_moe_pack_q4(&ok, g_buf, g_buf, nullptr), "pack q4: packed equals codes");
+  expect_error(gdn_moe_gemm_q4_packed(&ok, P, I, nullptr, P, P, P, nullptr), "moe q4 packed: codes NULL");
+  expect_error(gdn_moe_gemm_q4_packed(&ok, P, I, g_buf, P, P, g_buf + 8, nullptr), "moe q4 packed: y misaligned");
   expect_error(gdn_moe_gemm_q4(nullptr, P, I, g_buf, P, P, P, nullptr), "moe q4: shape NULL");
   expect_error(gdn_moe_gemm_q4(&ok, nullptr, I, g_buf, P, P, P, nullptr), "moe q4: x NULL");
   expect_error(gdn_moe_gemm_q4(&ok, P, nullptr, g_buf, P, P, P, nullptr), "moe q4: offsets NULL");

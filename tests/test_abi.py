@@ -234,6 +234,18 @@ def test_moe_rejects(lib):
     assert lib.gdn_dequant_q4(ctypes.byref(ok), p[2], p[3], p[4], None, None) == 1   # weights missing
     assert lib.gdn_moe_gemm_bf16(ctypes.byref(S(8, 100, 100, 256)), p[0], p[1], p[2], p[5], None) == 2
     assert lib.gdn_moe_gemm_bf16(ctypes.byref(ok), p[0], p[1], None, p[5], None) == 1
+    # packed codes: the pack and the packed GEMM validate like the others
+    big = 8 * 256 * 128  # bytes of the codes at the ok shape
+    assert lib.gdn_moe_pack_q4(None, p[2], p[2] + big, None) == 1
+    assert lib.gdn_moe_pack_q4(ctypes.byref(S(8, 100, 192, 256)), p[2], p[2] + big, None) == 2
+    assert lib.gdn_moe_pack_q4(ctypes.byref(ok), None, p[2] + big, None) == 1
+    assert lib.gdn_moe_pack_q4(ctypes.byref(ok), p[2], None, None) == 1
+    assert lib.gdn_moe_pack_q4(ctypes.byref(ok), p[2], p[2] + 8 + big, None) == 1   # misaligned
+    assert lib.gdn_moe_pack_q4(ctypes.byref(ok), p[2], p[2] + big - 1024, None) == 1  # overlaps codes
+    assert "overlaps" in lib.gdn_last_error().decode()
+    assert lib.gdn_moe_gemm_q4_packed(ctypes.byref(S(8, 100, 256, 192)), *p, None) == 2
+    assert lib.gdn_moe_gemm_q4_packed(ctypes.byref(ok), p[0], p[1], None, *p[3:], None) == 1
+    assert lib.gdn_moe_gemm_q4_packed(ctypes.byref(ok), *p[:5], p[0], None) == 1     # y aliases x
 
 
 def attn_ws_expected(B, h_q, d, nb):

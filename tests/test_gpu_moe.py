@@ -125,3 +125,36 @@ def test_moe_gemm_empty_batch():
     y = gdn.moe_gemm_q4(x0, off0, d["codes"], d["scales"], d["biases"])
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+def pack_reference(codes):
+    """The packed code layout by reshapes: 1 KiB block (e, t, u) holds, at lane
+    16 g + c, bytes 64 u + 16 g .. + 15 of row 16 t + c of expert e."""
+    E, N, KB = codes.shape
+    t = codes.reshape(E, N // 16, 16, 2 * KB // 128, 4, 16)  # [e, t, c, u, g, byte]
+    return np.ascontiguousarray(t.transpose(0, 1, 3, 4, 2, 5)).reshape(E, N, KB)
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 128, 128), (3, 256, 384), (2, 128, 2048)])
+def test_pack_layout(E, N, K):
+    codes = np.random.default_rng(E * 1000 + K).integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    packed = gdn.moe_pack_q4(torch.from_numpy(codes).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(packed), pack_reference(codes))
+
+
+@pytest.mark.parametrize("tokens,E,top_k,k,n", [
+    (64, 8, 2, 256, 256),
+    (300, 16, 4, 384, 128),
+    (16, 64, 1, 128, 256),          # most experts empty
+    (2048, 256, 8, 2048, 1024),     # the bench shape
+])
+def test_packed_gemm_equals_unpacked(tokens, E, top_k, k, n):
+    # the packed layout changes where the codes are read from, not the arithmetic
+    m = make_moe(tokens, num_experts=E, top_k=top_k, k=k, n=n, seed=7 * tokens + E)
+    d = dev(m)
+    y = gdn.moe_gemm_q4(**d)
+    packed = gdn.moe_pack_q4(d["codes"])
+    y2 = gdn.moe_gemm_q4_packed(d["x"], d["expert_offsets"], packed, d["scales"], d["biases"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
