@@ -114,6 +114,10 @@ def test_graph_moe():
     c, s, b = torch.from_numpy(m.codes).cuda(), bf(m.scales), bf(m.biases)
     check_replays(lambda o: gdn.moe_gemm_q4(x, off, c, s, b, y=o[0]),
                   lambda: [torch.empty((x.shape[0], 256), dtype=torch.bfloat16, device="cuda")])
+    # the code pack and the GEMM on packed codes, captured together
+    check_replays(lambda o: gdn.moe_gemm_q4_packed(x, off, gdn.moe_pack_q4(c, packed=o[1]), s, b, y=o[0]),
+                  lambda: [torch.empty((x.shape[0], 256), dtype=torch.bfloat16, device="cuda"),
+                           torch.empty_like(c)])
 
 
 @pytest.mark.parametrize("layout", ["general", "fixed_block"])
