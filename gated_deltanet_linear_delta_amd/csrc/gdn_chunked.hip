@@ -329,6 +329,21 @@ __device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, f4 x) {
         u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
   }
 }
+// 16 bytes of a per-chunk operand into the workspace, written through the
+// XCD's L2 (agent scope: cache-policy bit 4, sc1, on this chip).  Only the
+// next kernel reads them, so held dirty in L2 they would take space from the
+// prep's own loads and wait there to be written back; written through, they
+// still reach the sweep as fast as before (non-temporal stores, by contrast,
+// send its reads to HBM).  Measured at 4096 tokens: prep 31.0 -> 28.9 us,
+// the sweep unchanged.
+constexpr int kStoreThroughL2 = 16;
+__device__ __forceinline__ void ws_store16(Rsrc r, uint32_t off, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kStoreThroughL2);
+}
+__device__ __forceinline__ u32x4 bits(uint4 x) { return u32x4{x.x, x.y, x.z, x.w}; }
+__device__ __forceinline__ u32x4 bits(f4 x) {
+  return u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+}
 // A split (bf16 hi + lo, two planes `plane` bytes apart) or fp32 operand from global memory.
 __device__ __forceinline__ void ld_split(sp8& d, const uint8_t* p, int plane) {
   d.hi = *reinterpret_cast<const uint4*>(p);
@@ -429,18 +444,20 @@ __device__ __forceinline__ void prep_item(int h_qk, int h_v, const IO* __restric
     while (r + 1 < NB && frag_base(r + 1) <= p) ++r;
     s = p - frag_base(r);
   };
-  auto store_split = [&](uint8_t* dst, const f8& x) {  // two planes: hi, lo (fp32: a, b)
+  // two planes at byte `off` of the workspace block: hi, lo (fp32: a, b)
+  auto store_split = [&](Rsrc r, uint32_t off, const f8& x) {
     if constexpr (BF) {
       uint4 hi, lo;
       split_bf16x8(x, hi, lo);
-      *reinterpret_cast<uint4*>(dst) = hi;
-      *reinterpret_cast<uint4*>(dst + Geo::PLANE) = lo;
+      ws_store16(r, off, bits(hi));
+      ws_store16(r, off + Geo::PLANE, bits(lo));
     } else {
-      *reinterpret_cast<f4*>(dst) = x.a;
-      *reinterpret_cast<f4*>(dst + Geo::PLANE) = x.b;
+      ws_store16(r, off, bits(x.a));
+      ws_store16(r, off + Geo::PLANE, bits(x.b));
     }
   };
   uint8_t* wsb = ws + (size_t(gc) * h_v + h) * Geo::BYTES;
+  const Rsrc rws = make_rsrc(wsb, Geo::BYTES);
 
   // gate and beta of the chunk's tokens, for the gate wave (used after the barrier)
   float g_ld = 0.f, b_ld = 0.f;
@@ -524,16 +541,16 @@ __device__ __forceinline__ void prep_item(int h_qk, int h_v, const IO* __restric
   // the first value head of each query/key group stores Q and K as fragments
   if (h % (h_v / h_qk) == 0) {
     constexpr int NQF = NB * NKS;
-    uint8_t* qb = qf + (size_t(gc) * h_qk + j) * qk_frag_bytes(DK, C, BF);
+    const Rsrc rqb = make_rsrc(qf + (size_t(gc) * h_qk + j) * qk_frag_bytes(DK, C, BF), qk_frag_bytes(DK, C, BF));
     for (int p = wave; p < 2 * NQF; p += NW) {
       const int rq = (p % NQF) / NKS, sq = p % NKS;
       const IO* src = (p < NQF ? sQ : sK) + (16 * rq + col) * KP + 32 * sq + 8 * grp;
-      uint8_t* dst = qb + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
+      const uint32_t off = uint32_t(p * Geo::TPL * Geo::PLANE + lane * 16);
       if constexpr (BF) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        ws_store16(rqb, off, bits(*reinterpret_cast<const uint4*>(src)));
       } else {
-        *reinterpret_cast<f4*>(dst) = *reinterpret_cast<const f4*>(src);
-        *reinterpret_cast<f4*>(dst + Geo::PLANE) = *reinterpret_cast<const f4*>(src + 4);
+        ws_store16(rqb, off, bits(*reinterpret_cast<const f4*>(src)));
+        ws_store16(rqb, off + Geo::PLANE, bits(*reinterpret_cast<const f4*>(src + 4)));
       }
     }
   }
@@ -664,8 +681,7 @@ __device__ __forceinline__ void prep_item(int h_qk, int h_v, const IO* __restric
   for (int p = wave; p < Geo::NF; p += NW) {
     int r, s;
     frag_rs(p, r, s);
-    store_split(wsb + Geo::R_OFF + size_t(p) * 2 * Geo::PLANE + lane * 16,
-                row8(sR, 16 * r + col, 32 * s + 8 * grp));
+    store_split(rws, uint32_t(Geo::R_OFF + p * 2 * Geo::PLANE + lane * 16), row8(sR, 16 * r + col, 32 * s + 8 * grp));
   }
   // T' = diag(dec) T as the B operands of P's products, split once here:
   // fragment (r, s), s >= r / 2, holds column 16 r + col of T' at rows
@@ -738,16 +754,16 @@ __device__ __forceinline__ void prep_item(int h_qk, int h_v, const IO* __restric
   for (int p = wave; p < KB * NTS; p += NW) {
     const int b = p / NTS, s = p % NTS;
     const bool live = 32 * s + 8 * grp < C;
-    uint8_t* dst = wsb + Geo::P_OFF + size_t(p) * Geo::TPL * Geo::PLANE + lane * 16;
+    const uint32_t off = uint32_t(Geo::P_OFF + p * Geo::TPL * Geo::PLANE + lane * 16);
     if constexpr (BF) {
       const IO* src = sP + (32 * s + 8 * grp + col / 4) * KP + 16 * b + 4 * (col % 4);
       const uint2 lo = lds_tr16(src), hi = lds_tr16(src + 4 * KP);
-      *reinterpret_cast<uint4*>(dst) = live ? uint4{lo.x, lo.y, hi.x, hi.y} : uint4{0u, 0u, 0u, 0u};
+      ws_store16(rws, off, live ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{0u, 0u, 0u, 0u});
     } else {
       f8 t;
       ld8col(t, sP + (32 * s + 8 * grp) * KP + 16 * b + col, KP);
-      *reinterpret_cast<f4*>(dst) = live ? t.a : zero4();
-      *reinterpret_cast<f4*>(dst + Geo::PLANE) = live ? t.b : zero4();
+      ws_store16(rws, off, bits(live ? t.a : zero4()));
+      ws_store16(rws, off + Geo::PLANE, bits(live ? t.b : zero4()));
     }
   }
 }
